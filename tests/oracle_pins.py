@@ -1,0 +1,253 @@
+"""Pins of the float64 oracle against facts fixed by the mathematics.
+
+Each pin takes an ``impl`` object exposing the oracle's functions and raises
+AssertionError when the implementation disagrees with an independent fact:
+  * the SVD closed form  out = U p^k(S / (||u||_F + eps)) V^T  (LAPACK SVD);
+  * the cubic (1.5, -0.5, 0) iteration tends to the polar factor U V^T
+    (scipy.linalg.polar);
+  * exact rational closed forms for diagonal inputs (tests/golden);
+  * all singular values equal -> out = p^k(1/sqrt(m)) G/||G|| with p^k in
+    exact rational arithmetic;
+  * a naive pure-Python loop implementation on tiny inputs;
+  * invariants (scale, sign, transpose, orthogonal equivariance, rank, zero);
+  * momentum closed forms; bf16 rounding against torch's float32 -> bfloat16
+    cast and hand-made ties.
+``test_oracle.py`` runs every pin on the oracle; ``test_oracle_mutations.py``
+plants mistakes in copies of the oracle and checks a pin catches each one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+QUINTIC = (3.4445, -4.7750, 2.0315)
+CUBIC = (1.5, -0.5, 0.0)
+EPS = 1e-7
+
+
+def rel_fro(x, y):
+    return float(np.linalg.norm(np.asarray(x) - np.asarray(y)) / max(np.linalg.norm(y), 1e-300))
+
+
+def p_scalar(x, a, b, c, k):
+    for _ in range(k):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def closed_form(u, a, b, c, k, eps=EPS):
+    """U p^k(S / (||u||_F + eps)) V^T via LAPACK SVD."""
+    U, S, Vt = np.linalg.svd(u, full_matrices=False)
+    s = S / (np.linalg.norm(u) + eps)
+    return (U * p_scalar(s, a, b, c, k)[None, :]) @ Vt
+
+
+# ---------------------------------------------------------------- pins
+
+def pin_closed_form(impl):
+    rng = np.random.default_rng(11)
+    for (r, c_), coeffs, k in [((24, 40), QUINTIC, 5), ((40, 24), QUINTIC, 5),
+                               ((32, 32), QUINTIC, 5), ((17, 60), CUBIC, 7),
+                               ((60, 17), (2.0, -1.5, 0.5), 3), ((9, 9), QUINTIC, 1)]:
+        g = rng.standard_normal((r, c_))
+        g[:, 0] *= 30.0                     # spread the spectrum
+        out = impl.orthogonalize(g, *coeffs, k, EPS)
+        ref = closed_form(g, *coeffs, k)
+        assert out.shape == g.shape
+        assert rel_fro(out, ref) < 1e-11, (r, c_, rel_fro(out, ref))
+
+
+def pin_closed_form_with_momentum(impl):
+    """Two momentum steps from a zero buffer, then the SVD closed form of the
+    u given by the momentum recurrence written out by hand."""
+    rng = np.random.default_rng(5)
+    mu = 0.95
+    for shape in [(20, 36), (36, 20)]:
+        g1 = rng.standard_normal(shape)
+        g2 = rng.standard_normal(shape)
+        buf = np.zeros(shape)
+        out1, buf = impl.muon_update(g1, buf, a=QUINTIC[0], b=QUINTIC[1], c=QUINTIC[2], steps=5,
+                                     mu=mu, nesterov=True, eps=EPS, buf_dtype="f64")
+        assert rel_fro(out1, closed_form((1 + mu) * g1, *QUINTIC, 5)) < 1e-11
+        out2, buf = impl.muon_update(g2, buf, a=QUINTIC[0], b=QUINTIC[1], c=QUINTIC[2], steps=5,
+                                     mu=mu, nesterov=True, eps=EPS, buf_dtype="f64")
+        u2 = g2 + mu * (mu * g1 + g2)
+        assert rel_fro(buf, mu * g1 + g2) < 1e-15
+        assert rel_fro(out2, closed_form(u2, *QUINTIC, 5)) < 1e-11
+        # plain (non-Nesterov) momentum: u = buf'
+        out3, buf3 = impl.muon_update(g2, mu * 0 + g1, a=1.5, b=-0.5, c=0.0, steps=4,
+                                      mu=mu, nesterov=False, eps=EPS, buf_dtype="f64")
+        assert rel_fro(buf3, mu * g1 + g2) < 1e-15
+        assert rel_fro(out3, closed_form(mu * g1 + g2, 1.5, -0.5, 0.0, 4)) < 1e-11
+
+
+def pin_momentum_bf16_state(impl):
+    """The stored buffer is the bf16 rounding of mu*buf + g, and the Nesterov
+    vector uses that rounded buffer."""
+    rng = np.random.default_rng(3)
+    mu = 0.95
+    g1 = torch.tensor(rng.standard_normal((8, 12)), dtype=torch.bfloat16).double().numpy()
+    g2 = torch.tensor(rng.standard_normal((8, 12)), dtype=torch.bfloat16).double().numpy()
+    u1, b1 = impl.momentum_update(g1, np.zeros_like(g1), mu, True, "bf16")
+    assert np.array_equal(b1, g1) and np.array_equal(u1, g1 + mu * g1)   # u = (1+mu) g
+    u2, b2 = impl.momentum_update(g2, b1, mu, True, "bf16")
+    want_b2 = torch.tensor(mu * g1 + g2, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(b2, want_b2)
+    assert np.array_equal(u2, g2 + mu * want_b2)
+    assert not np.array_equal(b2, mu * g1 + g2)   # rounding actually happened
+    u0, b0 = impl.momentum_update(g2, None, 0.0, True, "bf16")
+    assert b0 is None and np.array_equal(u0, g2)
+
+
+def pin_polar_limit(impl):
+    """Cubic coefficients drive X0 to the polar factor U V^T."""
+    rng = np.random.default_rng(0)
+    g = rng.standard_normal((64, 128))          # the tiny fp32 check's draw
+    g32 = g.astype(np.float32).astype(np.float64)
+    U, _, Vt = np.linalg.svd(g32, full_matrices=False)
+    polar = U @ Vt
+    e10 = rel_fro(impl.orthogonalize(g32, *CUBIC, 10, EPS), polar)
+    assert 1e-4 < e10 < 1e-3, e10        # 10 steps: close but not converged
+    e30 = rel_fro(impl.orthogonalize(g32, *CUBIC, 30, EPS), polar)
+    assert e30 < 1e-12, e30
+    wp, _ = scipy.linalg.polar(g32.T)           # right polar of the tall transpose
+    assert rel_fro(impl.orthogonalize(g32.T, *CUBIC, 30, EPS), wp) < 1e-12
+
+
+def pin_equal_singular_values(impl):
+    """G with orthonormal rows (times 7): every normalised singular value is
+    1/sqrt(m)/(1 + eps/(7 sqrt m)) so out = p^k(s) G / 7; p^k exact."""
+    for m, n, want in [(768, 768, 1.0835945714), (64, 256, None)]:
+        q, _ = np.linalg.qr(np.random.default_rng(m).standard_normal((n, m)))
+        g = 7.0 * q.T                                   # m x n, orthonormal rows
+        fro = 7.0 * math.sqrt(m)
+        s = Fraction(7) / (Fraction(fro) + Fraction(EPS))
+        a, b, c = (Fraction(str(x)) for x in QUINTIC)
+        pk = float(p_scalar(s, a, b, c, 5))
+        if want is not None:
+            assert abs(pk - want) < 1e-9                # the surveyed worked value
+        out = impl.orthogonalize(g, *QUINTIC, 5, EPS)
+        assert rel_fro(out, pk * q.T) < 1e-11
+
+
+def pin_golden_diagonal(impl):
+    with open(os.path.join(GOLDEN, "diag_closed_forms.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        r, c_ = case["rows"], case["cols"]
+        for transpose in (False, True):
+            g = np.zeros((r, c_))
+            for i, d in enumerate(case["diag"]):
+                g[i, i] = d
+            want = np.zeros((r, c_))
+            for i, d in enumerate(case["out_diag"]):
+                want[i, i] = d
+            if transpose:
+                g, want = g.T, want.T
+            out = impl.orthogonalize(g, *case["coeffs"], case["steps"], gold["eps"])
+            assert out.shape == want.shape
+            assert np.max(np.abs(out - want)) < 1e-12, (case["name"], transpose)
+
+
+def naive_update(g, buf, a, b, c, k, mu, nesterov, eps):
+    """The whole update with Python lists and loops only (no numpy)."""
+    rows, cols = len(g), len(g[0])
+    if mu:
+        nb = [[mu * buf[i][j] + g[i][j] for j in range(cols)] for i in range(rows)]
+        u = [[(g[i][j] + mu * nb[i][j]) if nesterov else nb[i][j] for j in range(cols)]
+             for i in range(rows)]
+    else:
+        u = [row[:] for row in g]
+    ss = 0.0
+    for i in range(rows):
+        for j in range(cols):
+            ss += u[i][j] * u[i][j]
+    nrm = math.sqrt(ss) + eps
+    x = [[u[i][j] / nrm for j in range(cols)] for i in range(rows)]
+    tall = rows > cols
+    if tall:
+        x = [[x[i][j] for i in range(rows)] for j in range(cols)]
+    m, n = len(x), len(x[0])
+    for _ in range(k):
+        A = [[sum(x[i][t] * x[j][t] for t in range(n)) for j in range(m)] for i in range(m)]
+        AA = [[sum(A[i][t] * A[t][j] for t in range(m)) for j in range(m)] for i in range(m)]
+        B = [[b * A[i][j] + c * AA[i][j] for j in range(m)] for i in range(m)]
+        x = [[a * x[i][j] + sum(B[i][t] * x[t][j] for t in range(m)) for j in range(n)]
+             for i in range(m)]
+    if tall:
+        x = [[x[i][j] for i in range(m)] for j in range(n)]
+    return x
+
+
+def pin_brute_force(impl):
+    rng = np.random.default_rng(7)
+    for (r, c_), mu, nest, k in [((2, 3), 0.0, False, 5), ((5, 3), 0.9, True, 5),
+                                 ((8, 8), 0.5, False, 3), ((16, 40), 0.95, True, 2),
+                                 ((40, 16), 0.95, True, 2)]:
+        g = rng.standard_normal((r, c_))
+        buf = rng.standard_normal((r, c_)) if mu else None
+        want = np.array(naive_update(g.tolist(), None if buf is None else buf.tolist(),
+                                     *QUINTIC, k, mu, nest, EPS))
+        out, _ = impl.muon_update(g, buf, a=QUINTIC[0], b=QUINTIC[1], c=QUINTIC[2], steps=k,
+                                  mu=mu, nesterov=nest, eps=EPS, buf_dtype="f64")
+        assert rel_fro(out, want) < 1e-12, ((r, c_), rel_fro(out, want))
+
+
+def pin_invariants(impl):
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal((24, 56))
+    f = lambda x, k=5, abc=QUINTIC: impl.orthogonalize(x, *abc, k, 0.0)   # noqa: E731
+    base = f(g)
+    assert rel_fro(f(3.5 * g), base) < 1e-12                # scale
+    assert np.array_equal(f(-g), -base)                      # odd
+    assert rel_fro(f(g.T), base.T) < 1e-12                   # transpose
+    P, _ = np.linalg.qr(rng.standard_normal((24, 24)))
+    Q, _ = np.linalg.qr(rng.standard_normal((56, 56)))
+    assert rel_fro(f(P @ g @ Q), P @ base @ Q) < 1e-11       # orthogonal equivariance
+    low = rng.standard_normal((24, 3)) @ rng.standard_normal((3, 56))
+    sv = np.linalg.svd(f(low), compute_uv=False)
+    assert np.all(sv[3:] < 1e-12) and np.all(sv[:3] > 0.1)   # rank kept
+    z = impl.orthogonalize(np.zeros((5, 7)), *QUINTIC, 5, EPS)
+    assert np.all(z == 0) and np.all(np.isfinite(z))         # zero -> zero, no NaN
+    x0 = g / (np.linalg.norm(g) + EPS)
+    assert rel_fro(impl.orthogonalize(g, *QUINTIC, 0, EPS), x0) < 1e-15   # k = 0
+    assert rel_fro(impl.orthogonalize(g, 1.0, 0.0, 0.0, 4, EPS), x0) < 1e-15  # identity map
+    # (0,1,0): one step gives (X X^T) X
+    assert rel_fro(impl.orthogonalize(g, 0.0, 1.0, 0.0, 1, EPS), x0 @ x0.T @ x0) < 1e-12
+    A = x0 @ x0.T
+    assert rel_fro(impl.orthogonalize(g, 0.0, 0.0, 1.0, 1, EPS), A @ A @ x0) < 1e-12
+
+
+def pin_bf16_rounding(impl):
+    rng = np.random.default_rng(17)
+    x32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormals
+        (rng.standard_normal(2000) * 1e37).astype(np.float32),
+        np.array([3.3895e38, -3.3900e38, 3.4e38, 0.0, -0.0], np.float32),
+    ])
+    want = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    got = impl.bf16_round(x32.astype(np.float64))
+    assert np.array_equal(got, want)
+    # ties to even, by hand: 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6
+    one = 1.0
+    assert impl.bf16_round(np.array([one + 2 ** -8]))[0] == 1.0
+    assert impl.bf16_round(np.array([one + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    assert impl.bf16_round(np.array([one + 2 ** -8 + 2 ** -30]))[0] == 1.0 + 2 ** -7
+    assert impl.bf16_round(np.array([-(one + 2 ** -8)]))[0] == -1.0
+    assert impl.bf16_round(np.array([2.0 ** -134]))[0] == 0.0            # subnormal tie -> 0
+    assert impl.bf16_round(np.array([3 * 2.0 ** -134]))[0] == 2.0 ** -132
+    assert np.isinf(impl.bf16_round(np.array([2.0 ** 128 * (1 - 2 ** -9)]))[0])
+    assert np.isnan(impl.bf16_round(np.array([np.nan]))[0])
+
+
+ALL_PINS = [pin_closed_form, pin_closed_form_with_momentum, pin_momentum_bf16_state,
+            pin_polar_limit, pin_equal_singular_values, pin_golden_diagonal, pin_brute_force,
+            pin_invariants, pin_bf16_rounding]

@@ -1,0 +1,61 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutation edits the oracle's source text (a dropped term, a wrong sign,
+a wrong operand, an off-by-one, a missing rounding) and loads the edited copy
+as a separate module; the real oracle is untouched.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "muon_oracle.py")
+
+MUTATIONS = {
+    "drop_c_term": ("B = b * A + c * (A @ A)", "B = b * A"),
+    "drop_b_term": ("B = b * A + c * (A @ A)", "B = c * (A @ A)"),
+    "sign_of_BX": ("return a * x + B @ x", "return a * x - B @ x"),
+    "drop_aX": ("return a * x + B @ x", "return B @ x"),
+    "gram_wrong_side": ("A = x @ x.T", "A = (x.T @ x)[: x.shape[0], : x.shape[0]]"),
+    "norm_without_sqrt": ("u / (np.sqrt(np.sum(u * u)) + eps)", "u / (np.sum(u * u) + eps)"),
+    "eps_inside_sqrt": ("u / (np.sqrt(np.sum(u * u)) + eps)", "u / np.sqrt(np.sum(u * u) + eps)"),
+    "max_norm_instead_of_fro": ("u / (np.sqrt(np.sum(u * u)) + eps)", "u / (np.max(np.abs(u)) + eps)"),
+    "no_transpose_back": ("return x.T.copy() if tall else x.copy()", "return x.copy()"),
+    "one_step_short": ("for _ in range(int(steps)):", "for _ in range(max(int(steps) - 1, 0)):"),
+    "coeffs_swapped": ("x = ns_polynomial_step(x, a, b, c)", "x = ns_polynomial_step(x, a, c, b)"),
+    "nesterov_old_buffer": ("u = g + mu * new_buf if nesterov", "u = g + mu * buf if nesterov"),
+    "nesterov_ignored": ("u = g + mu * new_buf if nesterov else new_buf.copy()", "u = new_buf.copy()"),
+    "buffer_not_rounded": ("new_buf = _ROUND[buf_dtype](mu * buf + g)", "new_buf = mu * buf + g"),
+    "ema_momentum": ("new_buf = _ROUND[buf_dtype](mu * buf + g)",
+                     "new_buf = _ROUND[buf_dtype](mu * buf + (1 - mu) * g)"),
+    "bf16_7_bits": ("np.rint(np.ldexp(f[normal], 8)), e[normal] - 8)",
+                    "np.rint(np.ldexp(f[normal], 7)), e[normal] - 7)"),
+    "bf16_truncate": ("np.rint(np.ldexp(f[normal], 8))", "np.trunc(np.ldexp(f[normal], 8))"),
+    "bf16_half_up": ("np.rint(np.ldexp(f[normal], 8))", "np.floor(np.ldexp(f[normal], 8) + 0.5)"),
+}
+
+
+def load_mutant(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    spec = importlib.util.spec_from_loader(mod.__name__, loader=None)
+    mod.__spec__ = spec
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mutant = load_mutant(name, *MUTATIONS[name])
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception:            # AssertionError, or a shape error
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutation {name}"

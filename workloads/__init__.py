@@ -1,0 +1,15 @@
+"""Seeded synthetic workloads (matrix sets and their gradients).
+
+This package holds input recipes only: shapes, seeds and random draws. It
+contains none of the update's arithmetic, so both the float64 oracle and the
+HIP path can take their inputs from it without sharing any computation.
+"""
+from .configs import CONFIGS, WorkloadConfig, config_names  # noqa: F401
+from .generators import (  # noqa: F401
+    gaussian_matrix,
+    spiked_matrix,
+    powerlaw_matrix,
+    make_gradients,
+    make_workload,
+    to_f64,
+)
