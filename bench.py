@@ -1,0 +1,200 @@
+"""Throughput of the Muon update on one MI355X, GPT-2-124M hidden-matrix set.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                [--no-cpu-baseline] [--profile-steps N]
+
+A step is one muon_plan_step over all matrices of the workload (momentum,
+normalisation and k Newton-Schulz steps), inputs resident in HBM. `value` is
+algorithmic TFLOP/s of the whole step; `roofline` describes the kernel with
+the largest share of the step's time, timed with HIP events recorded around
+each launch on the step's stream in a second pass of the same length; the
+CPU baseline times the float64 oracle on a bounded sample of the same
+matrices. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon NS orthogonalisation TFLOPS & % bf16 MFMA peak, GPT-2-124M matrix set"
+PEAK = {"bf16": 2500.0, "fp32": 157.3}       # dense MFMA TFLOP/s, MI355X
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_work(shapes, steps):
+    """Algorithmic work per launch of each kernel: (amount, unit)."""
+    gram = poly = upd = 0
+    elems = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        gram += m * (m + 1) * n
+        poly += m * m * (m + 1)
+        upd += 2 * m * m * n
+        elems += r * c
+    return {
+        # momentum: read G and buf, write buf (bf16)  -> 6 B/elem
+        "momentum": (6.0 * elems, "B"),
+        # normalise: read G and buf (4 B), write fp32 master + bf16 operand (6 B)
+        "normalize": (10.0 * elems, "B"),
+        "gram": (float(gram), "flop"),
+        "poly": (float(poly), "flop"),
+        "update": (float(upd), "flop"),
+    }
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """Float64 oracle on the host cores over whole layers of the workload
+    (one layer = 4 square + 1 wide + 1 tall matrix) until ~budget_s."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workloads import make_gradients, to_f64
+
+    L = wl.n_matrices // 6 if wl.n_matrices % 6 == 0 else 0
+    layer_idx = (lambda l: [4 * l, 4 * l + 1, 4 * l + 2, 4 * l + 3, 4 * L + l, 5 * L + l]) \
+        if L else (lambda l: [l])
+    nlayers = L if L else wl.n_matrices
+    grads = make_gradients(wl, step=0, device="cpu")
+    done, flops, t_total = 0, 0, 0.0
+    a, b, c = (float(np.float32(x)) for x in wl.coeffs)
+    while done < nlayers and t_total < budget_s:
+        idx = layer_idx(done)
+        g64 = [to_f64(grads[i]) for i in idx]
+        t0 = time.perf_counter()
+        for g in g64:
+            oracle.muon_update(g, np.zeros_like(g), a=a, b=b, c=c, steps=wl.steps,
+                               mu=float(np.float32(wl.momentum)), nesterov=wl.nesterov,
+                               eps=wl.eps, buf_dtype=wl.dtype)
+        t_total += time.perf_counter() - t0
+        flops += sum(oracle.falg_flops(*wl.shapes[i], wl.steps) for i in idx)
+        done += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {nlayers} {'layers (6 matrices each)' if L else 'matrices'} "
+                      f"of {wl.name}, float64 NumPy, {t_total:.1f} s",
+            "seconds": t_total, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2_124m_matrix_set")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} "
+              "is not supported (the update shards by matrix; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import muon_newton_schulz_04_amd as mu
+    from workloads import CONFIGS, make_gradients
+
+    wl = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    grads = [g.to(dev) for g in make_gradients(wl, step=0, device="cpu")]
+    bufs = [torch.zeros_like(g) for g in grads] if wl.momentum else None
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, bufs, outs)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan.step(cfg, ws, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.step(cfg, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # second pass of the same length with per-launch HIP events
+    plan.set_timing(True)
+    plan.kernel_times()
+    for _ in range(args.steps):
+        plan.step(cfg, ws, stream)
+    torch.cuda.synchronize()
+    kt = plan.kernel_times()
+    plan.set_timing(False)
+
+    falg = wl.falg_flops()
+    value = falg / (ms * 1e-3) / 1e12
+    work = kernel_work(wl.shapes, wl.steps)
+    per_kernel = {}
+    for name, (tot_ms, n) in kt.items():
+        if n == 0:
+            continue
+        avg = tot_ms / n
+        amount, unit = work[name]
+        rate = amount / (avg * 1e-3)
+        per_kernel[name] = {"launches_per_step": n / args.steps, "avg_us": avg * 1e3,
+                            "ms_per_step": tot_ms / args.steps,
+                            ("TFLOP/s" if unit == "flop" else "GB/s"):
+                                rate / (1e12 if unit == "flop" else 1e9)}
+    dom = max(kt, key=lambda k: kt[k][0])
+    d_amount, d_unit = work[dom]
+    d_avg = kt[dom][0] / kt[dom][1]
+    if d_unit == "flop":
+        roof = {"bound": "mfma", "achieved": d_amount / (d_avg * 1e-3) / 1e12,
+                "peak": PEAK[wl.dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": d_amount / (d_avg * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = d_avg * 1e3
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded spiked-Gaussian gradients, GPT-2 shapes)",
+        "config": {"workload": wl.name, "matrices": wl.n_matrices,
+                   "shapes": "48x768x768 + 12x768x3072 + 12x3072x768"
+                   if wl.name == "gpt2_124m_matrix_set" else str(sorted(set(wl.shapes))),
+                   "ns_steps": wl.steps, "coeffs": list(wl.coeffs), "momentum": wl.momentum,
+                   "nesterov": wl.nesterov, "falg_gflop_per_step": falg / 1e9},
+        "pct_bf16_dense_peak": 100.0 * value / PEAK["bf16"],
+        "matrices_per_s": wl.n_matrices / (ms * 1e-3),
+        "wall_s_timed": wall,
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    plan.destroy()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon Newton-Schulz update library.
+ *
+ * The operation (blog.hotdry.top, "How to train a GPT model in 3 minutes: an
+ * analysis of modded-nanogpt's optimizations", section 2, item "customised
+ * Muon optimizer"): Muon updates each hidden weight matrix with its momentum
+ * orthogonalised by a Newton-Schulz iteration instead of an SVD, keeping one
+ * momentum buffer per matrix. For every matrix G (rows x cols) of a set:
+ *
+ *   buf' = mu * buf + G           (stored back at the buffer dtype, RNE)
+ *   u    = G + mu * buf'  (Nesterov)   or   u = buf'
+ *   X    = u / (||u||_F + eps)
+ *   if rows > cols: X = X^T        (so the Gram matrix is min(rows,cols)^2)
+ *   k times:  A = X X^T;  B = b A + c A A;  X = a X + B X
+ *   out  = X (transposed back), stored at the set's dtype (RNE)
+ *
+ * Arithmetic: bf16 sets multiply bf16 operands on the matrix cores with fp32
+ * accumulation and keep X in an fp32 master copy (momentum and norms in
+ * fp32); fp32 sets compute in fp32 throughout.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers in muon_matrix, `workspace` and `stream` are device-side
+ *    objects owned by the caller (`stream` is a hipStream_t; NULL = the
+ *    default stream). The library never frees or retains them beyond a call,
+ *    except that a plan remembers the matrix pointers it was created with.
+ *  - All arguments are validated before any work is enqueued. On an error
+ *    nothing is launched and nothing is written; the status says why.
+ *  - Work is enqueued asynchronously on `stream`; the caller synchronises.
+ *    No C++ exception crosses this interface.
+ *  - Results are deterministic: equal inputs give bitwise-equal outputs.
+ *  - NaN and Inf in the inputs propagate; they are not checked.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum {
+  MUON_OK = 0,
+  MUON_E_INVALID = 1,   /* NULL where a pointer is required, bad config value */
+  MUON_E_DTYPE = 2,     /* unknown dtype */
+  MUON_E_SHAPE = 3,     /* negative or too large sizes, ld < cols */
+  MUON_E_ALIGN = 4,     /* pointer not aligned to its element size */
+  MUON_E_WORKSPACE = 5, /* workspace NULL or smaller than muon_workspace_bytes */
+  MUON_E_DEVICE = 6,    /* no usable gfx950 device / HIP runtime error */
+  MUON_E_LAUNCH = 7,    /* a kernel launch failed */
+  MUON_E_ALLOC = 8      /* host or device allocation for a plan failed */
+} muon_status;
+
+/* Element type of grad, momentum and out (one type per call). */
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* Limits checked by validation (MUON_E_SHAPE beyond them). */
+#define MUON_MAX_DIM 65536           /* rows and cols each */
+#define MUON_MAX_ELEMS 1073741824LL  /* rows * cols per matrix (2^30) */
+#define MUON_MAX_MATRICES 65536      /* matrices per call */
+#define MUON_MAX_STEPS 64            /* Newton-Schulz steps */
+
+/* One matrix of the set. Row-major: element (i, j) of grad, momentum and out
+ * is at base + i * ld + j (elements of the set's dtype). rows == 0 or
+ * cols == 0 is an empty matrix and is skipped. `grad` is read only;
+ * `momentum` is read and overwritten with buf' (it may be NULL iff the
+ * config's momentum is 0, and must then not be used); `out` is written with
+ * the orthogonalised update. `out` may alias `grad` (same ld); it must not
+ * overlap `momentum` or any other matrix's buffers. All three pointers must
+ * be aligned to the element size; 16-byte alignment with ld and cols
+ * multiples of 16 bytes selects the vectorised elementwise path. */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  const void* grad;
+  void* momentum;
+  void* out;
+} muon_matrix;
+
+/* Per-call scalars. (a, b, c) are the odd polynomial's coefficients
+ * p(x) = a x + b x^3 + c x^5 (e.g. the quintic (3.4445, -4.7750, 2.0315) or
+ * the cubic (1.5, -0.5, 0)); steps in [0, MUON_MAX_STEPS] (0 returns X0);
+ * momentum mu in [0, 1) (0: no momentum state, u = G); nesterov 0 or 1;
+ * eps >= 0 is added to ||u||_F (1e-7 is the usual value). All must be
+ * finite. */
+typedef struct {
+  float a, b, c;
+  int32_t steps;
+  float momentum;
+  int32_t nesterov;
+  float eps;
+} muon_config;
+
+/* Opaque plan: validated shapes, per-matrix workspace layout and the tile
+ * schedules of every kernel, uploaded once to device memory. */
+typedef struct muon_plan_s muon_plan;
+
+/* ABI version of the loaded library (MUON_ABI_VERSION). */
+int32_t muon_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* muon_status_str(int32_t status);
+
+/* Bytes of device workspace a call on this matrix set needs (host only, no
+ * device calls). *bytes receives the size (0 for an all-empty set). */
+muon_status muon_workspace_bytes(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                                 size_t* bytes);
+
+/* Builds a plan for `mats` (copied; pointers included) and uploads its
+ * tables to the current device. Allocates a few KB to a few MB of device
+ * memory owned by the plan; *plan receives NULL on error. */
+muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                             muon_plan** plan);
+
+/* Enqueues one Muon update of every matrix of the plan on `stream`.
+ * `workspace` must hold at least muon_workspace_bytes bytes, 256-byte
+ * aligned, and must not be used by anything else until the work ends.
+ * Calls on the same workspace must be ordered (same stream). */
+muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Frees a plan after waiting for the device (NULL is a no-op). */
+void muon_plan_destroy(muon_plan* plan);
+
+/* One Muon update of `mats` without an explicit plan: looks up (or builds
+ * and caches, keyed by the full descriptor array including pointers) a plan
+ * and calls muon_plan_step. A cache miss allocates and synchronises once;
+ * training loops with stable buffers hit the cache on every later call. */
+muon_status muon_step(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                      const muon_config* cfg, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Orthogonalisation only: u = grad (momentum pointers ignored, cfg->momentum
+ * and cfg->nesterov ignored), then normalisation and the iteration. */
+muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                               const muon_config* cfg, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ---- introspection (tests, benchmarks, profiling) ---------------------- */
+
+/* Kernels of one step, in launch order: momentum, normalise, then per
+ * Newton-Schulz step gram, poly, update. */
+typedef enum {
+  MUON_K_MOMENTUM = 0, /* buf' and per-block sums of u^2            (HBM)  */
+  MUON_K_NORMALIZE = 1,/* X0 = u/(||u||+eps), fp32 master + operand (HBM)  */
+  MUON_K_GRAM = 2,     /* A = X X^T, upper-triangle tiles mirrored (MFMA) */
+  MUON_K_POLY = 3,     /* B = b A + c A A, upper tiles mirrored    (MFMA) */
+  MUON_K_UPDATE = 4,   /* X = a X + B X (last step writes out)     (MFMA) */
+  MUON_K_COUNT = 5
+} muon_kernel_kind;
+
+/* Host-only schedule query: the work items kernel `kind` runs for `mats`,
+ * four int32 per item {matrix, a, b, c} (momentum: {matrix, first row,
+ * row count, partial slot}; normalise: {matrix, tile row, tile col, 0} of
+ * 64 x 64 tiles of the rows<=cols orientation; gram/poly: {matrix, tile
+ * row, tile col, 0} upper-triangle 128 x 128 tiles; update: {matrix, tile
+ * row, tile col, 0}), in launch order with empty slots as {-1,-1,-1,-1}.
+ * Writes min(cap, count) items to `items` (may be NULL when cap == 0) and
+ * the total to *count. No device calls. */
+muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                                int32_t kind, int32_t* items, int64_t cap, int64_t* count);
+
+/* Per-kernel timing with HIP events recorded on the step's stream around
+ * each launch. Off by default; while on, every muon_plan_step records
+ * events, and muon_plan_kernel_times (which synchronises the plan's last
+ * stream) accumulates elapsed milliseconds and launch counts per
+ * muon_kernel_kind into ms[MUON_K_COUNT] and launches[MUON_K_COUNT], summed
+ * over the steps since timing was enabled or last read (reading resets). */
+muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable);
+muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches);
+
+/* Workspace layout of matrix `idx` of a plan (byte offsets from the
+ * workspace base; -1 where a buffer does not exist). x_master: fp32 X
+ * (rows<=cols orientation, padded mp x np, row-major); x_op0/x_op1: the
+ * two operand copies (bf16 sets; fp32 sets use two fp32 masters instead);
+ * gram: A (mp x mp); poly: B (mp x mp). Element types: bf16 for bf16 sets
+ * except x_master; fp32 for fp32 sets. The buffer that holds the final X of
+ * a step of k iterations is x_op[k % 2] / the master. */
+typedef struct {
+  int64_t m, n, mp, np;
+  int64_t x_master, x_op0, x_op1, gram, poly;
+} muon_buffer_info;
+
+muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffer_info* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

@@ -1,0 +1,347 @@
+// C ABI of the Muon update library: validation, plans (device tables),
+// launches, per-kernel timing and the plan cache behind muon_step.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+using muon::HostPlan;
+using muon::MatInfo;
+using muon::WorkItem;
+
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+struct muon_plan_s {
+  HostPlan host;
+  int device = -1;
+  void* dmem = nullptr;                       // MatInfo table + schedules
+  const MatInfo* d_mats = nullptr;
+  const WorkItem* d_items[MUON_K_COUNT] = {};
+  int grid[MUON_K_COUNT] = {};
+  bool timing = false;
+  std::vector<TimedLaunch> pending;           // recorded, not yet read
+  std::vector<hipEvent_t> free_events;
+  double acc_ms[MUON_K_COUNT] = {};
+  int64_t acc_n[MUON_K_COUNT] = {};
+};
+
+namespace {
+
+muon_status upload(muon_plan_s* p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MUON_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MUON_E_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_E_DEVICE;
+  p->device = dev;
+  size_t bytes = sizeof(MatInfo) * std::max<size_t>(1, p->host.info.size());
+  size_t offs[MUON_K_COUNT];
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    bytes = (bytes + 255) / 256 * 256;
+    offs[k] = bytes;
+    bytes += sizeof(WorkItem) * std::max<size_t>(1, p->host.sched[k].items.size());
+  }
+  std::vector<char> h(bytes, 0);
+  if (!p->host.info.empty())
+    std::memcpy(h.data(), p->host.info.data(), sizeof(MatInfo) * p->host.info.size());
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    const auto& it = p->host.sched[k].items;
+    if (!it.empty()) std::memcpy(h.data() + offs[k], it.data(), sizeof(WorkItem) * it.size());
+    p->grid[k] = static_cast<int>(it.size());
+  }
+  if (hipMalloc(&p->dmem, bytes) != hipSuccess) {
+    p->dmem = nullptr;
+    (void)hipGetLastError();
+    return MUON_E_ALLOC;
+  }
+  if (hipMemcpy(p->dmem, h.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p->dmem);
+    p->dmem = nullptr;
+    (void)hipGetLastError();
+    return MUON_E_DEVICE;
+  }
+  char* base = static_cast<char*>(p->dmem);
+  p->d_mats = reinterpret_cast<const MatInfo*>(base);
+  for (int k = 0; k < MUON_K_COUNT; ++k) p->d_items[k] = reinterpret_cast<const WorkItem*>(base + offs[k]);
+  return MUON_OK;
+}
+
+void release(muon_plan_s* p) {
+  if (!p) return;
+  (void)hipDeviceSynchronize();
+  for (auto& t : p->pending) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (auto e : p->free_events) (void)hipEventDestroy(e);
+  if (p->dmem) (void)hipFree(p->dmem);
+  delete p;
+}
+
+hipEvent_t get_event(muon_plan_s* p) {
+  if (!p->free_events.empty()) {
+    hipEvent_t e = p->free_events.back();
+    p->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t ws_bytes,
+                      void* stream, bool orthogonalize_only) {
+  if (p == nullptr) return MUON_E_INVALID;
+  muon_status st = muon::validate_config(cfg);
+  if (st != MUON_OK) return st;
+  const HostPlan& H = p->host;
+  if (H.ws_bytes == 0) return MUON_OK;  // nothing to do (all matrices empty)
+  if (ws == nullptr || ws_bytes < H.ws_bytes || reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return MUON_E_WORKSPACE;
+  const bool use_mom = !orthogonalize_only && cfg->momentum != 0.f;
+  if (use_mom)
+    for (const MatInfo& I : H.info)
+      if (I.m > 0 && I.mom == nullptr) return MUON_E_INVALID;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != p->device) return MUON_E_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  muon::StepArgs a{};
+  a.mats = p->d_mats;
+  a.ws = static_cast<char*>(ws);
+  a.parts = static_cast<float*>(ws);
+  a.a = cfg->a;
+  a.b = cfg->b;
+  a.c = cfg->c;
+  a.mu = use_mom ? cfg->momentum : 0.f;
+  a.eps = cfg->eps;
+  a.nesterov = cfg->nesterov;
+  a.use_mom = use_mom ? 1 : 0;
+  a.direct = cfg->steps == 0 ? 1 : 0;
+
+  auto launch = [&](int kind) -> muon_status {
+    a.items = p->d_items[kind];
+    TimedLaunch t{kind, nullptr, nullptr};
+    if (p->timing) {
+      t.start = get_event(p);
+      t.stop = get_event(p);
+      if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
+    }
+    if (muon::launch_kernel(kind, H.dtype, a, p->grid[kind], s) != hipSuccess) return MUON_E_LAUNCH;
+    if (p->timing) {
+      if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
+      p->pending.push_back(t);
+    }
+    return MUON_OK;
+  };
+
+  if ((st = launch(MUON_K_MOMENTUM)) != MUON_OK) return st;
+  if ((st = launch(MUON_K_NORMALIZE)) != MUON_OK) return st;
+  for (int t = 0; t < cfg->steps; ++t) {
+    a.cur = t & 1;
+    a.last = t == cfg->steps - 1 ? 1 : 0;
+    if ((st = launch(MUON_K_GRAM)) != MUON_OK) return st;
+    if ((st = launch(MUON_K_POLY)) != MUON_OK) return st;
+    if ((st = launch(MUON_K_UPDATE)) != MUON_OK) return st;
+  }
+  return MUON_OK;
+}
+
+// ---- plan cache for muon_step / muon_orthogonalize
+
+struct CacheEntry {
+  std::string key;
+  muon_plan_s* plan;
+};
+std::mutex g_cache_mu;
+std::list<CacheEntry> g_cache;  // front = most recently used
+constexpr size_t kCacheMax = 16;
+
+std::string make_key(const muon_matrix* mats, int32_t n, muon_dtype dt) {
+  std::string k(reinterpret_cast<const char*>(&dt), sizeof(dt));
+  int dev = -1;
+  (void)hipGetDevice(&dev);
+  k.append(reinterpret_cast<const char*>(&dev), sizeof(dev));
+  if (n > 0) k.append(reinterpret_cast<const char*>(mats), sizeof(muon_matrix) * size_t(n));
+  return k;
+}
+
+muon_status cached_step(const muon_matrix* mats, int32_t n, muon_dtype dt, const muon_config* cfg,
+                        void* ws, size_t ws_bytes, void* stream, bool ortho) {
+  muon_status st = muon::validate_config(cfg);
+  if (st != MUON_OK) return st;
+  st = muon::validate_matrices(mats, n, dt, !ortho && cfg->momentum != 0.f);
+  if (st != MUON_OK) return st;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  const std::string key = make_key(mats, n, dt);
+  for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
+    if (it->key == key) {
+      g_cache.splice(g_cache.begin(), g_cache, it);
+      return step_impl(it->plan, cfg, ws, ws_bytes, stream, ortho);
+    }
+  }
+  muon_plan_s* p = new (std::nothrow) muon_plan_s();
+  if (!p) return MUON_E_ALLOC;
+  st = muon::build_plan(mats, n, dt, &p->host);
+  if (st != MUON_OK) {
+    delete p;
+    return st;
+  }
+  // check the workspace before allocating anything
+  if (p->host.ws_bytes > 0 &&
+      (ws == nullptr || ws_bytes < p->host.ws_bytes || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) {
+    delete p;
+    return MUON_E_WORKSPACE;
+  }
+  if ((st = upload(p)) != MUON_OK) {
+    delete p;
+    return st;
+  }
+  g_cache.push_front({key, p});
+  if (g_cache.size() > kCacheMax) {
+    release(g_cache.back().plan);
+    g_cache.pop_back();
+  }
+  return step_impl(p, cfg, ws, ws_bytes, stream, ortho);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+const char* muon_status_str(int32_t s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_E_INVALID: return "invalid argument";
+    case MUON_E_DTYPE: return "unsupported dtype";
+    case MUON_E_SHAPE: return "invalid shape";
+    case MUON_E_ALIGN: return "misaligned pointer";
+    case MUON_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MUON_E_DEVICE: return "no usable gfx950 device or HIP runtime error";
+    case MUON_E_LAUNCH: return "kernel launch failed";
+    case MUON_E_ALLOC: return "allocation failed";
+    default: return "unknown status";
+  }
+}
+
+muon_status muon_workspace_bytes(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                                 size_t* bytes) {
+  if (bytes == nullptr) return MUON_E_INVALID;
+  HostPlan P;
+  muon_status st = muon::build_plan(mats, n, dtype, &P);
+  if (st != MUON_OK) return st;
+  *bytes = P.ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                             muon_plan** plan) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  *plan = nullptr;
+  muon_plan_s* p = new (std::nothrow) muon_plan_s();
+  if (!p) return MUON_E_ALLOC;
+  muon_status st = muon::build_plan(mats, n, dtype, &p->host);
+  if (st == MUON_OK) st = upload(p);
+  if (st != MUON_OK) {
+    delete p;
+    return st;
+  }
+  *plan = p;
+  return MUON_OK;
+}
+
+muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return step_impl(plan, cfg, workspace, workspace_bytes, stream, false);
+}
+
+void muon_plan_destroy(muon_plan* plan) { release(plan); }
+
+muon_status muon_step(const muon_matrix* mats, int32_t n, muon_dtype dtype, const muon_config* cfg,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return cached_step(mats, n, dtype, cfg, workspace, workspace_bytes, stream, false);
+}
+
+muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                               const muon_config* cfg, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return cached_step(mats, n, dtype, cfg, workspace, workspace_bytes, stream, true);
+}
+
+muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype, int32_t kind,
+                                int32_t* items, int64_t cap, int64_t* count) {
+  if (count == nullptr || kind < 0 || kind >= MUON_K_COUNT || cap < 0 ||
+      (cap > 0 && items == nullptr))
+    return MUON_E_INVALID;
+  HostPlan P;
+  muon_status st = muon::build_plan(mats, n, dtype, &P);
+  if (st != MUON_OK) return st;
+  const auto& v = P.sched[kind].items;
+  *count = static_cast<int64_t>(v.size());
+  const int64_t w = std::min<int64_t>(cap, *count);
+  for (int64_t i = 0; i < w; ++i) {
+    items[4 * i + 0] = v[i].mat;
+    items[4 * i + 1] = v[i].a;
+    items[4 * i + 2] = v[i].b;
+    items[4 * i + 3] = v[i].c;
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  plan->timing = enable != 0;
+  return MUON_OK;
+}
+
+muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches) {
+  if (plan == nullptr || ms == nullptr || launches == nullptr) return MUON_E_INVALID;
+  for (auto& t : plan->pending) {
+    if (hipEventSynchronize(t.stop) != hipSuccess) return MUON_E_DEVICE;
+    float e = 0.f;
+    if (hipEventElapsedTime(&e, t.start, t.stop) != hipSuccess) return MUON_E_DEVICE;
+    plan->acc_ms[t.kind] += e;
+    plan->acc_n[t.kind] += 1;
+    plan->free_events.push_back(t.start);
+    plan->free_events.push_back(t.stop);
+  }
+  plan->pending.clear();
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    ms[k] = plan->acc_ms[k];
+    launches[k] = plan->acc_n[k];
+    plan->acc_ms[k] = 0.0;
+    plan->acc_n[k] = 0;
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffer_info* info) {
+  if (plan == nullptr || info == nullptr) return MUON_E_INVALID;
+  if (idx < 0 || idx >= static_cast<int32_t>(plan->host.info.size())) return MUON_E_INVALID;
+  const MatInfo& I = plan->host.info[idx];
+  info->m = I.m;
+  info->n = I.n;
+  info->mp = I.mp;
+  info->np = I.np;
+  info->x_master = I.xm_off;
+  info->x_op0 = I.xo_off[0];
+  info->x_op1 = I.xo_off[1];
+  info->gram = I.a_off;
+  info->poly = I.b_off;
+  return MUON_OK;
+}
+
+}  // extern "C"

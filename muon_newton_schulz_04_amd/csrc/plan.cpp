@@ -1,0 +1,262 @@
+// Host-side planning: validation, workspace layout and XCD-aware schedules.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+
+namespace muon {
+
+size_t elem_size(muon_dtype dt) { return dt == MUON_F32 ? 4 : 2; }
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+namespace {
+struct Interval {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool write;
+  int32_t mat;
+};
+}  // namespace
+
+muon_status validate_matrices(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                              bool need_momentum) {
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_E_DTYPE;
+  if (n < 0 || n > MUON_MAX_MATRICES) return MUON_E_SHAPE;
+  if (n > 0 && mats == nullptr) return MUON_E_INVALID;
+  const size_t es = elem_size(dtype);
+  std::vector<Interval> iv;
+  iv.reserve(3 * static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_matrix& M = mats[i];
+    if (M.rows < 0 || M.cols < 0 || M.rows > MUON_MAX_DIM || M.cols > MUON_MAX_DIM)
+      return MUON_E_SHAPE;
+    if (M.rows * M.cols > MUON_MAX_ELEMS) return MUON_E_SHAPE;
+    if (M.rows == 0 || M.cols == 0) continue;  // empty: skipped
+    if (M.ld < M.cols) return MUON_E_SHAPE;
+    if (M.ld > (int64_t(1) << 40)) return MUON_E_SHAPE;
+    if (M.grad == nullptr || M.out == nullptr) return MUON_E_INVALID;
+    if (need_momentum && M.momentum == nullptr) return MUON_E_INVALID;
+    auto misaligned = [es](const void* p) { return reinterpret_cast<uintptr_t>(p) % es != 0; };
+    if (misaligned(M.grad) || misaligned(M.out) || (M.momentum && misaligned(M.momentum)))
+      return MUON_E_ALIGN;
+    const uintptr_t span = static_cast<uintptr_t>(((M.rows - 1) * M.ld + M.cols) * es);
+    auto add = [&](const void* p, bool w) {
+      uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      iv.push_back({lo, lo + span, w, i});
+    };
+    add(M.out, true);
+    if (M.momentum) add(M.momentum, true);
+    if (M.grad != M.out) add(M.grad, false);
+  }
+  // Any overlap that involves a written buffer is an error (out may equal
+  // its own grad exactly; that case is not recorded above).
+  std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) { return x.lo < y.lo; });
+  // Sweep keeping the furthest-reaching interval seen so far, separately for
+  // written and for any interval: a new interval overlaps an earlier written
+  // one if it starts below the max end of the written ones, and a new written
+  // interval overlaps anything that ends after its start.
+  uintptr_t max_hi_any = 0, max_hi_w = 0;
+  for (const Interval& x : iv) {
+    if (x.lo < max_hi_w) return MUON_E_INVALID;
+    if (x.write && x.lo < max_hi_any) return MUON_E_INVALID;
+    max_hi_any = std::max(max_hi_any, x.hi);
+    if (x.write) max_hi_w = std::max(max_hi_w, x.hi);
+  }
+  return MUON_OK;
+}
+
+muon_status validate_config(const muon_config* cfg) {
+  if (cfg == nullptr) return MUON_E_INVALID;
+  if (!std::isfinite(cfg->a) || !std::isfinite(cfg->b) || !std::isfinite(cfg->c) ||
+      !std::isfinite(cfg->momentum) || !std::isfinite(cfg->eps))
+    return MUON_E_INVALID;
+  if (cfg->steps < 0 || cfg->steps > MUON_MAX_STEPS) return MUON_E_INVALID;
+  if (cfg->momentum < 0.f || cfg->momentum >= 1.f) return MUON_E_INVALID;
+  if (cfg->nesterov != 0 && cfg->nesterov != 1) return MUON_E_INVALID;
+  if (cfg->eps < 0.f) return MUON_E_INVALID;
+  return MUON_OK;
+}
+
+namespace {
+
+// A run of consecutive work items of one matrix, with its summed cost.
+struct Chunk {
+  int32_t mat;
+  std::vector<WorkItem> items;
+  double cost;
+};
+
+// Distributes chunks over the XCDs (longest-processing-time first, ties by
+// lower XCD), keeps each XCD's chunks in matrix order, and interleaves the
+// per-XCD lists so that block b (dispatched to XCD b % 8) takes the
+// (b / 8)-th item of its XCD's list. Work of one matrix thus stays on one
+// XCD (one L2) while the eight XCDs get about equal cost.
+Schedule assign_xcd(std::vector<Chunk> chunks) {
+  std::vector<size_t> order(chunks.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t x, size_t y) { return chunks[x].cost > chunks[y].cost; });
+  std::vector<double> load(kNumXcd, 0.0);
+  std::vector<std::vector<size_t>> bins(kNumXcd);
+  for (size_t ci : order) {
+    int best = 0;
+    for (int x = 1; x < kNumXcd; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += chunks[ci].cost;
+    bins[best].push_back(ci);
+  }
+  std::vector<std::vector<WorkItem>> lists(kNumXcd);
+  size_t longest = 0;
+  for (int x = 0; x < kNumXcd; ++x) {
+    std::sort(bins[x].begin(), bins[x].end());  // chunk index order = matrix order
+    for (size_t ci : bins[x])
+      lists[x].insert(lists[x].end(), chunks[ci].items.begin(), chunks[ci].items.end());
+    longest = std::max(longest, lists[x].size());
+  }
+  Schedule s;
+  s.items.assign(longest * kNumXcd, WorkItem{-1, -1, -1, -1});
+  for (int x = 0; x < kNumXcd; ++x)
+    for (size_t p = 0; p < lists[x].size(); ++p) s.items[p * kNumXcd + x] = lists[x][p];
+  return s;
+}
+
+// Splits each matrix's item list into chunks of at most `max_cost`.
+void add_matrix_chunks(std::vector<Chunk>& chunks, int32_t mat, const std::vector<WorkItem>& items,
+                       const std::vector<double>& costs, double max_cost) {
+  Chunk cur{mat, {}, 0.0};
+  for (size_t i = 0; i < items.size(); ++i) {
+    if (!cur.items.empty() && cur.cost + costs[i] > max_cost) {
+      chunks.push_back(std::move(cur));
+      cur = Chunk{mat, {}, 0.0};
+    }
+    cur.items.push_back(items[i]);
+    cur.cost += costs[i];
+  }
+  if (!cur.items.empty()) chunks.push_back(std::move(cur));
+}
+
+}  // namespace
+
+muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, HostPlan* out) {
+  muon_status st = validate_matrices(mats, n, dtype, false);
+  if (st != MUON_OK) return st;
+  HostPlan P;
+  P.dtype = dtype;
+  P.mats.assign(mats, mats + n);
+  P.info.resize(n);
+  const size_t es = elem_size(dtype);
+  const bool bf16 = dtype == MUON_BF16;
+
+  // Per-matrix layout; the partials region comes first.
+  int32_t nparts = 0;
+  std::vector<std::vector<WorkItem>> items(MUON_K_COUNT);
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_matrix& M = mats[i];
+    MatInfo& I = P.info[i];
+    I = MatInfo{};
+    I.grad = M.grad;
+    I.mom = M.momentum;
+    I.out = M.out;
+    I.ld = M.ld;
+    I.rows = static_cast<int32_t>(M.rows);
+    I.cols = static_cast<int32_t>(M.cols);
+    I.xm_off = I.xo_off[0] = I.xo_off[1] = I.a_off = I.b_off = -1;
+    if (M.rows == 0 || M.cols == 0) continue;
+    I.tall = M.rows > M.cols;
+    I.m = static_cast<int32_t>(std::min(M.rows, M.cols));
+    I.n = static_cast<int32_t>(std::max(M.rows, M.cols));
+    I.mp = static_cast<int32_t>(round_up(I.m, kGemmTile));
+    I.np = static_cast<int32_t>(round_up(I.n, kGemmTile));
+    auto aligned16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    I.vec_ok = aligned16(M.grad) && aligned16(M.out) && (!M.momentum || aligned16(M.momentum)) &&
+               (M.ld * es) % 16 == 0 && (M.cols * es) % 16 == 0;
+    const int32_t rows_per_item =
+        static_cast<int32_t>(std::max<int64_t>(1, kMomentumElems / M.cols));
+    I.part_off = nparts;
+    I.part_cnt = static_cast<int32_t>((M.rows + rows_per_item - 1) / rows_per_item);
+    nparts += I.part_cnt;
+  }
+  P.total_partials = nparts;
+  size_t off = round_up(static_cast<int64_t>(nparts) * 4, kWsAlign);
+  auto take = [&off](size_t bytes) {
+    int64_t o = static_cast<int64_t>(off);
+    off = round_up(static_cast<int64_t>(off + bytes), kWsAlign);
+    return o;
+  };
+  for (int32_t i = 0; i < n; ++i) {
+    MatInfo& I = P.info[i];
+    if (I.m == 0) continue;
+    const size_t xel = static_cast<size_t>(I.mp) * I.np;
+    const size_t ael = static_cast<size_t>(I.mp) * I.mp;
+    if (bf16) {
+      I.xm_off = take(xel * 4);
+      I.xo_off[0] = take(xel * 2);
+      I.xo_off[1] = take(xel * 2);
+      I.a_off = take(ael * 2);
+      I.b_off = take(ael * 2);
+    } else {
+      I.xo_off[0] = take(xel * 4);
+      I.xo_off[1] = take(xel * 4);
+      I.a_off = take(ael * 4);
+      I.b_off = take(ael * 4);
+    }
+  }
+  P.ws_bytes = n == 0 || off == 0 ? 0 : off;
+  bool any = false;
+  for (const MatInfo& I : P.info) any = any || I.m > 0;
+  if (!any) P.ws_bytes = 0;
+
+  // Work items and their costs, per kernel.
+  double total_cost[MUON_K_COUNT] = {0, 0, 0, 0, 0};
+  std::vector<std::vector<std::vector<WorkItem>>> per(MUON_K_COUNT,
+                                                      std::vector<std::vector<WorkItem>>(n));
+  std::vector<std::vector<std::vector<double>>> cost(MUON_K_COUNT,
+                                                     std::vector<std::vector<double>>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const MatInfo& I = P.info[i];
+    if (I.m == 0) continue;
+    const int32_t rows_per_item = static_cast<int32_t>(std::max<int64_t>(1, kMomentumElems / I.cols));
+    for (int32_t p = 0; p < I.part_cnt; ++p) {
+      int32_t r0 = p * rows_per_item;
+      int32_t nr = std::min(rows_per_item, I.rows - r0);
+      per[MUON_K_MOMENTUM][i].push_back({i, r0, nr, I.part_off + p});
+      cost[MUON_K_MOMENTUM][i].push_back(double(nr) * I.cols);
+    }
+    const int32_t nti = I.mp / kNormTile, ntj = I.np / kNormTile;
+    for (int32_t ti = 0; ti < nti; ++ti)
+      for (int32_t tj = 0; tj < ntj; ++tj) {
+        per[MUON_K_NORMALIZE][i].push_back({i, ti, tj, 0});
+        cost[MUON_K_NORMALIZE][i].push_back(1.0);
+      }
+    const int32_t gt = I.mp / kGemmTile, gn = I.np / kGemmTile;
+    for (int32_t ti = 0; ti < gt; ++ti)
+      for (int32_t tj = ti; tj < gt; ++tj) {
+        per[MUON_K_GRAM][i].push_back({i, ti, tj, 0});
+        cost[MUON_K_GRAM][i].push_back(double(I.np));
+        per[MUON_K_POLY][i].push_back({i, ti, tj, 0});
+        cost[MUON_K_POLY][i].push_back(double(I.mp));
+      }
+    // update: column panels outer so neighbouring tiles share the X panel
+    for (int32_t tj = 0; tj < gn; ++tj)
+      for (int32_t ti = 0; ti < gt; ++ti) {
+        per[MUON_K_UPDATE][i].push_back({i, ti, tj, 0});
+        cost[MUON_K_UPDATE][i].push_back(double(I.mp));
+      }
+    for (int k = 0; k < MUON_K_COUNT; ++k)
+      for (double c : cost[k][i]) total_cost[k] += c;
+  }
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    // chunks no larger than 1/32 of the total keep the XCD bins balanced even
+    // for sets with a few large matrices
+    const double max_cost = std::max(total_cost[k] / (4.0 * kNumXcd), 1.0);
+    std::vector<Chunk> chunks;
+    for (int32_t i = 0; i < n; ++i)
+      if (!per[k][i].empty()) add_matrix_chunks(chunks, i, per[k][i], cost[k][i], max_cost);
+    P.sched[k] = assign_xcd(std::move(chunks));
+  }
+  *out = std::move(P);
+  return MUON_OK;
+}
+
+}  // namespace muon

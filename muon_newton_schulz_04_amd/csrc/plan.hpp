@@ -1,0 +1,68 @@
+// Host-side planning for the Muon update: argument validation, per-matrix
+// workspace layout and the XCD-aware work schedules of every kernel.
+// Plain C++ (no HIP headers) so the same code runs in CPU-only tests.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/muon.h"
+
+namespace muon {
+
+// Tile sizes shared by the planner and the kernels.
+constexpr int kGemmTile = 128;         // output tile of the three matrix-core kernels
+constexpr int kNormTile = 64;          // tile of the normalise / layout kernel
+constexpr int kMomentumElems = 16384;  // target elements per momentum work item
+constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X
+constexpr size_t kWsAlign = 256;
+
+// Per-matrix record read by the kernels (device table; plain data).
+struct MatInfo {
+  const void* grad;
+  void* mom;
+  void* out;
+  int64_t ld;        // caller row stride (elements)
+  int32_t rows, cols;
+  int32_t m, n;      // m = min(rows, cols), n = max(rows, cols)
+  int32_t mp, np;    // m, n rounded up to kGemmTile
+  int32_t tall;      // rows > cols: the iteration runs on the transpose
+  int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
+  int64_t xm_off;    // fp32 master X (bf16 sets), -1 otherwise
+  int64_t xo_off[2]; // operand copies (bf16) / ping-pong masters (fp32)
+  int64_t a_off;     // A = X X^T
+  int64_t b_off;     // B = b A + c A A
+  int32_t part_off;  // first slot of this matrix's sum-of-squares partials
+  int32_t part_cnt;
+};
+
+struct WorkItem {
+  int32_t mat, a, b, c;
+};
+
+struct Schedule {
+  std::vector<WorkItem> items;  // launch order; block i runs items[i]; mat < 0 = empty
+};
+
+struct HostPlan {
+  muon_dtype dtype = MUON_BF16;
+  std::vector<muon_matrix> mats;
+  std::vector<MatInfo> info;
+  Schedule sched[MUON_K_COUNT];
+  int32_t total_partials = 0;
+  size_t ws_bytes = 0;
+};
+
+// Validates the matrix set (shapes, dtype, alignment, overlaps).
+muon_status validate_matrices(const muon_matrix* mats, int32_t n, muon_dtype dtype,
+                              bool need_momentum);
+// Validates per-call scalars.
+muon_status validate_config(const muon_config* cfg);
+// Builds the full host plan (no device calls). need_momentum: momentum
+// pointers are part of the set (false for orthogonalisation-only plans).
+muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, HostPlan* out);
+
+size_t elem_size(muon_dtype dt);
+
+}  // namespace muon

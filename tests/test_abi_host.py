@@ -1,0 +1,180 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls):
+exported symbols, status strings, argument validation, workspace sizing and
+the work schedules of every kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import muon_newton_schulz_04_amd as mu
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mu.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return mu.load_library()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(muon_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in muon.h but not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert mu.muon_abi_version() == 1
+    for code in range(9):
+        s = mu.muon_status_str(code)
+        assert s and s != "unknown status"
+    assert mu.muon_status_str(99) == "unknown status"
+
+
+def arr_of(rows_cols_ld_ptrs):
+    arr = (mu.MuonMatrix * max(1, len(rows_cols_ld_ptrs)))()
+    for i, t in enumerate(rows_cols_ld_ptrs):
+        arr[i] = mu.MuonMatrix(*t)
+    return arr
+
+
+def ws_status(lib, mats, dtype=mu.MUON_BF16, n=None):
+    out = ctypes.c_size_t(0)
+    return lib.muon_workspace_bytes(arr_of(mats), len(mats) if n is None else n, dtype,
+                                    ctypes.byref(out)), out.value
+
+
+B = 1 << 40
+
+
+@pytest.mark.parametrize("mats,want", [
+    ([(-1, 4, 4, B, B + 4096, B + 8192)], 3),               # negative rows
+    ([(4, 8, 4, B, B + 4096, B + 8192)], 3),                # ld < cols
+    ([(70000, 8, 8, B, B + 4 << 20, B + 8 << 20)], 3),      # rows > max dim
+    ([(40000, 40000, 40000, B, B + (4 << 32), B + (8 << 32))], 3),  # too many elements
+    ([(4, 8, 8, 0, B, B + 4096)], 1),                       # NULL grad
+    ([(4, 8, 8, B, B + 4096, 0)], 1),                       # NULL out
+    ([(4, 8, 8, B + 1, B + 4096, B + 8192)], 4),            # misaligned grad
+    ([(4, 8, 8, B, B + 4096, B + 40)], 1),                  # out overlaps grad (not equal)
+    ([(4, 8, 8, B, B + 40, B + 8192)], 1),                  # momentum overlaps grad
+    ([(4, 8, 8, B, B + 4096, B + 8192), (4, 8, 8, B + 8192, B + 12288, B + 16384)], 1),  # out0 = grad1
+])
+def test_validation_errors(lib, mats, want):
+    st, _ = ws_status(lib, mats)
+    assert st == want
+
+
+def test_validation_accepts_aliasing_out_and_grad_and_empty(lib):
+    st, nb = ws_status(lib, [(4, 8, 8, B, B + 4096, B)])
+    assert st == 0 and nb > 0
+    st, nb = ws_status(lib, [(0, 8, 8, B, B + 4096, B + 8192), (5, 0, 0, 0, 0, 0)])
+    assert st == 0 and nb == 0
+    st, nb = ws_status(lib, [], n=0)
+    assert st == 0 and nb == 0
+    assert ws_status(lib, [(4, 8, 8, B, B + 4096, B + 8192)], dtype=7)[0] == 2
+    assert ws_status(lib, [(4, 8, 8, B, B + 4096, B + 8192)], n=-1)[0] == 3
+
+
+def test_config_validation_before_any_device_call(lib):
+    mats = arr_of([(4, 8, 8, B, B + 4096, B + 8192)])
+    bad = [mu.make_config(1, 0, 0, 65), mu.make_config(1, 0, 0, -1),
+           mu.make_config(float("nan"), 0, 0, 1), mu.make_config(1, 0, 0, 1, momentum=1.0),
+           mu.make_config(1, 0, 0, 1, momentum=-0.1), mu.make_config(1, 0, 0, 1, eps=-1.0)]
+    for cfg in bad:
+        assert lib.muon_step(mats, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 1
+    cfg = mu.make_config(1, 0, 0, 1, momentum=0.9)
+    nomom = arr_of([(4, 8, 8, B, 0, B + 8192)])   # momentum NULL with mu != 0
+    assert lib.muon_step(nomom, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 1
+    assert lib.muon_step(mats, 1, mu.MUON_BF16, None, None, 0, None) == 1
+    assert lib.muon_plan_step(None, ctypes.byref(cfg), None, 0, None) == 1
+
+
+def expected_ws(shapes, dtype):
+    def ru(x, m):
+        return (x + m - 1) // m * m
+    parts = 0
+    for r, c in shapes:
+        rpi = max(1, 16384 // c)
+        parts += (r + rpi - 1) // rpi
+    off = ru(parts * 4, 256)
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        mp, np_ = ru(m, 128), ru(n, 128)
+        sizes = ([mp * np_ * 4, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
+                 if dtype == mu.MUON_BF16 else
+                 [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
+        for s in sizes:
+            off = ru(off + s, 256)
+    return off
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_bytes_formula(lib, name):
+    cfg = CONFIGS[name]
+    dt = mu.MUON_F32 if cfg.dtype == "fp32" else mu.MUON_BF16
+    assert mu.muon_workspace_bytes(list(cfg.shapes), dt) == expected_ws(cfg.shapes, dt)
+
+
+SHAPE_SETS = {
+    "gpt2_124m": list(CONFIGS["gpt2_124m_matrix_set"].shapes),
+    "ragged": [(200, 333), (333, 200), (1, 1), (129, 129), (64, 128), (700, 50)],
+    "one_big": [(4096, 1024)],
+}
+
+
+@pytest.mark.parametrize("setname", list(SHAPE_SETS))
+def test_schedules_cover_every_tile_exactly_once(lib, setname):
+    shapes = SHAPE_SETS[setname]
+    scheds = [mu.muon_schedule_query(shapes, mu.MUON_BF16, k) for k in range(5)]
+    for k, s in enumerate(scheds):
+        assert len(s) % 8 == 0, "grid is a multiple of the XCD count"
+        empty = s[:, 0] < 0
+        assert np.all(s[empty] == -1)
+    mom, nrm, gram, poly, upd = (s[s[:, 0] >= 0] for s in scheds)
+    slots = mom[:, 3]
+    assert len(np.unique(slots)) == len(slots) and slots.min() == 0 and slots.max() == len(slots) - 1
+    for i, (r, c) in enumerate(shapes):
+        m, n = min(r, c), max(r, c)
+        mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+        mi = mom[mom[:, 0] == i]
+        rows = np.zeros(r, int)
+        for _, r0, nr, _s in mi:
+            rows[r0:r0 + nr] += 1
+        assert np.all(rows == 1), "every row summed exactly once"
+        ni = nrm[nrm[:, 0] == i]
+        assert sorted(map(tuple, ni[:, 1:3])) == [(a, b) for a in range(mp // 64) for b in range(np_ // 64)]
+        want_tri = [(a, b) for a in range(mp // 128) for b in range(a, mp // 128)]
+        for s in (gram, poly):
+            si = s[s[:, 0] == i]
+            assert sorted(map(tuple, si[:, 1:3])) == want_tri
+        ui = upd[upd[:, 0] == i]
+        assert sorted(map(tuple, ui[:, 1:3])) == [(a, b) for a in range(mp // 128) for b in range(np_ // 128)]
+
+
+def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):
+    shapes = SHAPE_SETS["gpt2_124m"]
+    s = mu.muon_schedule_query(shapes, mu.MUON_BF16, 2)
+    cost = np.zeros(8)
+    owner = {}
+    split = 0
+    for b, (mat, ti, tj, _) in enumerate(s):
+        if mat < 0:
+            continue
+        x = b % 8
+        cost[x] += max(shapes[mat])
+        if owner.setdefault(mat, x) != x:
+            split += 1
+    assert cost.max() / cost.mean() < 1.1
+    assert split <= 8

@@ -1,0 +1,260 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bar (per matrix, relative Frobenius error): 2e-2 for bf16 sets, 1e-4 for
+fp32 sets; momentum buffers within one bf16 ulp of the oracle's rounding.
+The oracle receives the same seeded inputs and the float32 values of the
+scalars the C ABI takes (a, b, c, mu, eps are floats there).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_gradients, to_f64
+
+pytestmark = pytest.mark.gpu
+
+mu = pytest.importorskip("muon_newton_schulz_04_amd")
+DEV = "cuda"
+QUINTIC = CONFIGS["gpt2_small_block"].coeffs
+CUBIC = (1.5, -0.5, 0.0)
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+TDT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def rel(got, want):
+    nw = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (nw if nw > 0 else 1.0))
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu_call(grads, bufs, coeffs, steps, momentum=0.0, nesterov=False, eps=1e-7,
+             ortho=False, outs=None):
+    """grads/bufs: device tensors. Returns (outs, bufs) as float64 arrays."""
+    if outs is None:
+        outs = [torch.empty_like(g) for g in grads]
+    cfg = mu.make_config(*coeffs, steps, momentum, nesterov, eps)
+    if ortho:
+        mu.muon_orthogonalize(grads, outs, cfg)
+    else:
+        mu.muon_step(grads, bufs, outs, cfg)
+    torch.cuda.synchronize()
+    return [to_f64(o) for o in outs], (None if bufs is None else [to_f64(b) for b in bufs])
+
+
+def oracle_call(grads64, bufs64, coeffs, steps, momentum=0.0, nesterov=False, eps=1e-7,
+                buf_dtype="bf16"):
+    a, b, c = (f32(x) for x in coeffs)
+    outs, nbs = [], []
+    for i, g in enumerate(grads64):
+        o, nb = oracle.muon_update(g, None if bufs64 is None else bufs64[i], a=a, b=b, c=c,
+                                   steps=steps, mu=f32(momentum), nesterov=nesterov,
+                                   eps=f32(eps), buf_dtype=buf_dtype)
+        outs.append(o)
+        nbs.append(nb)
+    return outs, nbs
+
+
+def check_buffers(got, want, dtype):
+    for gb, wb in zip(got, want):
+        if dtype == "fp32":
+            assert np.allclose(gb, wb, rtol=1e-6, atol=1e-30)
+            continue
+        # one bf16 ulp at most, and rarely (float32 vs float64 before rounding)
+        ulp = np.abs(wb) * 2.0 ** -7 + 1e-38
+        d = np.abs(gb - wb)
+        assert np.all(d <= ulp), float(np.max(d / ulp))
+        assert np.mean(d > 0) < 1e-3
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+def test_tiny_fp32_cubic_polar():
+    cfg = CONFIGS["tiny_fp32_64x128_cubic"]
+    g = make_gradients(cfg)[0]
+    say(f"tiny fp32 {tuple(g.shape)} cubic k={cfg.steps}")
+    outs, _ = gpu_call([g.to(DEV)], None, cfg.coeffs, cfg.steps, ortho=True)
+    want, _ = oracle_call([to_f64(g)], None, cfg.coeffs, cfg.steps)
+    assert rel(outs[0], want[0]) < 1e-4
+    U, _, Vt = np.linalg.svd(to_f64(g), full_matrices=False)
+    assert rel(outs[0], U @ Vt) < 1e-3
+
+
+# ------------------------------------------------------- sub-steps, ragged
+
+RAGGED = [(200, 333), (333, 200), (129, 257), (64, 128), (1, 5), (5, 1), (128, 128),
+          (300, 300), (7, 1000), (1000, 7)]
+CASES = {
+    "x0_only": (QUINTIC, 0),
+    "identity": ((1.0, 0.0, 0.0), 1),
+    "gram_times_x": ((0.0, 1.0, 0.0), 1),
+    "gram_sq_times_x": ((0.0, 0.0, 1.0), 1),
+    "quintic5": (QUINTIC, 5),
+    "cubic3": (CUBIC, 3),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", list(CASES))
+def test_substeps_ragged(dtype, case):
+    coeffs, steps = CASES[case]
+    wl = CONFIGS["gpt2_small_block"]
+    grads = make_gradients(wl, step=3, shapes=RAGGED)
+    grads = [g.to(TDT[dtype]) for g in grads]
+    bufs = [torch.randn(g.shape, generator=torch.Generator().manual_seed(i)).to(g.dtype)
+            for i, g in enumerate(grads)]
+    say(f"substeps {dtype} {case} shapes={RAGGED}")
+    outs, nbufs = gpu_call([g.to(DEV) for g in grads], [b.to(DEV) for b in bufs], coeffs, steps,
+                           momentum=0.9, nesterov=True)
+    want, wbufs = oracle_call([to_f64(g) for g in grads], [to_f64(b) for b in bufs], coeffs,
+                              steps, momentum=0.9, nesterov=True, buf_dtype=dtype)
+    for shp, o, w in zip(RAGGED, outs, want):
+        assert o.shape == w.shape
+        e = rel(o, w)
+        assert e < TOL[dtype], (shp, e)
+    check_buffers(nbufs, wbufs, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_plain_momentum_and_no_momentum(dtype):
+    wl = CONFIGS["gpt2_small_block"]
+    shapes = [(256, 384), (384, 256)]
+    grads = [g.to(TDT[dtype]) for g in make_gradients(wl, step=4, shapes=shapes)]
+    bufs = [(0.5 * g.float()).to(g.dtype) for g in grads]
+    for momentum, nesterov in [(0.8, False), (0.0, False)]:
+        say(f"momentum={momentum} nesterov={nesterov} {dtype}")
+        outs, nb = gpu_call([g.to(DEV) for g in grads], [b.to(DEV) for b in bufs], QUINTIC, 5,
+                            momentum=momentum, nesterov=nesterov)
+        want, wb = oracle_call([to_f64(g) for g in grads], [to_f64(b) for b in bufs], QUINTIC, 5,
+                               momentum=momentum, nesterov=nesterov, buf_dtype=dtype)
+        for o, w in zip(outs, want):
+            assert rel(o, w) < TOL[dtype]
+        if momentum:
+            check_buffers(nb, wb, dtype)
+        else:
+            for b0, b1 in zip(bufs, nb):      # untouched without momentum
+                assert np.array_equal(to_f64(b0), b1)
+
+
+# ------------------------------------------------------------ GPU invariants
+
+def test_gram_is_bitwise_symmetric_and_padding_zero():
+    shapes = [(200, 333), (333, 200), (256, 512)]
+    grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=5, shapes=shapes)]
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, None, outs)
+    ws = plan.step(mu.make_config(*QUINTIC, 1))
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        info = plan.buffer_info(i)
+        mp, m = info["mp"], info["m"]
+        for key in ("gram", "poly"):
+            off = info[key]
+            A = ws[off: off + mp * mp * 2].view(torch.bfloat16).view(mp, mp).float().cpu()
+            assert torch.equal(A, A.t()), key
+            assert torch.count_nonzero(A[m:, :]) == 0 and torch.count_nonzero(A[:, m:]) == 0
+        # trace(A) = ||X0||_F^2 = (||u|| / (||u|| + eps))^2 ~ 1
+        off = info["gram"]
+        A = ws[off: off + mp * mp * 2].view(torch.bfloat16).view(mp, mp).double().cpu()
+        assert abs(float(torch.trace(A)) - 1.0) < 1e-2
+    plan.destroy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_deterministic_odd_and_scale_invariant(dtype):
+    shapes = [(256, 640), (640, 256)]
+    grads = [g.to(TDT[dtype]).to(DEV) for g in
+             make_gradients(CONFIGS["gpt2_small_block"], step=6, shapes=shapes)]
+    o1, _ = gpu_call(grads, None, QUINTIC, 5, ortho=True)
+    o2, _ = gpu_call(grads, None, QUINTIC, 5, ortho=True)
+    on, _ = gpu_call([-g for g in grads], None, QUINTIC, 5, ortho=True)
+    o4, _ = gpu_call([g * 4 for g in grads], None, QUINTIC, 5, ortho=True)  # exact scaling
+    for a, b, n, s in zip(o1, o2, on, o4):
+        assert np.array_equal(a, b)
+        assert np.array_equal(n, -a)
+        assert rel(s, a) < 1e-5
+
+
+def test_zero_matrix_empty_matrix_and_aliasing():
+    g = [torch.zeros(130, 70, dtype=torch.bfloat16, device=DEV),
+         torch.empty(0, 64, dtype=torch.bfloat16, device=DEV),
+         torch.randn(96, 160, device=DEV).to(torch.bfloat16)]
+    g_copy = [x.clone() for x in g]
+    outs = [torch.full_like(x, 7.0) for x in g]
+    outs[2] = g[2]                      # out aliases grad
+    bufs = [torch.zeros_like(x) for x in g]
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True)
+    mu.muon_step(g, bufs, outs, cfg)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(outs[0]) == 0 and torch.isfinite(outs[0].float()).all()
+    want, _ = oracle_call([to_f64(g_copy[2])], [np.zeros((96, 160))], QUINTIC, 5, 0.95, True)
+    assert rel(to_f64(outs[2]), want[0]) < 2e-2
+
+
+# ------------------------------------------------------ full configurations
+
+def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu"):
+    wl = CONFIGS[name]
+    say(f"config {name}: {wl.n_matrices} matrices")
+    grads_cpu = None
+    bufs = None
+    outs = None
+    buf64 = None
+    for s in step_seeds:
+        grads = make_gradients(wl, step=s, device=device_gen)
+        grads_dev = [g.to(DEV) for g in grads]
+        if bufs is None:
+            bufs = [torch.zeros_like(g) for g in grads_dev]
+            outs = [torch.empty_like(g) for g in grads_dev]
+            buf64 = [np.zeros(g.shape) for g in grads]
+        # sampled matrices: first and last of every shape group
+        groups = {}
+        for i, shp in enumerate(wl.shapes):
+            groups.setdefault(shp, []).append(i)
+        k = max(1, sample_per_group // 2)
+        sample = sorted({i for idx in groups.values() for i in idx[:k] + idx[-k:]})
+        g_sample = {i: to_f64(grads[i]) for i in sample}
+        cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
+        mu.muon_step(grads_dev, bufs, outs, cfg)
+        torch.cuda.synchronize()
+        for i in sample:
+            want, nb = oracle.muon_update(g_sample[i], buf64[i], a=f32(wl.coeffs[0]),
+                                          b=f32(wl.coeffs[1]), c=f32(wl.coeffs[2]),
+                                          steps=wl.steps, mu=f32(wl.momentum),
+                                          nesterov=wl.nesterov, eps=f32(wl.eps))
+            buf64[i] = to_f64(bufs[i])       # continue from the GPU's (checked) buffer
+            check_buffers([buf64[i]], [nb], wl.dtype)
+            e = rel(to_f64(outs[i]), want)
+            say(f"  seed {s} matrix {i} {wl.shapes[i]} rel err {e:.3e}")
+            assert e < wl.tol, (i, e)
+        for i in range(len(outs)):        # every matrix: finite, singular values bounded
+            o = outs[i].float()
+            assert torch.isfinite(o).all()
+            m = min(o.shape)
+            assert float(torch.linalg.matrix_norm(o)) <= 1.21 * m ** 0.5
+    return outs
+
+
+def test_config_gpt2_small_block_two_steps():
+    run_config("gpt2_small_block", sample_per_group=6, step_seeds=(0, 1))
+
+
+def test_config_gpt2_124m_matrix_set():
+    run_config("gpt2_124m_matrix_set")
+
+
+@pytest.mark.slow
+def test_config_gpt2_350m_matrix_set():
+    run_config("gpt2_350m_matrix_set")
+
+
+@pytest.mark.slow
+def test_config_wide_powerlaw():
+    run_config("wide_2048x8192_powerlaw", device_gen=DEV)
