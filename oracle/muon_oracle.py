@@ -94,8 +94,9 @@ _ROUND = {"bf16": bf16_round, "fp32": fp32_round, "f64": lambda x: np.asarray(x,
 def momentum_update(g, buf, mu: float, nesterov: bool, buf_dtype: str = "bf16"):
     """Momentum step of the Muon update. Returns (u, new_buf).
 
-    buf' = mu * buf + g, rounded to the buffer's storage dtype; the vector
-    that is orthogonalised is u = g + mu * buf' (Nesterov) or u = buf'.
+    buf' = mu * buf + g, rounded to the buffer's storage dtype (via the
+    float32 fused multiply-add value for bf16/fp32 buffers); the vector that
+    is orthogonalised is u = g + mu * buf' (Nesterov) or u = buf'.
     With mu == 0 (no momentum state) u = g and buf is ignored.
     [MUON]: Muon keeps a single momentum buffer per hidden matrix.
     """
@@ -103,7 +104,14 @@ def momentum_update(g, buf, mu: float, nesterov: bool, buf_dtype: str = "bf16"):
     if mu == 0.0 or buf is None:
         return g.copy(), None
     buf = np.asarray(buf, dtype=np.float64)
-    new_buf = _ROUND[buf_dtype](mu * buf + g)
+    acc = mu * buf + g              # exact for bf16/fp32 state and float32 mu
+    if buf_dtype in ("bf16", "fp32"):
+        # The stored buffer is a quantisation of mu*buf + g. The decision is
+        # taken in the precision the update is computed in: one float32
+        # fused multiply-add (a single rounding of the exact value), then
+        # rounding to the buffer's storage type.
+        acc = fp32_round(acc)
+    new_buf = _ROUND[buf_dtype](acc)
     u = g + mu * new_buf if nesterov else new_buf.copy()
     return u, new_buf
 

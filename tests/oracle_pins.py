@@ -98,10 +98,22 @@ def pin_momentum_bf16_state(impl):
     u1, b1 = impl.momentum_update(g1, np.zeros_like(g1), mu, True, "bf16")
     assert np.array_equal(b1, g1) and np.array_equal(u1, g1 + mu * g1)   # u = (1+mu) g
     u2, b2 = impl.momentum_update(g2, b1, mu, True, "bf16")
-    want_b2 = torch.tensor(mu * g1 + g2, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    # float32 FMA value (torch: exact float64 value cast once to float32),
+    # then float32 -> bfloat16 (torch's round-to-nearest-even cast)
+    want_b2 = torch.tensor(mu * g1 + g2, dtype=torch.float64).float().to(torch.bfloat16)
+    want_b2 = want_b2.double().numpy()
     assert np.array_equal(b2, want_b2)
     assert np.array_equal(u2, g2 + mu * want_b2)
     assert not np.array_equal(b2, mu * g1 + g2)   # rounding actually happened
+    # a case where rounding the exact value directly would differ: mu32*b + g
+    # lies just below the bf16 tie 2.0234375, its float32 rounding sits on the
+    # tie, and ties go to the even neighbour 2.03125 (not 2.015625)
+    mu32 = float(np.float32(0.9))
+    b, g = np.array([0.078125]), np.array([1.953125])     # both bfloat16 values
+    exact = mu32 * b + g
+    assert exact[0] < 2.0234375 and np.float32(exact[0]) == np.float32(2.0234375)
+    _, nb = impl.momentum_update(g, b, mu32, False, "bf16")
+    assert nb[0] == 2.03125
     u0, b0 = impl.momentum_update(g2, None, 0.0, True, "bf16")
     assert b0 is None and np.array_equal(u0, g2)
 

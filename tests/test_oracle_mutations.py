@@ -29,9 +29,9 @@ MUTATIONS = {
     "coeffs_swapped": ("x = ns_polynomial_step(x, a, b, c)", "x = ns_polynomial_step(x, a, c, b)"),
     "nesterov_old_buffer": ("u = g + mu * new_buf if nesterov", "u = g + mu * buf if nesterov"),
     "nesterov_ignored": ("u = g + mu * new_buf if nesterov else new_buf.copy()", "u = new_buf.copy()"),
-    "buffer_not_rounded": ("new_buf = _ROUND[buf_dtype](mu * buf + g)", "new_buf = mu * buf + g"),
-    "ema_momentum": ("new_buf = _ROUND[buf_dtype](mu * buf + g)",
-                     "new_buf = _ROUND[buf_dtype](mu * buf + (1 - mu) * g)"),
+    "buffer_not_rounded": ("new_buf = _ROUND[buf_dtype](acc)", "new_buf = acc"),
+    "buffer_rounded_from_f64": ("        acc = fp32_round(acc)\n", "        pass\n"),
+    "ema_momentum": ("acc = mu * buf + g ", "acc = mu * buf + (1 - mu) * g "),
     "bf16_7_bits": ("np.rint(np.ldexp(f[normal], 8)), e[normal] - 8)",
                     "np.rint(np.ldexp(f[normal], 7)), e[normal] - 7)"),
     "bf16_truncate": ("np.rint(np.ldexp(f[normal], 8))", "np.trunc(np.ldexp(f[normal], 8))"),

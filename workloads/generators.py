@@ -35,6 +35,7 @@ def gaussian_matrix(rows: int, cols: int, rng: np.random.Generator) -> np.ndarra
 
 def spiked_matrix(rows: int, cols: int, rank: int, noise: float,
                   rng: np.random.Generator) -> np.ndarray:
+    rank = min(rank, rows, cols)          # tiny test shapes
     u = _orthonormal(rng, rows, rank)
     v = _orthonormal(rng, cols, rank)
     s = np.linspace(10.0, 1.0, rank)
