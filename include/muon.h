@@ -14,9 +14,12 @@
  *   k times:  A = X X^T;  B = b A + c A A;  X = a X + B X
  *   out  = X (transposed back), stored at the set's dtype (RNE)
  *
- * Arithmetic: bf16 sets multiply bf16 operands on the matrix cores with fp32
- * accumulation and keep X in an fp32 master copy (momentum and norms in
- * fp32); fp32 sets compute in fp32 throughout.
+ * Arithmetic: momentum, norms and the X master copy are fp32. The matrix
+ * products run on the matrix cores with fp32 accumulation; their operands
+ * (X, A, B) are fp16 for bf16 sets by default (MUON_PRECISION_DEFAULT:
+ * 11-bit significands at the same MFMA rate as bf16, and every iterate is
+ * bounded by the normalisation) or bf16 (MUON_PRECISION_BF16_OPERANDS);
+ * fp32 sets use fp32 operands throughout.
  *
  * Conventions shared by every entry point:
  *  - Pointers in muon_matrix, `workspace` and `stream` are device-side
@@ -82,18 +85,25 @@ typedef struct {
   void* out;
 } muon_matrix;
 
+/* Operand format of the matrix products (see the top of this file). */
+typedef enum { MUON_PRECISION_DEFAULT = 0, MUON_PRECISION_BF16_OPERANDS = 1 } muon_precision;
+
 /* Per-call scalars. (a, b, c) are the odd polynomial's coefficients
  * p(x) = a x + b x^3 + c x^5 (e.g. the quintic (3.4445, -4.7750, 2.0315) or
  * the cubic (1.5, -0.5, 0)); steps in [0, MUON_MAX_STEPS] (0 returns X0);
  * momentum mu in [0, 1) (0: no momentum state, u = G); nesterov 0 or 1;
- * eps >= 0 is added to ||u||_F (1e-7 is the usual value). All must be
- * finite. */
+ * eps >= 0 is added to ||u||_F (1e-7 is the usual value); precision is a
+ * muon_precision value (ignored for fp32 sets). All must be finite. With
+ * fp16 operands the iterates must stay below 65504 in magnitude, which
+ * holds for polynomials that keep [0, 1] inside [-2, 2] over the steps
+ * (all Newton-Schulz coefficient sets in use do). */
 typedef struct {
   float a, b, c;
   int32_t steps;
   float momentum;
   int32_t nesterov;
   float eps;
+  int32_t precision;
 } muon_config;
 
 /* Opaque plan: validated shapes, per-matrix workspace layout and the tile

@@ -19,7 +19,7 @@ __all__ = [
     "muon_workspace_bytes", "muon_plan_create", "muon_plan_step", "muon_plan_destroy",
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
-    "MUON_F32", "MUON_BF16",
+    "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT", "MUON_PRECISION_BF16_OPERANDS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmuon_mi355x.so")
@@ -44,7 +44,8 @@ class MuonMatrix(ctypes.Structure):
 class MuonConfig(ctypes.Structure):
     _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
                 ("steps", ctypes.c_int32), ("momentum", ctypes.c_float),
-                ("nesterov", ctypes.c_int32), ("eps", ctypes.c_float)]
+                ("nesterov", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("precision", ctypes.c_int32)]
 
 
 class MuonBufferInfo(ctypes.Structure):
@@ -164,9 +165,13 @@ def _shape_matrices(shapes: Sequence, dtype: int):
     return arr, n
 
 
+MUON_PRECISION_DEFAULT, MUON_PRECISION_BF16_OPERANDS = 0, 1
+
+
 def make_config(a: float, b: float, c: float, steps: int, momentum: float = 0.0,
-                nesterov: bool = False, eps: float = 1e-7) -> MuonConfig:
-    return MuonConfig(a, b, c, int(steps), momentum, 1 if nesterov else 0, eps)
+                nesterov: bool = False, eps: float = 1e-7,
+                precision: int = MUON_PRECISION_DEFAULT) -> MuonConfig:
+    return MuonConfig(a, b, c, int(steps), momentum, 1 if nesterov else 0, eps, int(precision))
 
 
 def _stream_handle(stream) -> Optional[int]:

@@ -138,7 +138,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
       t.stop = get_event(p);
       if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
     }
-    if (muon::launch_kernel(kind, H.dtype, a, p->grid[kind], s) != hipSuccess) return MUON_E_LAUNCH;
+    if (muon::launch_kernel(kind, H.dtype, cfg->precision, a, p->grid[kind], s) != hipSuccess) return MUON_E_LAUNCH;
     if (p->timing) {
       if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
       p->pending.push_back(t);

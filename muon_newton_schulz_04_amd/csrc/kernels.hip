@@ -11,8 +11,8 @@
 //
 // The three matrix-core kernels share one 128 x 128 output-tile engine:
 // 4 waves of 64 lanes, each wave owning a 64 x 64 sub-tile made of 4 x 4
-// v_mfma_f32_16x16x32_bf16 (bf16 sets) or v_mfma_f32_16x16x4_f32 (fp32
-// sets) accumulators. Operands are staged through LDS as [row][k] tiles of
+// v_mfma_f32_16x16x32_{f16,bf16} (bf16 sets; fp16 operands by default) or
+// v_mfma_f32_16x16x4_f32 (fp32 sets) accumulators. Operands are staged through LDS as [row][k] tiles of
 // 128 rows x 128 bytes (16-byte chunks XOR-swizzled against bank conflicts);
 // the next k-slab is prefetched into registers while the current one is
 // multiplied. Operands whose k index runs along memory rows (X in B X) are
@@ -60,6 +60,43 @@ template <> struct Elem<uint16_t> {
     static_cast<uint16_t*>(p)[i] = f2bf(v);
   }
   static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
+};
+
+// Operand formats of the matrix products (X, A, B in the workspace).
+enum OpFmt { OP_F32 = 0, OP_F16 = 1, OP_BF16 = 2 };
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <int OP> struct Op;
+template <> struct Op<OP_F32> {
+  static constexpr int bytes = 4;
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+template <> struct Op<OP_F16> {
+  static constexpr int bytes = 2;
+  static __device__ __forceinline__ uint16_t bits(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));  // RNE
+  }
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(p)[i]));
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = bits(v);
+  }
+};
+template <> struct Op<OP_BF16> {
+  static constexpr int bytes = 2;
+  static __device__ __forceinline__ uint16_t bits(float v) { return f2bf(v); }
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return bf2f(static_cast<const uint16_t*>(p)[i]);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = f2bf(v);
+  }
 };
 
 // Fixed-order block sum over 256 threads (deterministic).
@@ -151,7 +188,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
 // out row-major, zeros in the padding. With zero steps the scaled values go
 // straight to `out` in the caller's layout.
 
-template <typename T>
+template <typename T, int OP>
 __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
   if (it.mat < 0) return;
@@ -198,9 +235,9 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
     const int32_t r = e >> 6, cidx = e & 63;
     const float v = M.tall ? tile[cidx][r] : tile[r][cidx];
     const int64_t off = int64_t(i0 + r) * M.np + (j0 + cidx);
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (OP != OP_F32) {
       reinterpret_cast<float*>(A.ws + M.xm_off)[off] = v;
-      reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0])[off] = f2bf(v);
+      Op<OP>::store(A.ws + M.xo_off[0], off, v);
     } else {
       reinterpret_cast<float*>(A.ws + M.xo_off[0])[off] = v;
     }
@@ -243,10 +280,10 @@ __device__ __forceinline__ void store_rows(char* lds, const uint4 (&r)[4]) {
 // KS k-rows x 128 n-columns (KS = 64 bf16 or 32 fp32). Thread t loads a
 // block of 4 k-rows x V columns (V = 8 bf16 / 4 fp32, 16 bytes) and later
 // writes it transposed into the [n][k] LDS tile.
-template <typename T>
+template <int ES>
 __device__ __forceinline__ void load_cols(uint4 (&r)[4], const char* base, int64_t ld_bytes,
                                           int64_t k0) {
-  constexpr int V = 16 / sizeof(T);
+  constexpr int V = 16 / ES;
   constexpr int NG = 128 / V;  // column groups per slab (16 bf16, 32 fp32)
   const int t = threadIdx.x;
   const int kq = t / NG, ng = t % NG;
@@ -254,14 +291,14 @@ __device__ __forceinline__ void load_cols(uint4 (&r)[4], const char* base, int64
   for (int q = 0; q < 4; ++q)
     r[q] = *reinterpret_cast<const uint4*>(base + (k0 + 4 * kq + q) * ld_bytes + ng * 16);
 }
-template <typename T>
+template <int ES>
 __device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
-  constexpr int V = 16 / sizeof(T);
+  constexpr int V = 16 / ES;
   constexpr int NG = 128 / V;
   const int t = threadIdx.x;
   const int kq = t / NG, ng = t % NG;
-  if constexpr (sizeof(T) == 2) {
-    // k-quad kq covers bf16 k = 4kq..4kq+3: 8 bytes inside chunk kq/2
+  if constexpr (ES == 2) {
+    // k-quad kq covers 16-bit k = 4kq..4kq+3: 8 bytes inside chunk kq/2
     const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
     const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
     const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
@@ -293,7 +330,7 @@ __device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
 }
 
 // One k-slab (128 bytes of k per row) of MFMAs for this wave's 64 x 64.
-template <typename T>
+template <int OP>
 __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, const char* sB,
                                          int wm, int wn) {
   const int lane = threadIdx.x & 63;
@@ -308,13 +345,21 @@ __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, c
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       bfr[j] = *reinterpret_cast<const uint4*>(sB + lds_off(wn * 64 + j * 16 + lr, ch));
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (OP == OP_BF16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]),
+              acc[i][j], 0, 0, 0);
+    } else if constexpr (OP == OP_F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bfr[j]),
               acc[i][j], 0, 0, 0);
     } else {
       // four k=4 MFMAs per 16-byte chunk; lane group g supplies k = 4(ch)+e
@@ -333,13 +378,13 @@ __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, c
 
 // Item {mat, ti, tj}. GRAM/POLY: C = Op Op^T on upper-triangle tiles (ti <=
 // tj) mirrored into the lower triangle; UPDATE: X = a X + B X on all tiles.
-template <typename T, int KIND>
+template <typename T, int OP, int KIND>
 __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
   const MatInfo M = P.mats[it.mat];
-  constexpr int ES = sizeof(T);
-  constexpr int KS = ROWB / ES;  // k elements per slab
+  constexpr int ES = Op<OP>::bytes;  // operand element size
+  constexpr int KS = ROWB / ES;      // k elements per slab
 
   __shared__ __attribute__((aligned(16))) char sA[BM * ROWB];
   __shared__ __attribute__((aligned(16))) char sB[BM * ROWB];
@@ -379,20 +424,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
 
   uint4 ra[4], rb[4];
   load_rows(ra, opA, lda_b, 0);
-  if (KIND == UPDATE) load_cols<T>(rb, opB, ldb_b, 0);
+  if (KIND == UPDATE) load_cols<ES>(rb, opB, ldb_b, 0);
   else load_rows(rb, opB, ldb_b, 0);
   for (int64_t k0 = 0; k0 < K; k0 += KS) {
     __syncthreads();
     store_rows(sA, ra);
-    if (KIND == UPDATE) store_cols<T>(sB, rb);
+    if (KIND == UPDATE) store_cols<ES>(sB, rb);
     else store_rows(sB, rb);
     __syncthreads();
     if (k0 + KS < K) {
       load_rows(ra, opA, lda_b, (k0 + KS) * ES);
-      if (KIND == UPDATE) load_cols<T>(rb, opB, ldb_b, k0 + KS);
+      if (KIND == UPDATE) load_cols<ES>(rb, opB, ldb_b, k0 + KS);
       else load_rows(rb, opB, ldb_b, (k0 + KS) * ES);
     }
-    mma_slab<T>(acc, sA, sB, wm, wn);
+    mma_slab<OP>(acc, sA, sB, wm, wn);
   }
 
   // ------------------------------------------------------------ epilogue
@@ -417,13 +462,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
           // b A[gi][gj] read from the mirrored (contiguous) position A[gj][gi0..]
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            v[r] = __fmaf_rn(P.c, v[r], P.b * Elem<T>::load(Am, int64_t(gj) * ld + gi0 + r));
+            v[r] = __fmaf_rn(P.c, v[r], P.b * Op<OP>::load(Am, int64_t(gj) * ld + gi0 + r));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gi = gi0 + r;
-          if (!diag || gi <= gj) Elem<T>::store(C, int64_t(gi) * ld + gj, v[r]);
-          if (!diag || gi < gj) Elem<T>::store(C, int64_t(gj) * ld + gi, v[r]);
+          if (!diag || gi <= gj) Op<OP>::store(C, int64_t(gi) * ld + gj, v[r]);
+          if (!diag || gi < gj) Op<OP>::store(C, int64_t(gj) * ld + gi, v[r]);
         }
       }
   } else {
@@ -438,11 +483,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t off = int64_t(gi0 + r) * ldx + gj;
-            if constexpr (ES == 2) {
+            if constexpr (OP != OP_F32) {
               float* xm = reinterpret_cast<float*>(P.ws + M.xm_off);
               const float v = __fmaf_rn(P.a, xm[off], acc[i][j][r]);
               xm[off] = v;
-              reinterpret_cast<uint16_t*>(P.ws + M.xo_off[P.cur ^ 1])[off] = f2bf(v);
+              Op<OP>::store(P.ws + M.xo_off[P.cur ^ 1], off, v);
             } else {
               const float* xc = reinterpret_cast<const float*>(P.ws + M.xo_off[P.cur]);
               const float v = __fmaf_rn(P.a, xc[off], acc[i][j][r]);
@@ -453,7 +498,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
     } else {
       // last step: out in the caller's layout and dtype, valid region only
       const float* xsrc = reinterpret_cast<const float*>(
-          P.ws + (ES == 2 ? M.xm_off : M.xo_off[P.cur]));
+          P.ws + (OP != OP_F32 ? M.xm_off : M.xo_off[P.cur]));
       char* o = static_cast<char*>(M.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -477,23 +522,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
 
 // --------------------------------------------------------------- launchers
 
-template <typename T>
+template <typename T, int OP>
 static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   dim3 g(grid), b(256);
   switch (kind) {
     case MUON_K_MOMENTUM: hipLaunchKernelGGL(momentum_kernel<T>, g, b, 0, s, a); break;
-    case MUON_K_NORMALIZE: hipLaunchKernelGGL(normalize_kernel<T>, g, b, 0, s, a); break;
-    case MUON_K_GRAM: hipLaunchKernelGGL((gemm_kernel<T, GRAM>), g, b, 0, s, a); break;
-    case MUON_K_POLY: hipLaunchKernelGGL((gemm_kernel<T, POLY>), g, b, 0, s, a); break;
-    case MUON_K_UPDATE: hipLaunchKernelGGL((gemm_kernel<T, UPDATE>), g, b, 0, s, a); break;
+    case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;
+    case MUON_K_GRAM: hipLaunchKernelGGL((gemm_kernel<T, OP, GRAM>), g, b, 0, s, a); break;
+    case MUON_K_POLY: hipLaunchKernelGGL((gemm_kernel<T, OP, POLY>), g, b, 0, s, a); break;
+    case MUON_K_UPDATE: hipLaunchKernelGGL((gemm_kernel<T, OP, UPDATE>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s) {
-  return dt == MUON_BF16 ? launch_t<uint16_t>(kind, a, grid, s) : launch_t<float>(kind, a, grid, s);
+hipError_t launch_kernel(int kind, muon_dtype dt, int precision, const StepArgs& a, int grid,
+                         hipStream_t s) {
+  if (dt == MUON_F32) return launch_t<float, OP_F32>(kind, a, grid, s);
+  if (precision == MUON_PRECISION_BF16_OPERANDS) return launch_t<uint16_t, OP_BF16>(kind, a, grid, s);
+  return launch_t<uint16_t, OP_F16>(kind, a, grid, s);
 }
 
 }  // namespace muon

@@ -21,6 +21,8 @@ struct StepArgs {
   int32_t direct;   // zero steps: the normalise kernel writes `out`
 };
 
-hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s);
+// precision: muon_precision (operand format of bf16 sets).
+hipError_t launch_kernel(int kind, muon_dtype dt, int precision, const StepArgs& a, int grid,
+                         hipStream_t s);
 
 }  // namespace muon

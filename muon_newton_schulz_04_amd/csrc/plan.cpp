@@ -75,6 +75,8 @@ muon_status validate_config(const muon_config* cfg) {
   if (cfg->momentum < 0.f || cfg->momentum >= 1.f) return MUON_E_INVALID;
   if (cfg->nesterov != 0 && cfg->nesterov != 1) return MUON_E_INVALID;
   if (cfg->eps < 0.f) return MUON_E_INVALID;
+  if (cfg->precision != MUON_PRECISION_DEFAULT && cfg->precision != MUON_PRECISION_BF16_OPERANDS)
+    return MUON_E_INVALID;
   return MUON_OK;
 }
 

@@ -1,7 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle.
 
 Bar (per matrix, relative Frobenius error): 2e-2 for bf16 sets, 1e-4 for
-fp32 sets; momentum buffers within one bf16 ulp of the oracle's rounding.
+fp32 sets; momentum buffers bitwise equal to the oracle's. bf16 sets run
+with fp16 matrix-core operands (default) and with bf16 operands; the latter
+is held to 2e-2 except on matrices with min(rows, cols) <= 8, where a single
+bf16-rounded B entry near sigma = 1 is amplified by |B|/|a + B| ~ 4 per step
+(derived bound 5e-2, see the design notes).
 The oracle receives the same seeded inputs and the float32 values of the
 scalars the C ABI takes (a, b, c, mu, eps are floats there).
 """
@@ -35,12 +39,15 @@ def say(msg):
     print(msg, flush=True)
 
 
+PRECS = {"fp16ops": 0, "bf16ops": 1}
+
+
 def gpu_call(grads, bufs, coeffs, steps, momentum=0.0, nesterov=False, eps=1e-7,
-             ortho=False, outs=None):
+             ortho=False, outs=None, precision=0):
     """grads/bufs: device tensors. Returns (outs, bufs) as float64 arrays."""
     if outs is None:
         outs = [torch.empty_like(g) for g in grads]
-    cfg = mu.make_config(*coeffs, steps, momentum, nesterov, eps)
+    cfg = mu.make_config(*coeffs, steps, momentum, nesterov, eps, precision)
     if ortho:
         mu.muon_orthogonalize(grads, outs, cfg)
     else:
@@ -64,14 +71,7 @@ def oracle_call(grads64, bufs64, coeffs, steps, momentum=0.0, nesterov=False, ep
 
 def check_buffers(got, want, dtype):
     for gb, wb in zip(got, want):
-        if dtype == "fp32":
-            assert np.allclose(gb, wb, rtol=1e-6, atol=1e-30)
-            continue
-        # one bf16 ulp at most, and rarely (float32 vs float64 before rounding)
-        ulp = np.abs(wb) * 2.0 ** -7 + 1e-38
-        d = np.abs(gb - wb)
-        assert np.all(d <= ulp), float(np.max(d / ulp))
-        assert np.mean(d > 0) < 1e-3
+        assert np.array_equal(gb, wb), float(np.mean(gb != wb))
 
 
 # ------------------------------------------------------------------ tiny fp32
@@ -101,24 +101,30 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+MODES = [("bf16", "fp16ops"), ("bf16", "bf16ops"), ("fp32", "fp16ops")]
+
+
+@pytest.mark.parametrize("dtype,prec", MODES, ids=["bf16", "bf16-bf16ops", "fp32"])
 @pytest.mark.parametrize("case", list(CASES))
-def test_substeps_ragged(dtype, case):
+def test_substeps_ragged(dtype, prec, case):
     coeffs, steps = CASES[case]
     wl = CONFIGS["gpt2_small_block"]
     grads = make_gradients(wl, step=3, shapes=RAGGED)
     grads = [g.to(TDT[dtype]) for g in grads]
     bufs = [torch.randn(g.shape, generator=torch.Generator().manual_seed(i)).to(g.dtype)
             for i, g in enumerate(grads)]
-    say(f"substeps {dtype} {case} shapes={RAGGED}")
+    say(f"substeps {dtype} {prec} {case} shapes={RAGGED}")
     outs, nbufs = gpu_call([g.to(DEV) for g in grads], [b.to(DEV) for b in bufs], coeffs, steps,
-                           momentum=0.9, nesterov=True)
+                           momentum=0.9, nesterov=True, precision=PRECS[prec])
     want, wbufs = oracle_call([to_f64(g) for g in grads], [to_f64(b) for b in bufs], coeffs,
                               steps, momentum=0.9, nesterov=True, buf_dtype=dtype)
     for shp, o, w in zip(RAGGED, outs, want):
         assert o.shape == w.shape
         e = rel(o, w)
-        assert e < TOL[dtype], (shp, e)
+        tol = TOL[dtype]
+        if prec == "bf16ops" and min(shp) <= 8:
+            tol = 5e-2
+        assert e < tol, (shp, e)
     check_buffers(nbufs, wbufs, dtype)
 
 
@@ -157,12 +163,12 @@ def test_gram_is_bitwise_symmetric_and_padding_zero():
         mp, m = info["mp"], info["m"]
         for key in ("gram", "poly"):
             off = info[key]
-            A = ws[off: off + mp * mp * 2].view(torch.bfloat16).view(mp, mp).float().cpu()
+            A = ws[off: off + mp * mp * 2].view(torch.float16).view(mp, mp).float().cpu()
             assert torch.equal(A, A.t()), key
             assert torch.count_nonzero(A[m:, :]) == 0 and torch.count_nonzero(A[:, m:]) == 0
         # trace(A) = ||X0||_F^2 = (||u|| / (||u|| + eps))^2 ~ 1
         off = info["gram"]
-        A = ws[off: off + mp * mp * 2].view(torch.bfloat16).view(mp, mp).double().cpu()
+        A = ws[off: off + mp * mp * 2].view(torch.float16).view(mp, mp).double().cpu()
         assert abs(float(torch.trace(A)) - 1.0) < 1e-2
     plan.destroy()
 
@@ -176,10 +182,18 @@ def test_deterministic_odd_and_scale_invariant(dtype):
     o2, _ = gpu_call(grads, None, QUINTIC, 5, ortho=True)
     on, _ = gpu_call([-g for g in grads], None, QUINTIC, 5, ortho=True)
     o4, _ = gpu_call([g * 4 for g in grads], None, QUINTIC, 5, ortho=True)  # exact scaling
+    ob, _ = gpu_call(grads, None, QUINTIC, 5, ortho=True, precision=1)
+    for a, b in zip(o1, ob):                 # the two operand formats agree to ~1e-2
+        assert rel(b, a) < 2e-2
     for a, b, n, s in zip(o1, o2, on, o4):
         assert np.array_equal(a, b)
-        assert np.array_equal(n, -a)
-        assert rel(s, a) < 1e-5
+        if dtype == "fp32":
+            assert np.array_equal(n, -a)          # fp32 matrix cores round symmetrically
+        else:
+            # the 16-bit-input matrix-core sums are not sign-symmetric in their
+            # last bit; oddness holds to rounding
+            assert rel(n, -a) < 5e-3
+        assert rel(s, a) < (1e-5 if dtype == "fp32" else 5e-3)
 
 
 def test_zero_matrix_empty_matrix_and_aliasing():
@@ -200,7 +214,7 @@ def test_zero_matrix_empty_matrix_and_aliasing():
 
 # ------------------------------------------------------ full configurations
 
-def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu"):
+def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu", precision=0):
     wl = CONFIGS[name]
     say(f"config {name}: {wl.n_matrices} matrices")
     grads_cpu = None
@@ -221,7 +235,7 @@ def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu"):
         k = max(1, sample_per_group // 2)
         sample = sorted({i for idx in groups.values() for i in idx[:k] + idx[-k:]})
         g_sample = {i: to_f64(grads[i]) for i in sample}
-        cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
+        cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps, precision)
         mu.muon_step(grads_dev, bufs, outs, cfg)
         torch.cuda.synchronize()
         for i in sample:
@@ -242,12 +256,14 @@ def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu"):
     return outs
 
 
-def test_config_gpt2_small_block_two_steps():
-    run_config("gpt2_small_block", sample_per_group=6, step_seeds=(0, 1))
+@pytest.mark.parametrize("prec", list(PRECS))
+def test_config_gpt2_small_block_two_steps(prec):
+    run_config("gpt2_small_block", sample_per_group=6, step_seeds=(0, 1), precision=PRECS[prec])
 
 
-def test_config_gpt2_124m_matrix_set():
-    run_config("gpt2_124m_matrix_set")
+@pytest.mark.parametrize("prec", list(PRECS))
+def test_config_gpt2_124m_matrix_set(prec):
+    run_config("gpt2_124m_matrix_set", precision=PRECS[prec])
 
 
 @pytest.mark.slow
