@@ -30,6 +30,7 @@ namespace muon {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- bf16 bits
 
@@ -78,6 +79,9 @@ template <> struct Op<OP_F32> {
 };
 template <> struct Op<OP_F16> {
   static constexpr int bytes = 2;
+  static __device__ __forceinline__ float load16(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+  }
   static __device__ __forceinline__ uint16_t bits(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));  // RNE
   }
@@ -90,6 +94,7 @@ template <> struct Op<OP_F16> {
 };
 template <> struct Op<OP_BF16> {
   static constexpr int bytes = 2;
+  static __device__ __forceinline__ float load16(uint32_t h) { return bf2f(static_cast<uint16_t>(h)); }
   static __device__ __forceinline__ uint16_t bits(float v) { return f2bf(v); }
   static __device__ __forceinline__ float load(const void* p, int64_t i) {
     return bf2f(static_cast<const uint16_t*>(p)[i]);
@@ -112,6 +117,17 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 
 // StepArgs (kernel arguments) is declared in launch.hpp.
 
+// Component e (compile-time after unrolling) of a 16-byte register vector.
+__device__ __forceinline__ uint32_t comp(const uint4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// Offset of operand buffer `which` (0/1) without indexing the record's
+// array by a run-time value (which would move the record to scratch).
+__device__ __forceinline__ int64_t xo_sel(const MatInfo& M, int which) {
+  return which ? M.xo_off[1] : M.xo_off[0];
+}
+
 // u from the gradient and the already-updated buffer (same expression in
 // both elementwise kernels so u is bitwise identical).
 __device__ __forceinline__ float form_u(float g, float nb, const StepArgs& A) {
@@ -125,7 +141,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
   if (it.mat < 0) return;
-  const MatInfo M = A.mats[it.mat];
+  const MatInfo& M = A.mats[it.mat];
   const int32_t r0 = it.a, nr = it.b;
   float acc = 0.f;
   const T* g = static_cast<const T*>(M.grad);
@@ -192,7 +208,7 @@ template <typename T, int OP>
 __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
   if (it.mat < 0) return;
-  const MatInfo M = A.mats[it.mat];
+  const MatInfo& M = A.mats[it.mat];
   __shared__ float red[4];
   __shared__ float tile[64][65];
 
@@ -202,44 +218,107 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   s = block_sum_256(s, red);
   const float scale = 1.0f / (sqrtf(s) + A.eps);
 
-  // 2. caller-side tile: rows cr0.., cols cc0..
-  const int32_t i0 = it.a * 64, j0 = it.b * 64;  // X0 (wide) coordinates
+  // 2. caller-side tile rows cr0.., cols cc0..; thread handles 2 runs of 8
+  //    consecutive caller columns: run h covers row (tid + 256 h) / 8,
+  //    columns 8 * (tid % 8)..+7
+  const int32_t i0 = it.a * 64, j0 = it.b * 64;  // X0 (rows<=cols) coordinates
   const int32_t cr0 = M.tall ? j0 : i0, cc0 = M.tall ? i0 : j0;
   const T* g = static_cast<const T*>(M.grad);
   const T* mb = static_cast<const T*>(M.mom);
-  for (int32_t e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int32_t r = e >> 6, cidx = e & 63;
-    const int32_t cr = cr0 + r, cc = cc0 + cidx;
-    float v = 0.f;
-    if (cr < M.rows && cc < M.cols) {
-      const int64_t off = int64_t(cr) * M.ld + cc;
-      const float gf = Elem<T>::load(g, off);
-      const float nb = A.use_mom ? Elem<T>::load(mb, off) : 0.f;
-      v = form_u(gf, nb, A) * scale;
+  float u[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int32_t cr = cr0 + (v >> 3), cc = cc0 + (v & 7) * 8;
+    const int64_t off = int64_t(cr) * M.ld + cc;
+    if (cr < M.rows && M.vec_ok && cc + 8 <= M.cols) {
+      float gv[8], bv[8];
+      if constexpr (sizeof(T) == 2) {
+        const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(g + off);
+        u32x4_t bw = {0u, 0u, 0u, 0u};
+        if (A.use_mom) bw = *reinterpret_cast<const u32x4_t*>(mb + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          gv[e] = bf2f(static_cast<uint16_t>(gw[e >> 1] >> (16 * (e & 1))));
+          bv[e] = bf2f(static_cast<uint16_t>(bw[e >> 1] >> (16 * (e & 1))));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4_t gw = *reinterpret_cast<const f32x4_t*>(g + off + 4 * q);
+          f32x4_t bw = {0.f, 0.f, 0.f, 0.f};
+          if (A.use_mom) bw = *reinterpret_cast<const f32x4_t*>(mb + off + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[4 * q + e] = gw[e];
+            bv[4 * q + e] = bw[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[h][e] = form_u(gv[e], bv[e], A) * scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = 0.f;
+        if (cr < M.rows && cc + e < M.cols) {
+          const float gf = Elem<T>::load(g, off + e);
+          const float nb = A.use_mom ? Elem<T>::load(mb, off + e) : 0.f;
+          x = form_u(gf, nb, A) * scale;
+        }
+        u[h][e] = x;
+      }
     }
-    tile[r][cidx] = v;
   }
-  __syncthreads();
 
-  if (A.direct) {  // zero steps: X0 is the result, caller layout
+  if (A.direct) {  // zero steps: X0 is the result, in the caller's layout
     T* o = static_cast<T*>(M.out);
-    for (int32_t e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int32_t r = e >> 6, cidx = e & 63;
-      const int32_t cr = cr0 + r, cc = cc0 + cidx;
-      if (cr < M.rows && cc < M.cols) Elem<T>::store(o, int64_t(cr) * M.ld + cc, tile[r][cidx]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+      const int32_t cr = cr0 + (v >> 3), cc = cc0 + (v & 7) * 8;
+      if (cr >= M.rows) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (cc + e < M.cols) Elem<T>::store(o, int64_t(cr) * M.ld + cc + e, u[h][e]);
     }
     return;
   }
-  // 3. X0 rows i0.., cols j0.. of the padded wide layout (row stride np)
-  for (int32_t e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int32_t r = e >> 6, cidx = e & 63;
-    const float v = M.tall ? tile[cidx][r] : tile[r][cidx];
-    const int64_t off = int64_t(i0 + r) * M.np + (j0 + cidx);
+
+  // 3. X0 rows i0.., cols j0.. of the padded layout (row stride np), written
+  //    as runs of 8 (fp32 master + operand copy); tall tiles go through LDS
+  if (M.tall) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[(v & 7) * 8 + e][v >> 3] = u[h][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[h][e] = tile[v >> 3][(v & 7) * 8 + e];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int64_t off = int64_t(i0 + (v >> 3)) * M.np + j0 + (v & 7) * 8;
     if constexpr (OP != OP_F32) {
-      reinterpret_cast<float*>(A.ws + M.xm_off)[off] = v;
-      Op<OP>::store(A.ws + M.xo_off[0], off, v);
+      float* xm = reinterpret_cast<float*>(A.ws + M.xm_off) + off;
+      reinterpret_cast<f32x4_t*>(xm)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
+      reinterpret_cast<f32x4_t*>(xm)[1] = f32x4_t{u[h][4], u[h][5], u[h][6], u[h][7]};
+      u32x4_t w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = uint32_t(Op<OP>::bits(u[h][2 * q])) | (uint32_t(Op<OP>::bits(u[h][2 * q + 1])) << 16);
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = w;
     } else {
-      reinterpret_cast<float*>(A.ws + M.xo_off[0])[off] = v;
+      float* x0 = reinterpret_cast<float*>(A.ws + M.xo_off[0]) + off;
+      reinterpret_cast<f32x4_t*>(x0)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
+      reinterpret_cast<f32x4_t*>(x0)[1] = f32x4_t{u[h][4], u[h][5], u[h][6], u[h][7]};
     }
   }
 }
@@ -299,32 +378,25 @@ __device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
   const int kq = t / NG, ng = t % NG;
   if constexpr (ES == 2) {
     // k-quad kq covers 16-bit k = 4kq..4kq+3: 8 bytes inside chunk kq/2
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       // columns 2d (low halves) and 2d+1 (high halves)
+      const uint32_t w0 = comp(r[0], d), w1 = comp(r[1], d), w2 = comp(r[2], d), w3 = comp(r[3], d);
       uint2 lo, hi;
-      lo.x = (w0[d] & 0xffffu) | (w1[d] << 16);
-      lo.y = (w2[d] & 0xffffu) | (w3[d] << 16);
-      hi.x = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
-      hi.y = (w2[d] >> 16) | (w3[d] & 0xffff0000u);
+      lo.x = (w0 & 0xffffu) | (w1 << 16);
+      lo.y = (w2 & 0xffffu) | (w3 << 16);
+      hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
+      hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
       const int n0 = ng * 8 + 2 * d;
       *reinterpret_cast<uint2*>(lds + lds_off(n0, kq >> 1) + (kq & 1) * 8) = lo;
       *reinterpret_cast<uint2*>(lds + lds_off(n0 + 1, kq >> 1) + (kq & 1) * 8) = hi;
     }
   } else {
     // k-quad kq covers fp32 k = 4kq..4kq+3: exactly chunk kq
-    const float* f0 = reinterpret_cast<const float*>(&r[0]);
-    const float* f1 = reinterpret_cast<const float*>(&r[1]);
-    const float* f2 = reinterpret_cast<const float*>(&r[2]);
-    const float* f3 = reinterpret_cast<const float*>(&r[3]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float4 v = make_float4(f0[e], f1[e], f2[e], f3[e]);
-      *reinterpret_cast<float4*>(lds + lds_off(ng * 4 + e, kq)) = v;
+      const uint4 v = make_uint4(comp(r[0], e), comp(r[1], e), comp(r[2], e), comp(r[3], e));
+      *reinterpret_cast<uint4*>(lds + lds_off(ng * 4 + e, kq)) = v;
     }
   }
 }
@@ -370,19 +442,20 @@ __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, c
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                __uint_as_float((&af[i].x)[e]), __uint_as_float((&bfr[j].x)[e]), acc[i][j], 0,
+                __uint_as_float(comp(af[i], e)), __uint_as_float(comp(bfr[j], e)), acc[i][j], 0,
                 0, 0);
     }
   }
 }
 
-// Item {mat, ti, tj}. GRAM/POLY: C = Op Op^T on upper-triangle tiles (ti <=
-// tj) mirrored into the lower triangle; UPDATE: X = a X + B X on all tiles.
+// fp32 sets. Item {mat, ti, tj} of 128 x 128 tiles. GRAM/POLY: C = Op Op^T
+// on upper-triangle tiles (ti <= tj) mirrored into the lower triangle;
+// UPDATE: X = a X + B X on all tiles.
 template <typename T, int OP, int KIND>
-__global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
+__global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
-  const MatInfo M = P.mats[it.mat];
+  const MatInfo& M = P.mats[it.mat];
   constexpr int ES = Op<OP>::bytes;  // operand element size
   constexpr int KS = ROWB / ES;      // k elements per slab
 
@@ -394,7 +467,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
   const char* opB;
   int64_t lda_b, ldb_b, K;
   if (KIND == GRAM) {  // rows of X (mp x np): A[i][j] = sum_k X[i][k] X[j][k]
-    const char* X = P.ws + M.xo_off[P.cur];
+    const char* X = P.ws + xo_sel(M, P.cur);
     lda_b = ldb_b = int64_t(M.np) * ES;
     opA = X + int64_t(ti) * BM * lda_b;
     opB = X + int64_t(tj) * BM * ldb_b;
@@ -410,7 +483,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
     lda_b = int64_t(M.mp) * ES;
     ldb_b = int64_t(M.np) * ES;
     opA = Bm + int64_t(ti) * BM * lda_b;
-    opB = P.ws + M.xo_off[P.cur] + int64_t(tj) * BM * ES;
+    opB = P.ws + xo_sel(M, P.cur) + int64_t(tj) * BM * ES;
     K = M.mp;
   }
 
@@ -487,18 +560,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
               float* xm = reinterpret_cast<float*>(P.ws + M.xm_off);
               const float v = __fmaf_rn(P.a, xm[off], acc[i][j][r]);
               xm[off] = v;
-              Op<OP>::store(P.ws + M.xo_off[P.cur ^ 1], off, v);
+              Op<OP>::store(P.ws + xo_sel(M, P.cur ^ 1), off, v);
             } else {
-              const float* xc = reinterpret_cast<const float*>(P.ws + M.xo_off[P.cur]);
+              const float* xc = reinterpret_cast<const float*>(P.ws + xo_sel(M, P.cur));
               const float v = __fmaf_rn(P.a, xc[off], acc[i][j][r]);
-              reinterpret_cast<float*>(P.ws + M.xo_off[P.cur ^ 1])[off] = v;
+              reinterpret_cast<float*>(P.ws + xo_sel(M, P.cur ^ 1))[off] = v;
             }
           }
         }
     } else {
       // last step: out in the caller's layout and dtype, valid region only
       const float* xsrc = reinterpret_cast<const float*>(
-          P.ws + (OP != OP_F32 ? M.xm_off : M.xo_off[P.cur]));
+          P.ws + (OP != OP_F32 ? M.xm_off : xo_sel(M, P.cur)));
       char* o = static_cast<char*>(M.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -520,6 +593,409 @@ __global__ __launch_bounds__(256) void gemm_kernel(StepArgs P) {
   }
 }
 
+
+// ------------------------------------------- 16-bit operand engine (bf16 sets)
+//
+// Output tile 256 (rows) x 128 (cols), k-slab 64 elements (128 bytes). Four
+// waves in 2 x 2, each owning 128 x 64 = 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_{f16,bf16}. The MFMA is fed (column operand, row
+// operand), so lane l holds, for accumulator (i, j) and register e,
+//   C[m][n], m = row0 + 32 i + l % 32, n = col0 + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4,
+// i.e. runs of 4 consecutive output columns: vector epilogue loads/stores.
+//   Row operand (k contiguous in memory): LDS [row][k], 128-byte rows.
+//   Column operand, k contiguous (Gram, A A):  LDS [col][k], 128-byte rows.
+//   Column operand, k along memory rows (X in B X): LDS [k][col], 256-byte
+//     rows, read with ds_read_b64_tr_b16: in each 16-lane group, lane s
+//     addresses row k0 + s/4, columns c0 + 4(s%4)..+3, and lane i receives
+//     column c0 + i of rows k0..k0+3.
+// Two LDS stages and two register sets; the loop is unrolled by two so
+// stage and register-set choices are constants: multiply stage 0, write the
+// next slab (registers) to stage 1, barrier, load the slab three ahead,
+// multiply stage 1, and so on.
+
+#ifndef MUON_GEMM_PIPE
+#define MUON_GEMM_PIPE 1
+#endif
+
+namespace e16 {
+
+constexpr int TM = 256, TN = 128;
+// PIPE 2: two LDS stages + two register sets, one workgroup per CU.
+// PIPE 1: one LDS stage + one register set, two workgroups per CU.
+constexpr int PIPE = MUON_GEMM_PIPE;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int off_rows(int row, int chunk) {   // 128-byte rows
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+// [k][col] tile, 256-byte rows; the XOR spreads the rows touched by one
+// transposed read over distinct 32-byte bank groups (2 passes, the minimum)
+__device__ __forceinline__ int off_kn(int k, int chunk) {
+  return k * 256 + ((chunk ^ (((k ^ ((k >> 3) << 2)) & 7) << 1)) << 4);
+}
+
+template <int R>  // R rows x 128 bytes at base + row*ldb + k0b
+__device__ __forceinline__ void load_rows(u32x4 (&r)[R / 32], const char* base, int64_t ldb,
+                                          int64_t k0b) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < R / 32; ++q)
+    r[q] = *reinterpret_cast<const u32x4*>(base + int64_t((t >> 3) + 32 * q) * ldb + k0b +
+                                           (t & 7) * 16);
+}
+template <int R>
+__device__ __forceinline__ void store_rows(char* lds, const u32x4 (&r)[R / 32]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < R / 32; ++q)
+    *reinterpret_cast<u32x4*>(lds + off_rows((t >> 3) + 32 * q, t & 7)) = r[q];
+}
+// 64 k-rows x 256 bytes at base + (k0 + k)*ldb
+__device__ __forceinline__ void load_kn(u32x4 (&r)[4], const char* base, int64_t ldb, int64_t k0) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = *reinterpret_cast<const u32x4*>(base + (k0 + (t >> 4) + 16 * q) * ldb + (t & 15) * 16);
+}
+__device__ __forceinline__ void store_kn(char* lds, const u32x4 (&r)[4]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<u32x4*>(lds + off_kn((t >> 4) + 16 * q, t & 15)) = r[q];
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <int OP>
+__device__ __forceinline__ f32x16_t mfma(const u32x4& colop, const u32x4& rowop, f32x16_t c) {
+  if constexpr (OP == OP_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, colop),
+                                                  __builtin_bit_cast(f16x8_t, rowop), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, colop),
+                                                   __builtin_bit_cast(bf16x8_t, rowop), c, 0, 0, 0);
+}
+
+// One 64-k slab of this wave's 128 x 64 block: 4 k-steps of 16.
+template <int OP, bool KN>
+__device__ __forceinline__ void mma_slab(f32x16_t (&acc)[4][2], const char* sA, const char* sB,
+                                         int wm, int wn) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = ks * 2 + lh;  // 16-byte k chunk of this lane half
+    u32x4 bf[2], af[4];
+    if constexpr (!KN) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows(wn * 64 + j * 32 + l32, ch));
+    } else {
+      const int s = lane & 15, h = lane >> 4;        // 16-lane group h
+      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
+        const int chunk = col >> 3, byte = (col & 7) * 2;
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows(wm * 128 + i * 32 + l32, ch));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
+  }
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool f16) {
+  uint2 r;
+  if (f16) {
+    r.x = uint32_t(Op<OP_F16>::bits(a)) | (uint32_t(Op<OP_F16>::bits(b)) << 16);
+    r.y = uint32_t(Op<OP_F16>::bits(c)) | (uint32_t(Op<OP_F16>::bits(d)) << 16);
+  } else {
+    r.x = uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+    r.y = uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16);
+  }
+  return r;
+}
+
+}  // namespace e16
+
+// bf16 sets. Item {mat, TI, TJ} of 256 x 128 tiles. GRAM/POLY: tiles that
+// reach the upper triangle (TJ >= 2 TI); each stored element (m <= n) is
+// mirrored to (n, m). UPDATE: X = a X + B X on all tiles.
+template <typename T, int OP, int KIND>
+__global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(StepArgs P) {
+  using namespace e16;
+  const WorkItem it = P.items[blockIdx.x];
+  if (it.mat < 0) return;
+  const MatInfo& M = P.mats[it.mat];
+  constexpr bool KN = KIND == UPDATE;
+
+  // LDS: operand stages (PIPE 1: one, PIPE 2: two); reused by the epilogue.
+  constexpr int STAGE = (TM + TN) * 128;
+  __shared__ __attribute__((aligned(16))) char lds[PIPE * STAGE];
+  char* const sA0 = lds;
+  char* const sB0 = lds + TM * 128;
+  char* const sA1 = lds + (PIPE == 2 ? STAGE : 0);
+  char* const sB1 = sA1 + TM * 128;
+
+  const int TI = it.a, TJ = it.b;
+  const char* opA;
+  const char* opB;
+  int64_t lda, ldb, K;
+  if (KIND == GRAM) {
+    const char* X = P.ws + xo_sel(M, P.cur);
+    lda = ldb = int64_t(M.np) * 2;
+    opA = X + int64_t(TI) * TM * lda;
+    opB = X + int64_t(TJ) * TN * ldb;
+    K = M.np;
+  } else if (KIND == POLY) {
+    const char* Am = P.ws + M.a_off;
+    lda = ldb = int64_t(M.mp) * 2;
+    opA = Am + int64_t(TI) * TM * lda;
+    opB = Am + int64_t(TJ) * TN * ldb;
+    K = M.mp;
+  } else {
+    lda = int64_t(M.mp) * 2;
+    ldb = int64_t(M.np) * 2;
+    opA = P.ws + M.b_off + int64_t(TI) * TM * lda;
+    opB = P.ws + xo_sel(M, P.cur) + int64_t(TJ) * TN * 2;
+    K = M.mp;
+  }
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Two register sets hold the next two slabs, so each global load has two
+  // slabs of multiplies to land before its data is written to LDS.
+  u32x4 ra0[TM / 32], rb0[4], ra1[TM / 32], rb1[4];
+  auto load = [&](u32x4 (&ra)[TM / 32], u32x4 (&rb)[4], int64_t slab) {
+    const int64_t k0 = slab * 64;
+    load_rows<TM>(ra, opA, lda, k0 * 2);
+    if constexpr (KN) load_kn(rb, opB, ldb, k0);
+    else load_rows<TN>(rb, opB, ldb, k0 * 2);
+  };
+  auto store = [&](const u32x4 (&ra)[TM / 32], const u32x4 (&rb)[4], char* a, char* b) {
+    store_rows<TM>(a, ra);
+    if constexpr (KN) store_kn(b, rb);
+    else store_rows<TN>(b, rb);
+  };
+  // K is a multiple of 128: an even number (>= 2) of 64-element slabs.
+  // Loads past the last slab are clamped to it (valid, unused).
+  const int nslab = static_cast<int>(K >> 6);
+  if constexpr (PIPE == 1) {
+    load(ra0, rb0, 0);
+    for (int t = 0; t < nslab; ++t) {
+      __syncthreads();
+      store(ra0, rb0, sA0, sB0);
+      __syncthreads();
+      load(ra0, rb0, min(t + 1, nslab - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
+    }
+  } else {
+  load(ra0, rb0, 0);
+  store(ra0, rb0, sA0, sB0);
+  load(ra0, rb0, 1);
+  load(ra1, rb1, min(2, nslab - 1));
+  __syncthreads();
+  // sched_barrier(0) keeps the compiler from moving the loads past the
+  // multiplies that are meant to hide their latency.
+  for (int t = 0; t < nslab - 2; t += 2) {
+    mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
+    store(ra0, rb0, sA1, sB1);
+    __syncthreads();
+    load(ra0, rb0, t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
+    store(ra1, rb1, sA0, sB0);
+    __syncthreads();
+    load(ra1, rb1, min(t + 4, nslab - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
+  store(ra0, rb0, sA1, sB1);
+  __syncthreads();
+  mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // acc[i][j][4 g + r] = C[m][n], m = mb + 32 i + l32, n = nb + 32 j + 8 g + 4 lh + r
+  // with mb = TI*256 + wm*128, nb = TJ*128 + wn*64. Each row group i (32 rows
+  // x 64 columns per wave) is staged through LDS (fp32, 68-float pitch) so
+  // global accesses are row-contiguous: "direct" reads 4 columns of a row,
+  // "transposed" reads 8 consecutive rows of one column.
+  const int l32 = lane & 31, lh = lane >> 5;
+  constexpr bool F16 = OP == OP_F16;
+  constexpr int PITCH = 68;
+  const int mb = TI * TM + wm * 128, nb = TJ * TN + wn * 64;
+  float* const stg = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
+  __syncthreads();  // every wave is done reading the operand stages
+
+  auto stage_acc = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4_t*>(stg + l32 * PITCH + 32 * j + 8 * g + 4 * lh) =
+            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+  };
+  // direct access q (0..7): row 4 q + lane / 16 of the group, columns 4 (lane % 16)..+3
+  auto drow = [&](int q) { return 4 * q + (lane >> 4); };
+  const int dcol = 4 * (lane & 15);
+  // transposed access q (0..3): column (lane + 64 q) / 4, rows 8 ((lane + 64 q) % 4)..+7
+  auto tcol = [&](int q) { return (lane + 64 * q) >> 2; };
+  auto trow = [&](int q) { return 8 * ((lane + 64 * q) & 3); };
+
+  if (KIND == GRAM || KIND == POLY) {
+    char* C = P.ws + (KIND == GRAM ? M.a_off : M.b_off);
+    const char* Am = P.ws + M.a_off;
+    const int64_t ld = M.mp;
+    const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_acc(i);
+      __syncthreads();
+      const int m0 = mb + 32 * i;
+      // direct rows (POLY: bias loads first, then b A + c acc back into LDS)
+      u32x2 bias[8];
+      if (KIND == POLY) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          bias[q] = *reinterpret_cast<const u32x2*>(Am + (int64_t(m0 + drow(q)) * ld + nb + dcol) * 2);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = m0 + drow(q), n = nb + dcol;
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
+        if (KIND == POLY) {
+          const float a4[4] = {Op<OP>::load16(bias[q].x & 0xffffu), Op<OP>::load16(bias[q].x >> 16),
+                               Op<OP>::load16(bias[q].y & 0xffffu), Op<OP>::load16(bias[q].y >> 16)};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = __fmaf_rn(P.c, v[r], P.b * a4[r]);
+          *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = v;
+        }
+        if (strict || m <= n) {
+          *reinterpret_cast<uint2*>(C + (int64_t(m) * ld + n) * 2) = pack4(v[0], v[1], v[2], v[3], F16);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (m <= n + r) Op<OP>::store(C, int64_t(m) * ld + n + r, v[r]);
+        }
+      }
+      if (KIND == POLY) __syncthreads();
+      // mirrored rows: C[n][m..m+7] = C[m..m+7][n]
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = tcol(q), rr = trow(q);
+        const int n = nb + cc, m = m0 + rr;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
+        if (strict || m + 7 < n) {
+          const uint2 lo = pack4(v[0], v[1], v[2], v[3], F16), hi = pack4(v[4], v[5], v[6], v[7], F16);
+          *reinterpret_cast<uint4*>(C + (int64_t(n) * ld + m) * 2) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (m + e < n) Op<OP>::store(C, int64_t(n) * ld + m + e, v[e]);
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    const int64_t ldx = M.np;
+    float* xm = reinterpret_cast<float*>(P.ws + M.xm_off);
+    char* xn = P.ws + xo_sel(M, P.cur ^ 1);
+    T* o = static_cast<T*>(M.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_acc(i);
+      __syncthreads();
+      const int m0 = mb + 32 * i;
+      f32x4_t xv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        xv[q] = *reinterpret_cast<const f32x4_t*>(xm + int64_t(m0 + drow(q)) * ldx + nb + dcol);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = m0 + drow(q), n = nb + dcol;
+        const int64_t off = int64_t(m) * ldx + n;
+        f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = __fmaf_rn(P.a, xv[q][r], x[r]);
+        if (!P.last) {
+          *reinterpret_cast<f32x4_t*>(xm + off) = x;
+          *reinterpret_cast<uint2*>(xn + off * 2) = pack4(x[0], x[1], x[2], x[3], F16);
+        } else if (!M.tall) {
+          // last step, rows<=cols matrix: `out` rows m, columns n..n+3
+          if (m < M.m) {
+            const int64_t co = int64_t(m) * M.ld + n;
+            if (M.vec_ok && n + 3 < M.n) {
+              if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<uint2*>(o + co) = pack4(x[0], x[1], x[2], x[3], false);
+              else
+                *reinterpret_cast<f32x4_t*>(o + co) = x;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < M.n) Elem<T>::store(o, co + r, x[r]);
+            }
+          }
+        } else {
+          *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = x;  // for the transposed write
+        }
+      }
+      if (P.last && M.tall) {
+        __syncthreads();
+        // `out` is the transpose: out rows n, columns m..m+7
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cc = tcol(q), rr = trow(q);
+          const int n = nb + cc, m = m0 + rr;
+          if (n >= M.n) continue;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
+          const int64_t co = int64_t(n) * M.ld + m;
+          if (M.vec_ok && m + 7 < M.m) {
+            if constexpr (sizeof(T) == 2) {
+              const uint2 lo = pack4(v[0], v[1], v[2], v[3], false), hi = pack4(v[4], v[5], v[6], v[7], false);
+              *reinterpret_cast<uint4*>(o + co) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+              *reinterpret_cast<f32x4_t*>(o + co) = f32x4_t{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4_t*>(o + co + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (m + e < M.m) Elem<T>::store(o, co + e, v[e]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 template <typename T, int OP>
@@ -529,9 +1005,18 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
   switch (kind) {
     case MUON_K_MOMENTUM: hipLaunchKernelGGL(momentum_kernel<T>, g, b, 0, s, a); break;
     case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;
-    case MUON_K_GRAM: hipLaunchKernelGGL((gemm_kernel<T, OP, GRAM>), g, b, 0, s, a); break;
-    case MUON_K_POLY: hipLaunchKernelGGL((gemm_kernel<T, OP, POLY>), g, b, 0, s, a); break;
-    case MUON_K_UPDATE: hipLaunchKernelGGL((gemm_kernel<T, OP, UPDATE>), g, b, 0, s, a); break;
+    case MUON_K_GRAM:
+      if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, GRAM>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM>), g, b, 0, s, a);
+      break;
+    case MUON_K_POLY:
+      if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, POLY>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, POLY>), g, b, 0, s, a);
+      break;
+    case MUON_K_UPDATE:
+      if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, UPDATE>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE>), g, b, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

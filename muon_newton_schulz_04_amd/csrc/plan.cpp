@@ -110,10 +110,18 @@ Schedule assign_xcd(std::vector<Chunk> chunks) {
   }
   std::vector<std::vector<WorkItem>> lists(kNumXcd);
   size_t longest = 0;
+  for (int x = 0; x < kNumXcd; ++x) std::sort(bins[x].begin(), bins[x].end());
   for (int x = 0; x < kNumXcd; ++x) {
-    std::sort(bins[x].begin(), bins[x].end());  // chunk index order = matrix order
-    for (size_t ci : bins[x])
-      lists[x].insert(lists[x].end(), chunks[ci].items.begin(), chunks[ci].items.end());
+    // Longest items first (they would otherwise form the tail); items of
+    // equal cost stay in matrix order, so one matrix's tiles run together.
+    std::vector<std::pair<double, WorkItem>> its;
+    for (size_t ci : bins[x]) {
+      const double per = chunks[ci].cost / double(chunks[ci].items.size());
+      for (const WorkItem& w : chunks[ci].items) its.push_back({per, w});
+    }
+    std::stable_sort(its.begin(), its.end(),
+                     [](const auto& p, const auto& q) { return p.first > q.first; });
+    for (const auto& p : its) lists[x].push_back(p.second);
     longest = std::max(longest, lists[x].size());
   }
   Schedule s;
@@ -168,8 +176,8 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     I.tall = M.rows > M.cols;
     I.m = static_cast<int32_t>(std::min(M.rows, M.cols));
     I.n = static_cast<int32_t>(std::max(M.rows, M.cols));
-    I.mp = static_cast<int32_t>(round_up(I.m, kGemmTile));
-    I.np = static_cast<int32_t>(round_up(I.n, kGemmTile));
+    I.mp = static_cast<int32_t>(round_up(I.m, bf16 ? kTileM16 : kGemmTile));
+    I.np = static_cast<int32_t>(round_up(I.n, bf16 ? kTileN16 : kGemmTile));
     auto aligned16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     I.vec_ok = aligned16(M.grad) && aligned16(M.out) && (!M.momentum || aligned16(M.momentum)) &&
                (M.ld * es) % 16 == 0 && (M.cols * es) % 16 == 0;
@@ -231,19 +239,24 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
         per[MUON_K_NORMALIZE][i].push_back({i, ti, tj, 0});
         cost[MUON_K_NORMALIZE][i].push_back(1.0);
       }
-    const int32_t gt = I.mp / kGemmTile, gn = I.np / kGemmTile;
+    // Tiles of tm x tn; gram/poly keep the tiles that reach the upper
+    // triangle (first row <= last column: tj * tn + tn - 1 >= ti * tm).
+    const int32_t tm = bf16 ? kTileM16 : kGemmTile, tn = bf16 ? kTileN16 : kGemmTile;
+    const int32_t gt = I.mp / tm, gc = I.mp / tn, gn = I.np / tn;
+    const double area = double(tm) * tn;
     for (int32_t ti = 0; ti < gt; ++ti)
-      for (int32_t tj = ti; tj < gt; ++tj) {
+      for (int32_t tj = 0; tj < gc; ++tj) {
+        if (int64_t(tj) * tn + tn - 1 < int64_t(ti) * tm) continue;
         per[MUON_K_GRAM][i].push_back({i, ti, tj, 0});
-        cost[MUON_K_GRAM][i].push_back(double(I.np));
+        cost[MUON_K_GRAM][i].push_back(area * I.np);
         per[MUON_K_POLY][i].push_back({i, ti, tj, 0});
-        cost[MUON_K_POLY][i].push_back(double(I.mp));
+        cost[MUON_K_POLY][i].push_back(area * I.mp);
       }
     // update: column panels outer so neighbouring tiles share the X panel
     for (int32_t tj = 0; tj < gn; ++tj)
       for (int32_t ti = 0; ti < gt; ++ti) {
         per[MUON_K_UPDATE][i].push_back({i, ti, tj, 0});
-        cost[MUON_K_UPDATE][i].push_back(double(I.mp));
+        cost[MUON_K_UPDATE][i].push_back(area * I.mp);
       }
     for (int k = 0; k < MUON_K_COUNT; ++k)
       for (double c : cost[k][i]) total_cost[k] += c;

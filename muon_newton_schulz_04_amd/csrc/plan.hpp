@@ -12,7 +12,9 @@
 namespace muon {
 
 // Tile sizes shared by the planner and the kernels.
-constexpr int kGemmTile = 128;         // output tile of the three matrix-core kernels
+constexpr int kGemmTile = 128;         // output tile of the matrix-core kernels (fp32 sets)
+constexpr int kTileM16 = 256;          // 16-bit-operand engine (bf16 sets): 256 x 128 tiles
+constexpr int kTileN16 = 128;
 constexpr int kNormTile = 64;          // tile of the normalise / layout kernel
 constexpr int kMomentumElems = 16384;  // target elements per momentum work item
 constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X
@@ -26,7 +28,7 @@ struct MatInfo {
   int64_t ld;        // caller row stride (elements)
   int32_t rows, cols;
   int32_t m, n;      // m = min(rows, cols), n = max(rows, cols)
-  int32_t mp, np;    // m, n rounded up to kGemmTile
+  int32_t mp, np;    // m, n padded to the engine's tile multiples
   int32_t tall;      // rows > cols: the iteration runs on the transpose
   int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
   int64_t xm_off;    // fp32 master X (bf16 sets), -1 otherwise

@@ -111,7 +111,7 @@ def expected_ws(shapes, dtype):
     off = ru(parts * 4, 256)
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
-        mp, np_ = ru(m, 128), ru(n, 128)
+        mp, np_ = ru(m, 256 if dtype == mu.MUON_BF16 else 128), ru(n, 128)
         sizes = ([mp * np_ * 4, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
                  if dtype == mu.MUON_BF16 else
                  [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
@@ -134,10 +134,13 @@ SHAPE_SETS = {
 }
 
 
+@pytest.mark.parametrize("dtype", [mu.MUON_BF16, mu.MUON_F32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("setname", list(SHAPE_SETS))
-def test_schedules_cover_every_tile_exactly_once(lib, setname):
+def test_schedules_cover_every_tile_exactly_once(lib, setname, dtype):
     shapes = SHAPE_SETS[setname]
-    scheds = [mu.muon_schedule_query(shapes, mu.MUON_BF16, k) for k in range(5)]
+    tm = 256 if dtype == mu.MUON_BF16 else 128
+    tn = 128
+    scheds = [mu.muon_schedule_query(shapes, dtype, k) for k in range(5)]
     for k, s in enumerate(scheds):
         assert len(s) % 8 == 0, "grid is a multiple of the XCD count"
         empty = s[:, 0] < 0
@@ -147,7 +150,7 @@ def test_schedules_cover_every_tile_exactly_once(lib, setname):
     assert len(np.unique(slots)) == len(slots) and slots.min() == 0 and slots.max() == len(slots) - 1
     for i, (r, c) in enumerate(shapes):
         m, n = min(r, c), max(r, c)
-        mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+        mp, np_ = -(-m // tm) * tm, -(-n // tn) * tn
         mi = mom[mom[:, 0] == i]
         rows = np.zeros(r, int)
         for _, r0, nr, _s in mi:
@@ -155,12 +158,18 @@ def test_schedules_cover_every_tile_exactly_once(lib, setname):
         assert np.all(rows == 1), "every row summed exactly once"
         ni = nrm[nrm[:, 0] == i]
         assert sorted(map(tuple, ni[:, 1:3])) == [(a, b) for a in range(mp // 64) for b in range(np_ // 64)]
-        want_tri = [(a, b) for a in range(mp // 128) for b in range(a, mp // 128)]
+        # tiles that reach the upper triangle, and every upper element in exactly one
+        want_tri = [(a, b) for a in range(mp // tm) for b in range(mp // tn)
+                    if b * tn + tn - 1 >= a * tm]
         for s in (gram, poly):
             si = s[s[:, 0] == i]
             assert sorted(map(tuple, si[:, 1:3])) == want_tri
+            cover = np.zeros((mp, mp), int)
+            for _, a, b, _c in si:
+                cover[a * tm:(a + 1) * tm, b * tn:(b + 1) * tn] += 1
+            assert np.all(np.triu(cover) == np.triu(np.ones((mp, mp), int)))
         ui = upd[upd[:, 0] == i]
-        assert sorted(map(tuple, ui[:, 1:3])) == [(a, b) for a in range(mp // 128) for b in range(np_ // 128)]
+        assert sorted(map(tuple, ui[:, 1:3])) == [(a, b) for a in range(mp // tm) for b in range(np_ // tn)]
 
 
 def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):
@@ -173,7 +182,7 @@ def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):
         if mat < 0:
             continue
         x = b % 8
-        cost[x] += max(shapes[mat])
+        cost[x] += max(shapes[mat])      # all tiles have the same area
         if owner.setdefault(mat, x) != x:
             split += 1
     assert cost.max() / cost.mean() < 1.1
