@@ -185,15 +185,17 @@ muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable);
 muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches);
 
 /* Workspace layout of matrix `idx` of a plan (byte offsets from the
- * workspace base; -1 where a buffer does not exist). x_master: fp32 X
- * (rows<=cols orientation, padded mp x np, row-major); x_op0/x_op1: the
- * two operand copies (bf16 sets; fp32 sets use two fp32 masters instead);
- * gram: A (mp x mp); poly: B (mp x mp). Element types: bf16 for bf16 sets
- * except x_master; fp32 for fp32 sets. The buffer that holds the final X of
- * a step of k iterations is x_op[k % 2] / the master. */
+ * workspace base; -1 where a buffer does not exist). All buffers use the
+ * rows<=cols orientation, zero-padded to mp x np (X) or mp x mp (A, B),
+ * row-major. bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
+ * matrix-core operand, ping-pong between steps) and x_lo the low part in
+ * the same format (X = hi + lo * 2^-11 for fp16 operands, hi + lo for bf16
+ * operands); gram (A) and poly (B) are 16-bit. fp32 sets: x_op0/x_op1 are
+ * fp32 X (ping-pong), gram/poly fp32, x_lo = -1. After a step of k
+ * iterations X is in x_op[k % 2]. */
 typedef struct {
   int64_t m, n, mp, np;
-  int64_t x_master, x_op0, x_op1, gram, poly;
+  int64_t x_lo, x_op0, x_op1, gram, poly;
 } muon_buffer_info;
 
 muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffer_info* info);

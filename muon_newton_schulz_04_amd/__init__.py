@@ -50,7 +50,7 @@ class MuonConfig(ctypes.Structure):
 
 class MuonBufferInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("m", "n", "mp", "np", "x_master", "x_op0", "x_op1", "gram", "poly")]
+                ("m", "n", "mp", "np", "x_lo", "x_op0", "x_op1", "gram", "poly")]
 
 
 _lib = None

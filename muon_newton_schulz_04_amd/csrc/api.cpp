@@ -336,7 +336,7 @@ muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffe
   info->n = I.n;
   info->mp = I.mp;
   info->np = I.np;
-  info->x_master = I.xm_off;
+  info->x_lo = I.xl_off;
   info->x_op0 = I.xo_off[0];
   info->x_op1 = I.xo_off[1];
   info->gram = I.a_off;

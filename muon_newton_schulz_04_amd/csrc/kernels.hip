@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "launch.hpp"
 
@@ -79,6 +80,16 @@ template <> struct Op<OP_F32> {
 };
 template <> struct Op<OP_F16> {
   static constexpr int bytes = 2;
+  // X = hi + lo * 2^-11: hi is the operand, lo the scaled residual (about
+  // 22 significant bits together; the scaling keeps lo out of subnormals)
+  static __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
+    const _Float16 h = static_cast<_Float16>(x);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x - static_cast<float>(h)) * 2048.f));
+  }
+  static __device__ __forceinline__ float join(uint32_t hi, uint32_t lo) {
+    return __fmaf_rn(load16(lo), 1.f / 2048.f, load16(hi));
+  }
   static __device__ __forceinline__ float load16(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
   }
@@ -94,6 +105,14 @@ template <> struct Op<OP_F16> {
 };
 template <> struct Op<OP_BF16> {
   static constexpr int bytes = 2;
+  // X = hi + lo (about 17 significant bits together)
+  static __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
+    hi = f2bf(x);
+    lo = f2bf(x - bf2f(static_cast<uint16_t>(hi)));
+  }
+  static __device__ __forceinline__ float join(uint32_t hi, uint32_t lo) {
+    return bf2f(static_cast<uint16_t>(hi)) + bf2f(static_cast<uint16_t>(lo));
+  }
   static __device__ __forceinline__ float load16(uint32_t h) { return bf2f(static_cast<uint16_t>(h)); }
   static __device__ __forceinline__ uint16_t bits(float v) { return f2bf(v); }
   static __device__ __forceinline__ float load(const void* p, int64_t i) {
@@ -307,14 +326,17 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
     const int v = threadIdx.x + 256 * h;
     const int64_t off = int64_t(i0 + (v >> 3)) * M.np + j0 + (v & 7) * 8;
     if constexpr (OP != OP_F32) {
-      float* xm = reinterpret_cast<float*>(A.ws + M.xm_off) + off;
-      reinterpret_cast<f32x4_t*>(xm)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
-      reinterpret_cast<f32x4_t*>(xm)[1] = f32x4_t{u[h][4], u[h][5], u[h][6], u[h][7]};
-      u32x4_t w;
+      u32x4_t whi, wlo;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = uint32_t(Op<OP>::bits(u[h][2 * q])) | (uint32_t(Op<OP>::bits(u[h][2 * q + 1])) << 16);
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = w;
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h0, l0, h1, l1;
+        Op<OP>::split(u[h][2 * q], h0, l0);
+        Op<OP>::split(u[h][2 * q + 1], h1, l1);
+        whi[q] = h0 | (h1 << 16);
+        wlo[q] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = whi;
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xl_off) + off) = wlo;
     } else {
       float* x0 = reinterpret_cast<float*>(A.ws + M.xo_off[0]) + off;
       reinterpret_cast<f32x4_t*>(x0)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
@@ -453,6 +475,7 @@ __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, c
 // UPDATE: X = a X + B X on all tiles.
 template <typename T, int OP, int KIND>
 __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
+  static_assert(OP == OP_F32, "the 128 x 128 engine serves fp32 sets");
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
   const MatInfo& M = P.mats[it.mat];
@@ -556,22 +579,14 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t off = int64_t(gi0 + r) * ldx + gj;
-            if constexpr (OP != OP_F32) {
-              float* xm = reinterpret_cast<float*>(P.ws + M.xm_off);
-              const float v = __fmaf_rn(P.a, xm[off], acc[i][j][r]);
-              xm[off] = v;
-              Op<OP>::store(P.ws + xo_sel(M, P.cur ^ 1), off, v);
-            } else {
-              const float* xc = reinterpret_cast<const float*>(P.ws + xo_sel(M, P.cur));
-              const float v = __fmaf_rn(P.a, xc[off], acc[i][j][r]);
-              reinterpret_cast<float*>(P.ws + xo_sel(M, P.cur ^ 1))[off] = v;
-            }
+            const float* xc = reinterpret_cast<const float*>(P.ws + xo_sel(M, P.cur));
+            const float v = __fmaf_rn(P.a, xc[off], acc[i][j][r]);
+            reinterpret_cast<float*>(P.ws + xo_sel(M, P.cur ^ 1))[off] = v;
           }
         }
     } else {
       // last step: out in the caller's layout and dtype, valid region only
-      const float* xsrc = reinterpret_cast<const float*>(
-          P.ws + (OP != OP_F32 ? M.xm_off : xo_sel(M, P.cur)));
+      const float* xsrc = reinterpret_cast<const float*>(P.ws + xo_sel(M, P.cur));
       char* o = static_cast<char*>(M.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -622,7 +637,17 @@ namespace e16 {
 constexpr int TM = 256, TN = 128;
 // PIPE 2: two LDS stages + two register sets, one workgroup per CU.
 // PIPE 1: one LDS stage + one register set, two workgroups per CU.
+// PIPE 3: ring of NST direct-to-LDS stages of 32-k slabs (NST <= 3: two
+//         workgroups per CU; larger: one).
 constexpr int PIPE = MUON_GEMM_PIPE;
+#ifndef MUON_GEMM_NST
+#define MUON_GEMM_NST 6
+#endif
+constexpr int NST = MUON_GEMM_NST;
+constexpr int WG_PER_CU = (PIPE == 1 || (PIPE == 3 && NST <= 3)) ? 2 : 1;
+// PIPE 4: PIPE 2's buffers with one barrier per slab: while slab t is
+//         multiplied, slab t+1 goes from registers to the other LDS stage and
+//         slab t+3 is loaded into the registers just freed.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -729,13 +754,135 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
   return r;
 }
 
+
+
+// One 64-k slab like mma_slab, with `hook(ks)` called before each of the 4
+// k-steps; used to spread the next slab's LDS stores and global loads over
+// the multiplies (sched_barrier keeps each k-step's group together).
+template <int OP, bool KN, class Hook>
+__device__ __forceinline__ void mma_slab_hooked(f32x16_t (&acc)[4][2], const char* sA,
+                                                const char* sB, int wm, int wn, Hook&& hook) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = ks * 2 + lh;
+    u32x4 bf[2], af[4];
+    if constexpr (!KN) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows(wn * 64 + j * 32 + l32, ch));
+    } else {
+      const int s = lane & 15, h = lane >> 4;
+      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
+        const int chunk = col >> 3, byte = (col & 7) * 2;
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows(wm * 128 + i * 32 + l32, ch));
+    hook(ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---- PIPE 3: direct-to-LDS ring of 32-k slabs (64-byte rows for k-contiguous
+// operands, 256-byte rows for the [k][col] operand). Each
+// global_load_lds_dwordx4 fills 1 KB of LDS: lane i writes base + 16 i, so
+// the XOR swizzle is applied by choosing which global chunk lane i fetches.
+__device__ __forceinline__ int off_rows64(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Issues the DMA of one 32-k slab: row operand R rows (k contiguous), column
+// operand either TN rows (k contiguous) or 32 k-rows x TN columns.
+template <bool KN>
+__device__ __forceinline__ void dma_slab(char* sA, char* sB, const char* opA, int64_t lda,
+                                         const char* opB, int64_t ldb, int64_t k0) {
+  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // A: 16 instructions of 16 rows x 64 B
+    const int I = w + 4 * q, row = 16 * I + (i >> 2), lch = (i & 3) ^ ((row >> 2) & 3);
+    __builtin_amdgcn_global_load_lds(opA + row * lda + k0 * 2 + lch * 16,
+                                     (lds_void_t*)(sA + I * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int I = w + 4 * q;
+    if constexpr (!KN) {  // 8 instructions of 16 rows x 64 B
+      const int row = 16 * I + (i >> 2), lch = (i & 3) ^ ((row >> 2) & 3);
+      __builtin_amdgcn_global_load_lds(opB + row * ldb + k0 * 2 + lch * 16,
+                                       (lds_void_t*)(sB + I * 1024), 16, 0, 0);
+    } else {              // 8 instructions of 4 k-rows x 256 B
+      const int kr = 4 * I + (i >> 4);
+      const int lch = (i & 15) ^ ((((kr ^ ((kr >> 3) << 2)) & 7)) << 1);
+      __builtin_amdgcn_global_load_lds(opB + (k0 + kr) * ldb + lch * 16,
+                                       (lds_void_t*)(sB + I * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// One 32-k slab of this wave's 128 x 64 block (2 k-steps of 16).
+template <int OP, bool KN>
+__device__ __forceinline__ void mma_slab32(f32x16_t (&acc)[4][2], const char* sA, const char* sB,
+                                           int wm, int wn) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ch = ks * 2 + lh;
+    u32x4 bf[2], af[4];
+    if constexpr (!KN) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows64(wn * 64 + j * 32 + l32, ch));
+    } else {
+      const int s = lane & 15, h = lane >> 4;
+      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
+        const int chunk = col >> 3, byte = (col & 7) * 2;
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows64(wm * 128 + i * 32 + l32, ch));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
+  }
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
+#define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
 }  // namespace e16
 
 // bf16 sets. Item {mat, TI, TJ} of 256 x 128 tiles. GRAM/POLY: tiles that
 // reach the upper triangle (TJ >= 2 TI); each stored element (m <= n) is
 // mirrored to (n, m). UPDATE: X = a X + B X on all tiles.
 template <typename T, int OP, int KIND>
-__global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(StepArgs P) {
+__global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
@@ -744,10 +891,12 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
 
   // LDS: operand stages (PIPE 1: one, PIPE 2: two); reused by the epilogue.
   constexpr int STAGE = (TM + TN) * 128;
-  __shared__ __attribute__((aligned(16))) char lds[PIPE * STAGE];
+  constexpr int STAGE32 = (TM + TN) * 64;  // PIPE 3: 32-k slab
+  constexpr int LDS_BYTES = PIPE == 3 ? NST * STAGE32 : (PIPE == 1 ? 1 : 2) * STAGE;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   char* const sA0 = lds;
   char* const sB0 = lds + TM * 128;
-  char* const sA1 = lds + (PIPE == 2 ? STAGE : 0);
+  char* const sA1 = lds + (PIPE == 1 ? 0 : STAGE);  // (PIPE 1/2/4)
   char* const sB1 = sA1 + TM * 128;
 
   const int TI = it.a, TJ = it.b;
@@ -801,7 +950,87 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
   // K is a multiple of 128: an even number (>= 2) of 64-element slabs.
   // Loads past the last slab are clamped to it (valid, unused).
   const int nslab = static_cast<int>(K >> 6);
-  if constexpr (PIPE == 1) {
+  if constexpr (PIPE == 4) {
+    // per-thread pieces of a slab: A rows in ra[0..7], B rows (or k-rows) in rb[0..3]
+    auto st_piece = [&](const u32x4 (&ra)[TM / 32], const u32x4 (&rb)[4], char* a, char* b, int q) {
+      const int t = threadIdx.x;
+      if (q < 8) {
+        *reinterpret_cast<u32x4*>(a + off_rows((t >> 3) + 32 * q, t & 7)) = ra[q];
+      } else {
+        const int r = q - 8;
+        if constexpr (KN) *reinterpret_cast<u32x4*>(b + off_kn((t >> 4) + 16 * r, t & 15)) = rb[r];
+        else *reinterpret_cast<u32x4*>(b + off_rows((t >> 3) + 32 * r, t & 7)) = rb[r];
+      }
+    };
+    auto ld_piece = [&](u32x4 (&ra)[TM / 32], u32x4 (&rb)[4], int64_t slab, int q) {
+      const int t = threadIdx.x;
+      const int64_t k0 = slab * 64;
+      if (q < 8) {
+        ra[q] = *reinterpret_cast<const u32x4*>(opA + int64_t((t >> 3) + 32 * q) * lda + k0 * 2 + (t & 7) * 16);
+      } else {
+        const int r = q - 8;
+        if constexpr (KN)
+          rb[r] = *reinterpret_cast<const u32x4*>(opB + (k0 + (t >> 4) + 16 * r) * ldb + (t & 15) * 16);
+        else
+          rb[r] = *reinterpret_cast<const u32x4*>(opB + int64_t((t >> 3) + 32 * r) * ldb + k0 * 2 + (t & 7) * 16);
+      }
+    };
+    load(ra0, rb0, 0);
+    store(ra0, rb0, sA0, sB0);
+    load(ra0, rb0, 1);
+    load(ra1, rb1, min(2, nslab - 1));
+    __syncthreads();
+    for (int t = 0; t < nslab - 2; t += 2) {
+      // slab t from stage 0; slab t+1 (ra0) -> stage 1; ra0 <- slab t+3
+      mma_slab_hooked<OP, KN>(acc, sA0, sB0, wm, wn, [&](int ks) {
+#pragma unroll
+        for (int q = 3 * ks; q < 3 * ks + 3; ++q) {
+          st_piece(ra0, rb0, sA1, sB1, q);
+          ld_piece(ra0, rb0, t + 3, q);
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // slab t+1 from stage 1; slab t+2 (ra1) -> stage 0; ra1 <- slab t+4
+      const int64_t s4 = min(t + 4, nslab - 1);
+      mma_slab_hooked<OP, KN>(acc, sA1, sB1, wm, wn, [&](int ks) {
+#pragma unroll
+        for (int q = 3 * ks; q < 3 * ks + 3; ++q) {
+          st_piece(ra1, rb1, sA0, sB0, q);
+          ld_piece(ra1, rb1, s4, q);
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    mma_slab_hooked<OP, KN>(acc, sA0, sB0, wm, wn, [&](int ks) {
+#pragma unroll
+      for (int q = 3 * ks; q < 3 * ks + 3; ++q) st_piece(ra0, rb0, sA1, sB1, q);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
+  } else if constexpr (PIPE == 3) {
+    // ring of NST stages; slab t (32 k) lives in stage t % NST, NST-1 in flight
+    const int n32 = static_cast<int>(K >> 5);
+    auto stA = [&](int st) { return lds + st * STAGE32; };
+    auto stB = [&](int st) { return lds + st * STAGE32 + TM * 64; };
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+      dma_slab<KN>(stA(p), stB(p), opA, lda, opB, ldb, int64_t(min(p, n32 - 1)) * 32);
+    int st = 0;
+    for (int t = 0; t < n32; ++t) {
+      MUON_WAIT_VMCNT(6 * (NST - 2));  // this wave's loads of slab t are done
+      // Everyone's are, and slab t-1 is consumed. A bare s_barrier: the
+      // workgroup fence of __syncthreads would wait for all loads in flight;
+      // the memory clobber keeps the compiler from moving LDS accesses across.
+      asm volatile("s_barrier" ::: "memory");
+      const int stn = st == 0 ? NST - 1 : st - 1;  // stage of slab t+NST-1 (= t-1's)
+      dma_slab<KN>(stA(stn), stB(stn), opA, lda, opB, ldb,
+                   int64_t(min(t + NST - 1, n32 - 1)) * 32);  // past the end: a valid, unused slab
+      __builtin_amdgcn_sched_barrier(0);
+      mma_slab32<OP, KN>(acc, stA(st), stB(st), wm, wn);
+      st = st == NST - 1 ? 0 : st + 1;
+    }
+    MUON_WAIT_VMCNT(0);  // drain the trailing loads before the LDS is reused
+  } else if constexpr (PIPE == 1) {
     load(ra0, rb0, 0);
     for (int t = 0; t < nslab; ++t) {
       __syncthreads();
@@ -850,7 +1079,8 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
   float* const stg = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
   __syncthreads();  // every wave is done reading the operand stages
 
-  auto stage_acc = [&](int i) {
+  auto stage_acc = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -870,9 +1100,9 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
     const char* Am = P.ws + M.a_off;
     const int64_t ld = M.mp;
     const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      stage_acc(i);
+auto round = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      stage_acc(ic);
       __syncthreads();
       const int m0 = mb + 32 * i;
       // direct rows (POLY: bias loads first, then b A + c acc back into LDS)
@@ -920,31 +1150,47 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
         }
       }
       __syncthreads();
-    }
+    };
+    round(std::integral_constant<int, 0>{});
+    round(std::integral_constant<int, 1>{});
+    round(std::integral_constant<int, 2>{});
+    round(std::integral_constant<int, 3>{});
   } else {
     const int64_t ldx = M.np;
-    float* xm = reinterpret_cast<float*>(P.ws + M.xm_off);
-    char* xn = P.ws + xo_sel(M, P.cur ^ 1);
+    const char* xh = P.ws + xo_sel(M, P.cur);      // hi part of X (operand)
+    char* xl = P.ws + M.xl_off;                      // lo part, updated in place
+    char* xn = P.ws + xo_sel(M, P.cur ^ 1);        // next hi part
     T* o = static_cast<T*>(M.out);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      stage_acc(i);
+auto round = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_sched_barrier(0);  // keep each round's loads inside it
+      stage_acc(ic);
       __syncthreads();
       const int m0 = mb + 32 * i;
-      f32x4_t xv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        xv[q] = *reinterpret_cast<const f32x4_t*>(xm + int64_t(m0 + drow(q)) * ldx + nb + dcol);
+      for (int qb = 0; qb < 8; qb += 4) {
+      u32x2 hv[8], lv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = qb; q < qb + 4; ++q) {
+        const int64_t off = int64_t(m0 + drow(q)) * ldx + nb + dcol;
+        hv[q] = *reinterpret_cast<const u32x2*>(xh + off * 2);
+        lv[q] = *reinterpret_cast<const u32x2*>(xl + off * 2);
+      }
+#pragma unroll
+      for (int q = qb; q < qb + 4; ++q) {
         const int m = m0 + drow(q), n = nb + dcol;
         const int64_t off = int64_t(m) * ldx + n;
         f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
+        const uint32_t hw[4] = {hv[q].x & 0xffffu, hv[q].x >> 16, hv[q].y & 0xffffu, hv[q].y >> 16};
+        const uint32_t lw[4] = {lv[q].x & 0xffffu, lv[q].x >> 16, lv[q].y & 0xffffu, lv[q].y >> 16};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = __fmaf_rn(P.a, xv[q][r], x[r]);
+        for (int r = 0; r < 4; ++r) x[r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), x[r]);
         if (!P.last) {
-          *reinterpret_cast<f32x4_t*>(xm + off) = x;
-          *reinterpret_cast<uint2*>(xn + off * 2) = pack4(x[0], x[1], x[2], x[3], F16);
+          uint32_t nh[4], nl[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Op<OP>::split(x[r], nh[r], nl[r]);
+          *reinterpret_cast<uint2*>(xn + off * 2) = make_uint2(nh[0] | (nh[1] << 16), nh[2] | (nh[3] << 16));
+          *reinterpret_cast<uint2*>(xl + off * 2) = make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
         } else if (!M.tall) {
           // last step, rows<=cols matrix: `out` rows m, columns n..n+3
           if (m < M.m) {
@@ -963,6 +1209,7 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
         } else {
           *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = x;  // for the transposed write
         }
+      }
       }
       if (P.last && M.tall) {
         __syncthreads();
@@ -992,7 +1239,11 @@ __global__ __launch_bounds__(256, e16::PIPE == 1 ? 2 : 1) void gemm16_kernel(Ste
         }
       }
       __syncthreads();
-    }
+    };
+    round(std::integral_constant<int, 0>{});
+    round(std::integral_constant<int, 1>{});
+    round(std::integral_constant<int, 2>{});
+    round(std::integral_constant<int, 3>{});
   }
 }
 

@@ -171,7 +171,7 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     I.ld = M.ld;
     I.rows = static_cast<int32_t>(M.rows);
     I.cols = static_cast<int32_t>(M.cols);
-    I.xm_off = I.xo_off[0] = I.xo_off[1] = I.a_off = I.b_off = -1;
+    I.xl_off = I.xo_off[0] = I.xo_off[1] = I.a_off = I.b_off = -1;
     if (M.rows == 0 || M.cols == 0) continue;
     I.tall = M.rows > M.cols;
     I.m = static_cast<int32_t>(std::min(M.rows, M.cols));
@@ -200,7 +200,7 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     const size_t xel = static_cast<size_t>(I.mp) * I.np;
     const size_t ael = static_cast<size_t>(I.mp) * I.mp;
     if (bf16) {
-      I.xm_off = take(xel * 4);
+      I.xl_off = take(xel * 2);
       I.xo_off[0] = take(xel * 2);
       I.xo_off[1] = take(xel * 2);
       I.a_off = take(ael * 2);

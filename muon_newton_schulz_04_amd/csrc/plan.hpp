@@ -31,8 +31,10 @@ struct MatInfo {
   int32_t mp, np;    // m, n padded to the engine's tile multiples
   int32_t tall;      // rows > cols: the iteration runs on the transpose
   int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
-  int64_t xm_off;    // fp32 master X (bf16 sets), -1 otherwise
-  int64_t xo_off[2]; // operand copies (bf16) / ping-pong masters (fp32)
+  int64_t xl_off;    // bf16 sets: low part of X (X = hi + lo * 2^-11 for fp16
+                     // operands, hi + lo for bf16 operands), -1 otherwise
+  int64_t xo_off[2]; // bf16 sets: ping-pong high parts (the matrix-core
+                     // operand); fp32 sets: ping-pong fp32 X
   int64_t a_off;     // A = X X^T
   int64_t b_off;     // B = b A + c A A
   int32_t part_off;  // first slot of this matrix's sum-of-squares partials

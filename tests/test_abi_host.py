@@ -112,7 +112,7 @@ def expected_ws(shapes, dtype):
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
         mp, np_ = ru(m, 256 if dtype == mu.MUON_BF16 else 128), ru(n, 128)
-        sizes = ([mp * np_ * 4, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
+        sizes = ([mp * np_ * 2, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
                  if dtype == mu.MUON_BF16 else
                  [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
         for s in sizes:
