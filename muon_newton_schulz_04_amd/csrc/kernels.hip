@@ -35,12 +35,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- bf16 bits
 
-// float -> bfloat16 bits, round to nearest, ties to even (NaN stays NaN).
+// float -> bfloat16 bits, round to nearest, ties to even (gfx950's
+// v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
@@ -223,6 +221,20 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
 // out row-major, zeros in the padding. With zero steps the scaled values go
 // straight to `out` in the caller's layout.
 
+// fp16 operand sets keep the low part of X in the update kernel's
+// accumulator order: per 256 x 128 tile, per wave, per accumulator group
+// (i, j, g) a contiguous 64-lane x 4-element block. Lane loads and stores of
+// the update epilogue are then contiguous across the wave. Element index of
+// X(m, n) in that layout (np = padded row length):
+__device__ __forceinline__ int64_t lo_index(int m, int n, int np) {
+  const int tile = (m >> 8) * (np >> 7) + (n >> 7);
+  const int mm = m & 255, nn = n & 127;
+  const int wave = (mm >> 7) * 2 + (nn >> 6);
+  const int lane = (mm & 31) + 32 * ((nn >> 2) & 1);
+  const int grp = (((mm >> 5) & 3) * 2 + ((nn >> 5) & 1)) * 4 + ((nn >> 3) & 3);
+  return (((int64_t(tile) * 4 + wave) * 32 + grp) * 64 + lane) * 4 + (nn & 3);
+}
+
 template <typename T, int OP>
 __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
@@ -336,7 +348,14 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
         wlo[q] = l0 | (l1 << 16);
       }
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = whi;
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xl_off) + off) = wlo;
+      uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
+      if constexpr (OP == OP_F16) {  // two runs of 4 in accumulator order
+        const int m = i0 + (v >> 3), n = j0 + (v & 7) * 8;
+        *reinterpret_cast<uint2*>(lo + lo_index(m, n, M.np)) = make_uint2(wlo[0], wlo[1]);
+        *reinterpret_cast<uint2*>(lo + lo_index(m, n + 4, M.np)) = make_uint2(wlo[2], wlo[3]);
+      } else {
+        *reinterpret_cast<u32x4_t*>(lo + off) = wlo;
+      }
     } else {
       float* x0 = reinterpret_cast<float*>(A.ws + M.xo_off[0]) + off;
       reinterpret_cast<f32x4_t*>(x0)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
@@ -661,14 +680,22 @@ __device__ __forceinline__ int off_kn(int k, int chunk) {
   return k * 256 + ((chunk ^ (((k ^ ((k >> 3) << 2)) & 7) << 1)) << 4);
 }
 
+// Operand slabs are read with buffer loads: a scalar resource descriptor
+// per slab (so offsets stay small for any matrix size) and one 32-bit
+// per-lane offset, instead of a 64-bit address per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
 template <int R>  // R rows x 128 bytes at base + row*ldb + k0b
 __device__ __forceinline__ void load_rows(u32x4 (&r)[R / 32], const char* base, int64_t ldb,
                                           int64_t k0b) {
   const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = slab_rsrc(base + k0b);
+  const int32_t vo = (t >> 3) * int32_t(ldb) + (t & 7) * 16;
 #pragma unroll
   for (int q = 0; q < R / 32; ++q)
-    r[q] = *reinterpret_cast<const u32x4*>(base + int64_t((t >> 3) + 32 * q) * ldb + k0b +
-                                           (t & 7) * 16);
+    r[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 32 * q * int32_t(ldb), 0);
 }
 template <int R>
 __device__ __forceinline__ void store_rows(char* lds, const u32x4 (&r)[R / 32]) {
@@ -680,9 +707,11 @@ __device__ __forceinline__ void store_rows(char* lds, const u32x4 (&r)[R / 32]) 
 // 64 k-rows x 256 bytes at base + (k0 + k)*ldb
 __device__ __forceinline__ void load_kn(u32x4 (&r)[4], const char* base, int64_t ldb, int64_t k0) {
   const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = slab_rsrc(base + k0 * ldb);
+  const int32_t vo = (t >> 4) * int32_t(ldb) + (t & 15) * 16;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    r[q] = *reinterpret_cast<const u32x4*>(base + (k0 + (t >> 4) + 16 * q) * ldb + (t & 15) * 16);
+    r[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 16 * q * int32_t(ldb), 0);
 }
 __device__ __forceinline__ void store_kn(char* lds, const u32x4 (&r)[4]) {
   const int t = threadIdx.x;
@@ -881,12 +910,24 @@ __device__ __forceinline__ void mma_slab32(f32x16_t (&acc)[4][2], const char* sA
 // bf16 sets. Item {mat, TI, TJ} of 256 x 128 tiles. GRAM/POLY: tiles that
 // reach the upper triangle (TJ >= 2 TI); each stored element (m <= n) is
 // mirrored to (n, m). UPDATE: X = a X + B X on all tiles.
-template <typename T, int OP, int KIND>
+template <typename T, int OP, int KIND, bool LAST>
 __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
-  const MatInfo& M = P.mats[it.mat];
+  // Matrix record fields read once into registers: re-reading them after a
+  // global store would force a reload (the compiler cannot rule out aliasing).
+  struct {
+    int32_t m, n, mp, np, tall, vec_ok;
+    int64_t ld, a_off, b_off, xl_off, xo_cur, xo_nxt;
+    void* out;
+  } M;
+  {
+    const MatInfo& R = P.mats[it.mat];
+    M.m = R.m; M.n = R.n; M.mp = R.mp; M.np = R.np; M.tall = R.tall; M.vec_ok = R.vec_ok;
+    M.ld = R.ld; M.a_off = R.a_off; M.b_off = R.b_off; M.xl_off = R.xl_off;
+    M.xo_cur = xo_sel(R, P.cur); M.xo_nxt = xo_sel(R, P.cur ^ 1); M.out = R.out;
+  }
   constexpr bool KN = KIND == UPDATE;
 
   // LDS: operand stages (PIPE 1: one, PIPE 2: two); reused by the epilogue.
@@ -904,7 +945,7 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
   const char* opB;
   int64_t lda, ldb, K;
   if (KIND == GRAM) {
-    const char* X = P.ws + xo_sel(M, P.cur);
+    const char* X = P.ws + M.xo_cur;
     lda = ldb = int64_t(M.np) * 2;
     opA = X + int64_t(TI) * TM * lda;
     opB = X + int64_t(TJ) * TN * ldb;
@@ -919,7 +960,7 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
     lda = int64_t(M.mp) * 2;
     ldb = int64_t(M.np) * 2;
     opA = P.ws + M.b_off + int64_t(TI) * TM * lda;
-    opB = P.ws + xo_sel(M, P.cur) + int64_t(TJ) * TN * 2;
+    opB = P.ws + M.xo_cur + int64_t(TJ) * TN * 2;
     K = M.mp;
   }
 
@@ -1088,6 +1129,15 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
         *reinterpret_cast<f32x4_t*>(stg + l32 * PITCH + 32 * j + 8 * g + 4 * lh) =
             f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
   };
+  // staging of a run-time row group (one small copy of the stores per group)
+  auto stage_acc_rt = [&](int i) {
+    switch (i) {
+      case 0: stage_acc(std::integral_constant<int, 0>{}); break;
+      case 1: stage_acc(std::integral_constant<int, 1>{}); break;
+      case 2: stage_acc(std::integral_constant<int, 2>{}); break;
+      default: stage_acc(std::integral_constant<int, 3>{}); break;
+    }
+  };
   // direct access q (0..7): row 4 q + lane / 16 of the group, columns 4 (lane % 16)..+3
   auto drow = [&](int q) { return 4 * q + (lane >> 4); };
   const int dcol = 4 * (lane & 15);
@@ -1100,7 +1150,7 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
     const char* Am = P.ws + M.a_off;
     const int64_t ld = M.mp;
     const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
-auto round = [&](auto ic) {
+    auto round = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       stage_acc(ic);
       __syncthreads();
@@ -1117,10 +1167,17 @@ auto round = [&](auto ic) {
         const int m = m0 + drow(q), n = nb + dcol;
         f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
         if (KIND == POLY) {
-          const float a4[4] = {Op<OP>::load16(bias[q].x & 0xffffu), Op<OP>::load16(bias[q].x >> 16),
-                               Op<OP>::load16(bias[q].y & 0xffffu), Op<OP>::load16(bias[q].y >> 16)};
+          const u32x2 bq = bias[q];
+          const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
+                               Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = __fmaf_rn(P.c, v[r], P.b * a4[r]);
+          if constexpr (OP == OP_F16) {
+            // fp16 operands: B' = a I + b A + c A A, so the update is B' X
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
+          }
           *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = v;
         }
         if (strict || m <= n) {
@@ -1155,11 +1212,110 @@ auto round = [&](auto ic) {
     round(std::integral_constant<int, 1>{});
     round(std::integral_constant<int, 2>{});
     round(std::integral_constant<int, 3>{});
+  } else if constexpr (OP == OP_F16) {
+    // X' = B' hi + a 2^-11 lo  (B' = a I + B carries the a X term of the high
+    // part). lo lives in accumulator order, so no staging is needed.
+    const int64_t ldx = M.np;
+    uint16_t* lo = reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
+                   (((int64_t(TI) * (M.np >> 7) + TJ) * 4 + wave) * 32) * 256 + lane * 4;
+    char* xn = P.ws + M.xo_nxt;
+    const float a2 = P.a * (1.f / 2048.f);
+    auto round = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      u32x2 lv[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          lv[j][g] = *reinterpret_cast<const u32x2*>(lo + ((i * 2 + j) * 4 + g) * 256);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lw[4] = {lv[j][g].x & 0xffffu, lv[j][g].x >> 16, lv[j][g].y & 0xffffu,
+                                  lv[j][g].y >> 16};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][4 * g + r] = __fmaf_rn(a2, Op<OP>::load16(lw[r]), acc[i][j][4 * g + r]);
+          if constexpr (!LAST) {
+            const int m = mb + 32 * i + l32, n0 = nb + 32 * j + 8 * g + 4 * lh;
+            uint32_t nh[4], nl[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Op<OP>::split(acc[i][j][4 * g + r], nh[r], nl[r]);
+            *reinterpret_cast<uint2*>(xn + (int64_t(m) * ldx + n0) * 2) =
+                make_uint2(nh[0] | (nh[1] << 16), nh[2] | (nh[3] << 16));
+            *reinterpret_cast<uint2*>(lo + ((i * 2 + j) * 4 + g) * 256) =
+                make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
+          }
+        }
+    };
+    round(std::integral_constant<int, 0>{});
+    round(std::integral_constant<int, 1>{});
+    round(std::integral_constant<int, 2>{});
+    round(std::integral_constant<int, 3>{});
+    if constexpr (LAST) {
+      // `out` in the caller's layout: stage X' through LDS
+      T* o = static_cast<T*>(M.out);
+      auto out_round = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        stage_acc(ic);
+        __syncthreads();
+        const int m0 = mb + 32 * i;
+        if (!M.tall) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int m = m0 + drow(q), n = nb + dcol;
+            if (m >= M.m) continue;
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
+            const int64_t co = int64_t(m) * M.ld + n;
+            if (M.vec_ok && n + 3 < M.n) {
+              if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<uint2*>(o + co) = pack4(x[0], x[1], x[2], x[3], false);
+              else
+                *reinterpret_cast<f32x4_t*>(o + co) = x;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < M.n) Elem<T>::store(o, co + r, x[r]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cc = tcol(q), rr = trow(q);
+            const int n = nb + cc, m = m0 + rr;
+            if (n >= M.n) continue;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
+            const int64_t co = int64_t(n) * M.ld + m;
+            if (M.vec_ok && m + 7 < M.m) {
+              if constexpr (sizeof(T) == 2) {
+                const uint2 l4 = pack4(v[0], v[1], v[2], v[3], false), h4 = pack4(v[4], v[5], v[6], v[7], false);
+                *reinterpret_cast<uint4*>(o + co) = make_uint4(l4.x, l4.y, h4.x, h4.y);
+              } else {
+                *reinterpret_cast<f32x4_t*>(o + co) = f32x4_t{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4_t*>(o + co + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (m + e < M.m) Elem<T>::store(o, co + e, v[e]);
+            }
+          }
+        }
+        __syncthreads();
+      };
+      out_round(std::integral_constant<int, 0>{});
+      out_round(std::integral_constant<int, 1>{});
+      out_round(std::integral_constant<int, 2>{});
+      out_round(std::integral_constant<int, 3>{});
+    }
   } else {
     const int64_t ldx = M.np;
-    const char* xh = P.ws + xo_sel(M, P.cur);      // hi part of X (operand)
+    const char* xh = P.ws + M.xo_cur;      // hi part of X (operand)
     char* xl = P.ws + M.xl_off;                      // lo part, updated in place
-    char* xn = P.ws + xo_sel(M, P.cur ^ 1);        // next hi part
+    char* xn = P.ws + M.xo_nxt;        // next hi part
     T* o = static_cast<T*>(M.out);
 auto round = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -1185,7 +1341,7 @@ auto round = [&](auto ic) {
         const uint32_t lw[4] = {lv[q].x & 0xffffu, lv[q].x >> 16, lv[q].y & 0xffffu, lv[q].y >> 16};
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), x[r]);
-        if (!P.last) {
+        if constexpr (!LAST) {
           uint32_t nh[4], nl[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) Op<OP>::split(x[r], nh[r], nl[r]);
@@ -1211,7 +1367,7 @@ auto round = [&](auto ic) {
         }
       }
       }
-      if (P.last && M.tall) {
+      if (LAST && M.tall) {
         __syncthreads();
         // `out` is the transpose: out rows n, columns m..m+7
 #pragma unroll
@@ -1258,15 +1414,16 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
     case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;
     case MUON_K_GRAM:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, GRAM>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM, false>), g, b, 0, s, a);
       break;
     case MUON_K_POLY:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, POLY>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((gemm16_kernel<T, OP, POLY>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, POLY, false>), g, b, 0, s, a);
       break;
     case MUON_K_UPDATE:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, UPDATE>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE>), g, b, 0, s, a);
+      else if (a.last) hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, true>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, false>), g, b, 0, s, a);
       break;
     default: return hipErrorInvalidValue;
   }
