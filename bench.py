@@ -1,7 +1,7 @@
 """Throughput of the Muon update on one MI355X, GPT-2-124M hidden-matrix set.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                [--no-cpu-baseline] [--profile-steps N]
+                [--no-cpu-baseline] [--cpu-budget SECONDS] [--calibrate-copy]
 
 A step is one muon_plan_step over all matrices of the workload (momentum,
 normalisation and k Newton-Schulz steps), inputs resident in HBM. `value` is
@@ -9,7 +9,9 @@ algorithmic TFLOP/s of the whole step; `roofline` describes the kernel with
 the largest share of the step's time, timed with HIP events recorded around
 each launch on the step's stream in a second pass of the same length; the
 CPU baseline times the float64 oracle on a bounded sample of the same
-matrices. Prints one JSON line.
+matrices. `roofline.traffic` is the dominant kernel's HBM bytes per launch
+from the committed rocprofv3 counter summary (null if that summary was taken
+on a different kernel source). Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -42,17 +44,39 @@ def kernel_work(shapes, steps):
     return {
         # momentum: read G and buf, write buf (bf16)  -> 6 B/elem
         "momentum": (6.0 * elems, "B"),
-        # normalise: read G and buf (4 B), write fp32 master + bf16 operand (6 B)
-        "normalize": (10.0 * elems, "B"),
+        # normalise: read G and buf (4 B), write X's 16-bit high and low parts (4 B)
+        "normalize": (8.0 * elems, "B"),
         "gram": (float(gram), "flop"),
         "poly": (float(poly), "flop"),
         "update": (float(upd), "flop"),
     }
 
 
-def cpu_baseline(wl, budget_s: float = 15.0):
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or
+    None when it is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    src = os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", "kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    key = "update_step_average" if kernel == "update" else kernel
+    ent = rec.get("per_launch", {}).get(key)
+    return None if ent is None else ent["traffic_bytes"]
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
     """Float64 oracle on the host cores over whole layers of the workload
-    (one layer = 4 square + 1 wide + 1 tall matrix) until ~budget_s."""
+    (one layer = 4 square + 1 wide + 1 tall matrix), cycling through the
+    layers until at least budget_s of oracle time has accumulated."""
     import oracle
     from threadpoolctl import threadpool_info
     from workloads import make_gradients, to_f64
@@ -64,8 +88,8 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     grads = make_gradients(wl, step=0, device="cpu")
     done, flops, t_total = 0, 0, 0.0
     a, b, c = (float(np.float32(x)) for x in wl.coeffs)
-    while done < nlayers and t_total < budget_s:
-        idx = layer_idx(done)
+    while t_total < budget_s:
+        idx = layer_idx(done % nlayers)
         g64 = [to_f64(grads[i]) for i in idx]
         t0 = time.perf_counter()
         for g in g64:
@@ -79,8 +103,9 @@ def cpu_baseline(wl, budget_s: float = 15.0):
                    if p.get("user_api") == "blas"] or [1])
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {nlayers} {'layers (6 matrices each)' if L else 'matrices'} "
-                      f"of {wl.name}, float64 NumPy, {t_total:.1f} s",
+            "sample": f"{done} {'layers (6 matrices each)' if L else 'matrices'} "
+                      f"({done / nlayers:.2f} passes over the {wl.n_matrices} matrices) of "
+                      f"{wl.name}, float64 NumPy, {t_total:.1f} s",
             "seconds": t_total, "host_cpus": os.cpu_count()}
 
 
@@ -91,8 +116,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2_124m_matrix_set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 512 MiB three times (the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 3}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} "
@@ -162,7 +199,7 @@ def main():
         roof = {"bound": "hbm", "achieved": d_amount / (d_avg * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name, dom)
     roof["kernel"] = dom
     roof["avg_launch_us"] = d_avg * 1e3
 
