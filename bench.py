@@ -31,25 +31,51 @@ PEAK = {"bf16": 2500.0, "fp32": 157.3}       # dense MFMA TFLOP/s, MI355X
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_work(shapes, steps):
-    """Algorithmic work per launch of each kernel: (amount, unit)."""
-    gram = poly = upd = 0
-    elems = 0
+def kernel_work(shapes, steps, dtype):
+    """Algorithmic work per launch of each kernel: {kernel: (flops, bytes)}.
+
+    Bytes count each operand read once and each result written once, in the
+    library's formats: bf16 sets keep X as two 16-bit halves (high part = the
+    matrix-core operand, low part = the residual) and A, B as 16-bit; fp32
+    sets keep everything in fp32. The update's bytes are the average over the
+    `steps` launches of a step (the last one writes `out` instead of X's
+    halves)."""
+    es = 2 if dtype == "bf16" else 4
+    xb = 4                                  # X per element: hi + lo halves, or fp32
+    xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
+    w = {k: [0.0, 0.0] for k in ("momentum", "normalize", "gram", "poly", "update")}
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
-        gram += m * (m + 1) * n
-        poly += m * m * (m + 1)
-        upd += 2 * m * m * n
-        elems += r * c
-    return {
-        # momentum: read G and buf, write buf (bf16)  -> 6 B/elem
-        "momentum": (6.0 * elems, "B"),
-        # normalise: read G and buf (4 B), write X's 16-bit high and low parts (4 B)
-        "normalize": (8.0 * elems, "B"),
-        "gram": (float(gram), "flop"),
-        "poly": (float(poly), "flop"),
-        "update": (float(upd), "flop"),
-    }
+        mn, mm = float(m * n), float(m * m)
+        w["momentum"][1] += 3 * es * mn          # read G, buf; write buf'
+        w["normalize"][1] += 2 * es * mn + xb * mn   # read G, buf'; write X
+        w["gram"][0] += m * (m + 1) * n
+        w["gram"][1] += xop * mn + es * mm       # read X operand; write A
+        w["poly"][0] += m * m * (m + 1)
+        w["poly"][1] += 2 * es * mm              # read A; write B
+        w["update"][0] += 2 * m * m * n
+        reg = es * mm + xb * mn + xb * mn        # read B, X; write X
+        last = es * mm + xb * mn + es * mn       # read B, X; write out
+        w["update"][1] += (reg * (steps - 1) + last) / steps if steps else 0.0
+    return {k: (v[0], v[1]) for k, v in w.items()}
+
+
+def roofline_of(flops, nbytes, avg_s, dtype):
+    """Both roofs for one kernel; the binding one (the larger lower bound on
+    the launch time) is the headline, the other is kept under `other`."""
+    mf = {"bound": "mfma", "achieved": flops / avg_s / 1e12, "peak": PEAK[dtype],
+          "unit": "TFLOP/s"}
+    hb = {"bound": "hbm", "achieved": nbytes / avg_s / 1e9, "peak": HBM_PEAK_GBS,
+          "unit": "GB/s"}
+    for r in (mf, hb):
+        r["frac"] = r["achieved"] / r["peak"]
+    t_mfma = flops / (PEAK[dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    head, other = (hb, mf) if t_hbm >= t_mfma else (mf, hb)
+    if flops > 0:
+        head["other"] = other
+    head["bound_us"] = {"hbm": t_hbm * 1e6, "mfma": t_mfma * 1e6}
+    return head
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -177,28 +203,22 @@ def main():
 
     falg = wl.falg_flops()
     value = falg / (ms * 1e-3) / 1e12
-    work = kernel_work(wl.shapes, wl.steps)
+    work = kernel_work(wl.shapes, wl.steps, wl.dtype)
     per_kernel = {}
     for name, (tot_ms, n) in kt.items():
         if n == 0:
             continue
         avg = tot_ms / n
-        amount, unit = work[name]
-        rate = amount / (avg * 1e-3)
-        per_kernel[name] = {"launches_per_step": n / args.steps, "avg_us": avg * 1e3,
-                            "ms_per_step": tot_ms / args.steps,
-                            ("TFLOP/s" if unit == "flop" else "GB/s"):
-                                rate / (1e12 if unit == "flop" else 1e9)}
+        flops, nbytes = work[name]
+        ent = {"launches_per_step": n / args.steps, "avg_us": avg * 1e3,
+               "ms_per_step": tot_ms / args.steps,
+               "GB/s": nbytes / (avg * 1e-3) / 1e9}
+        if flops:
+            ent["TFLOP/s"] = flops / (avg * 1e-3) / 1e12
+        per_kernel[name] = ent
     dom = max(kt, key=lambda k: kt[k][0])
-    d_amount, d_unit = work[dom]
     d_avg = kt[dom][0] / kt[dom][1]
-    if d_unit == "flop":
-        roof = {"bound": "mfma", "achieved": d_amount / (d_avg * 1e-3) / 1e12,
-                "peak": PEAK[wl.dtype], "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": d_amount / (d_avg * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = roofline_of(*work[dom], d_avg * 1e-3, wl.dtype)
     roof["traffic"] = measured_traffic(wl.name, dom)
     roof["kernel"] = dom
     roof["avg_launch_us"] = d_avg * 1e3
