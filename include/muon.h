@@ -168,8 +168,10 @@ typedef enum {
  * four int32 per item {matrix, a, b, c} (momentum: {matrix, first row,
  * row count, partial slot}; normalise: {matrix, tile row, tile col, 0} of
  * 64 x 64 tiles of the rows<=cols orientation; gram/poly: {matrix, tile
- * row, tile col, 0} upper-triangle 128 x 128 tiles; update: {matrix, tile
- * row, tile col, 0}), in launch order with empty slots as {-1,-1,-1,-1}.
+ * row, tile col, 0} of the tiles on or above the diagonal; update: {matrix,
+ * tile row, tile col, 0}; matrix-core tiles are 256 x 256 for bf16 sets and
+ * 128 x 128 for fp32 sets), in launch order with empty slots as
+ * {-1,-1,-1,-1}.
  * Writes min(cap, count) items to `items` (may be NULL when cap == 0) and
  * the total to *count. No device calls. */
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,
@@ -187,7 +189,8 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
 /* Workspace layout of matrix `idx` of a plan (byte offsets from the
  * workspace base; -1 where a buffer does not exist). All buffers use the
  * rows<=cols orientation, zero-padded to mp x np (X) or mp x mp (A, B),
- * row-major. bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
+ * row-major, with mp and np the tile multiples (256 for bf16 sets, 128 for
+ * fp32 sets). bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
  * matrix-core operand, ping-pong between steps) and x_lo the low part in
  * the same format (X = hi + lo * 2^-11 for fp16 operands, hi + lo for bf16
  * operands); gram (A) and poly are 16-bit. With fp16 operands poly holds

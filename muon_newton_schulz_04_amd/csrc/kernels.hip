@@ -222,17 +222,19 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
 // straight to `out` in the caller's layout.
 
 // fp16 operand sets keep the low part of X in the update kernel's
-// accumulator order: per 256 x 128 tile, per wave, per accumulator group
-// (i, j, g) a contiguous 64-lane x 4-element block. Lane loads and stores of
-// the update epilogue are then contiguous across the wave. Element index of
-// X(m, n) in that layout (np = padded row length):
+// accumulator order: per 256 x TN tile, per wave (2 x TN/64 waves of
+// 128 x 64), per accumulator group (i, j, g) a contiguous 64-lane x
+// 4-element block. Lane loads and stores of the update epilogue are then
+// contiguous across the wave. Element index of X(m, n) in that layout
+// (np = padded row length):
 __device__ __forceinline__ int64_t lo_index(int m, int n, int np) {
-  const int tile = (m >> 8) * (np >> 7) + (n >> 7);
-  const int mm = m & 255, nn = n & 127;
-  const int wave = (mm >> 7) * 2 + (nn >> 6);
+  constexpr int TN = kTileN16, WN = TN / 64;
+  const int tile = (m >> 8) * (np / TN) + n / TN;
+  const int mm = m & 255, nn = n % TN;
+  const int wave = (mm >> 7) * WN + (nn >> 6);
   const int lane = (mm & 31) + 32 * ((nn >> 2) & 1);
   const int grp = (((mm >> 5) & 3) * 2 + ((nn >> 5) & 1)) * 4 + ((nn >> 3) & 3);
-  return (((int64_t(tile) * 4 + wave) * 32 + grp) * 64 + lane) * 4 + (nn & 3);
+  return (((int64_t(tile) * 2 * WN + wave) * 32 + grp) * 64 + lane) * 4 + (nn & 3);
 }
 
 template <typename T, int OP>
@@ -630,98 +632,115 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
 
 // ------------------------------------------- 16-bit operand engine (bf16 sets)
 //
-// Output tile 256 (rows) x 128 (cols), k-slab 64 elements (128 bytes). Four
-// waves in 2 x 2, each owning 128 x 64 = 4 x 2 accumulators of
-// v_mfma_f32_32x32x16_{f16,bf16}. The MFMA is fed (column operand, row
-// operand), so lane l holds, for accumulator (i, j) and register e,
+// Output tile 256 x 256, 512 threads: eight waves in 2 (rows) x 4 (cols),
+// each owning 128 x 64 = 4 x 2 accumulators of v_mfma_f32_32x32x16_{f16,bf16}.
+// The MFMA is fed (column operand, row operand), so lane l holds, for
+// accumulator (i, j) and register e,
 //   C[m][n], m = row0 + 32 i + l % 32, n = col0 + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4,
 // i.e. runs of 4 consecutive output columns: vector epilogue loads/stores.
-//   Row operand (k contiguous in memory): LDS [row][k], 128-byte rows.
-//   Column operand, k contiguous (Gram, A A):  LDS [col][k], 128-byte rows.
-//   Column operand, k along memory rows (X in B X): LDS [k][col], 256-byte
-//     rows, read with ds_read_b64_tr_b16: in each 16-lane group, lane s
-//     addresses row k0 + s/4, columns c0 + 4(s%4)..+3, and lane i receives
-//     column c0 + i of rows k0..k0+3.
-// Two LDS stages and two register sets; the loop is unrolled by two so
-// stage and register-set choices are constants: multiply stage 0, write the
-// next slab (registers) to stage 1, barrier, load the slab three ahead,
-// multiply stage 1, and so on.
-
-#ifndef MUON_GEMM_PIPE
-#define MUON_GEMM_PIPE 1
-#endif
+//
+// k advances in stages of 32. Operands go from global memory straight into
+// a ring of NS LDS stages (global_load_lds_dwordx4: lane i of a 1 KB piece
+// writes base + 16 i, so the bank swizzle is applied by choosing which
+// global 16-byte chunk lane i fetches). While stage g is multiplied, stages
+// g+1 .. g+NS-2 are in flight and stage g+NS-1 is issued into the slot that
+// stage g-1 freed; one barrier per stage.
+//   Row operand (k contiguous in memory): [row][k], 64-byte rows.
+//   Column operand, k contiguous (Gram, A A): [col][k], 64-byte rows.
+//   Column operand, k along memory rows (X in B X): [k][col], 512-byte rows,
+//     read with ds_read_b64_tr_b16: in each 16-lane group, lane s addresses
+//     row k0 + s/4, columns c0 + 4(s%4)..+3, and lane i receives column
+//     c0 + i of rows k0..k0+3.
 
 namespace e16 {
 
-constexpr int TM = 256, TN = 128;
-// PIPE 2: two LDS stages + two register sets, one workgroup per CU.
-// PIPE 1: one LDS stage + one register set, two workgroups per CU.
-// PIPE 3: ring of NST direct-to-LDS stages of 32-k slabs (NST <= 3: two
-//         workgroups per CU; larger: one).
-constexpr int PIPE = MUON_GEMM_PIPE;
-#ifndef MUON_GEMM_NST
-#define MUON_GEMM_NST 6
-#endif
-constexpr int NST = MUON_GEMM_NST;
-constexpr int WG_PER_CU = (PIPE == 1 || (PIPE == 3 && NST <= 3)) ? 2 : 1;
-// PIPE 4: PIPE 2's buffers with one barrier per slab: while slab t is
-//         multiplied, slab t+1 goes from registers to the other LDS stage and
-//         slab t+3 is loaded into the registers just freed.
+constexpr int TM = 256;                // output tile rows
+constexpr int TN = kTileN16;           // output tile columns (128 or 256)
+constexpr int WN = TN / 64;            // waves per tile row (2 rows of waves)
+constexpr int NWAVE = 2 * WN;
+constexpr int NTHR = 64 * NWAVE;
+constexpr int KS = 32;                 // k per stage
+// Ring depth: 256 x 256 tiles run one workgroup per CU with four 32 KB
+// stages; 256 x 128 tiles run two per CU with three 24 KB stages each.
+constexpr int NS = TN == 256 ? 4 : 3;
+constexpr int WG_PER_CU = TN == 256 ? 1 : 2;
+constexpr int HALF_A = TM * KS * 2;    // row operand of one stage: 16 KB
+constexpr int HALF_B = TN * KS * 2;    // column operand of one stage
+constexpr int STAGE = HALF_A + HALF_B;
+constexpr int LDS_BYTES = NS * STAGE;
+constexpr int KROW = TN * 2;           // bytes of one k-row of the [k][col] layout
+static_assert(TN == 128 || TN == 256, "tile width");
+static_assert(NS >= 3 && NS <= 8, "a stage in use, one in flight, one being refilled; K >= 8 stages");
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ int off_rows(int row, int chunk) {   // 128-byte rows
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
-// [k][col] tile, 256-byte rows; the XOR spreads the rows touched by one
-// transposed read over distinct 32-byte bank groups (2 passes, the minimum)
-__device__ __forceinline__ int off_kn(int k, int chunk) {
-  return k * 256 + ((chunk ^ (((k ^ ((k >> 3) << 2)) & 7) << 1)) << 4);
-}
-
-// Operand slabs are read with buffer loads: a scalar resource descriptor
-// per slab (so offsets stay small for any matrix size) and one 32-bit
-// per-lane offset, instead of a 64-bit address per load.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const char* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
-}
-
-template <int R>  // R rows x 128 bytes at base + row*ldb + k0b
-__device__ __forceinline__ void load_rows(u32x4 (&r)[R / 32], const char* base, int64_t ldb,
-                                          int64_t k0b) {
-  const int t = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rs = slab_rsrc(base + k0b);
-  const int32_t vo = (t >> 3) * int32_t(ldb) + (t & 7) * 16;
-#pragma unroll
-  for (int q = 0; q < R / 32; ++q)
-    r[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 32 * q * int32_t(ldb), 0);
-}
-template <int R>
-__device__ __forceinline__ void store_rows(char* lds, const u32x4 (&r)[R / 32]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < R / 32; ++q)
-    *reinterpret_cast<u32x4*>(lds + off_rows((t >> 3) + 32 * q, t & 7)) = r[q];
-}
-// 64 k-rows x 256 bytes at base + (k0 + k)*ldb
-__device__ __forceinline__ void load_kn(u32x4 (&r)[4], const char* base, int64_t ldb, int64_t k0) {
-  const int t = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rs = slab_rsrc(base + k0 * ldb);
-  const int32_t vo = (t >> 4) * int32_t(ldb) + (t & 15) * 16;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    r[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 16 * q * int32_t(ldb), 0);
-}
-__device__ __forceinline__ void store_kn(char* lds, const u32x4 (&r)[4]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<u32x4*>(lds + off_kn((t >> 4) + 16 * q, t & 15)) = r[q];
-}
-
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// LDS of gfx950 serves 256 bytes (64 banks of 4 bytes) per clock; a
+// ds_read_b128 is served 16 lanes at a time.
+// [row][k] layout: 16-byte chunk c (8 k) of row r. A fragment read puts 16
+// consecutive rows (64 bytes apart, same chunk) in one phase: rows r, r+4,
+// r+8, r+12 share a 64-byte bank quarter, and the XOR gives them four
+// distinct chunks (measured: conflict-free; XOR with (r >> 1) & 3 alone
+// leaves 2-way conflicts).
+__device__ __forceinline__ int off_r(int r, int c) {
+  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 2)) & 3)) << 4);
+}
+// [k][col] layout: chunk c (8 columns) of k-row k (KROW-byte rows, a
+// multiple of the 256-byte bank row). The XOR moves the four k-rows of one
+// transposed read to four different 64-byte quarters of the bank row
+// (measured: as fast as a contiguous transposed read).
+__device__ __forceinline__ int off_k(int k, int c) { return k * KROW + ((c ^ ((k & 3) << 2)) << 4); }
+
+// One 1 KB piece of LDS DMA: lane i copies the 16 bytes at `src` to LDS
+// address lds_base + 16 i (lds_base wave-uniform, taken through M0).
+// Written as asm on purpose: the instruction has no register result, and
+// hiding it from the compiler keeps it from guarding every later LDS read
+// with a wait for all DMA in flight (it cannot tell the ring slots apart,
+// and it cannot see the alias scopes of the transposing LDS reads). The
+// ring's own waits (s_waitcnt vmcnt + s_barrier) order the accesses.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_base), "v"(src)
+      : "memory", "m0");
+}
+
+// Issues this wave's share of the DMA of one stage (pieces of 1 KB: 16 of
+// the row operand, TN/16 of the column operand): rows of the row operand at
+// opA + row * lda (bytes), k0 .. k0+31; the column operand either the same
+// way from opB, or k-rows k0 .. k0+31 of TN columns at opB + k * ldb.
+constexpr int DMA_PER_STAGE = (16 + TN / 16) / NWAVE;  // pieces per wave per stage
+template <bool KN>
+__device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
+                                          int64_t ldb, int64_t k0) {
+  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + (w << 10));
+#pragma unroll
+  for (int q = 0; q < 16 / NWAVE; ++q) {
+    const int I = w + NWAVE * q;  // piece of the row operand
+    const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    dma16(opA + row * lda + k0 * 2 + g * 16, base + q * NWAVE * 1024);
+  }
+#pragma unroll
+  for (int q = 0; q < TN / 16 / NWAVE; ++q) {
+    const int I = w + NWAVE * q;  // piece of the column operand
+    if constexpr (!KN) {
+      const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+      dma16(opB + row * ldb + k0 * 2 + g * 16, base + HALF_A + q * NWAVE * 1024);
+    } else {
+      constexpr int RPP = 1024 / KROW;  // k-rows per piece
+      const int kr = RPP * I + i / (64 / RPP), g = (i % (64 / RPP)) ^ ((kr & 3) << 2);
+      dma16(opB + (k0 + kr) * ldb + g * 16, base + HALF_A + q * NWAVE * 1024);
+    }
+  }
+}
 
 template <int OP>
 __device__ __forceinline__ f32x16_t mfma(const u32x4& colop, const u32x4& rowop, f32x16_t c) {
@@ -733,42 +752,61 @@ __device__ __forceinline__ f32x16_t mfma(const u32x4& colop, const u32x4& rowop,
                                                    __builtin_bit_cast(bf16x8_t, rowop), c, 0, 0, 0);
 }
 
-// One 64-k slab of this wave's 128 x 64 block: 4 k-steps of 16.
-template <int OP, bool KN>
-__device__ __forceinline__ void mma_slab(f32x16_t (&acc)[4][2], const char* sA, const char* sB,
-                                         int wm, int wn) {
+// Operand fragments of one k-step (16 k) of this wave's 128 x 64 block.
+struct Frag {
+  u32x4 a[4];  // row operand: rows wm*128 + 32 i + l%32, 8 k per lane half
+  u32x4 b[2];  // column operand: columns wn*64 + 32 j + l%32
+};
+
+// Reads the fragments of k-step ks (0/1) of the stage at `st`; the reads
+// stay in flight until the MFMAs that use them.
+template <bool KN>
+__device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int wm, int wn) {
+  const char* sA = st;
+  const char* sB = st + HALF_A;
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+  const int ch = ks * 2 + lh;  // 16-byte k chunk of this lane half
+  if constexpr (KN) {
+    const int s = lane & 15, h = lane >> 4;  // 16-lane group h
+    const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int ch = ks * 2 + lh;  // 16-byte k chunk of this lane half
-    u32x4 bf[2], af[4];
-    if constexpr (!KN) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows(wn * 64 + j * 32 + l32, ch));
-    } else {
-      const int s = lane & 15, h = lane >> 4;        // 16-lane group h
-      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
-        const int chunk = col >> 3, byte = (col & 7) * 2;
-        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
+      const int chunk = col >> 3, byte = (col & 7) * 2;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(sB + off_k(krow, chunk) + byte));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(sB + off_k(krow + 4, chunk) + byte));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      f.b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
     }
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows(wm * 128 + i * 32 + l32, ch));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
+    for (int j = 0; j < 2; ++j)
+      f.b[j] = *reinterpret_cast<const u32x4*>(sB + off_r(wn * 64 + j * 32 + l32, ch));
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const u32x4*>(sA + off_r(wm * 128 + i * 32 + l32, ch));
+}
+
+// Scheduling hint for a region holding one k-step of MFMAs (8) and the LDS
+// reads of the next k-step (8): alternate them, so the reads are spread over
+// the multiplies instead of bunching before or after them.
+__device__ __forceinline__ void interleave_mma_reads() {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ void frag_mma(f32x16_t (&acc)[4][2], const Frag& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(f.b[j], f.a[i], acc[i][j]);
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool f16) {
@@ -783,135 +821,16 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
   return r;
 }
 
-
-
-// One 64-k slab like mma_slab, with `hook(ks)` called before each of the 4
-// k-steps; used to spread the next slab's LDS stores and global loads over
-// the multiplies (sched_barrier keeps each k-step's group together).
-template <int OP, bool KN, class Hook>
-__device__ __forceinline__ void mma_slab_hooked(f32x16_t (&acc)[4][2], const char* sA,
-                                                const char* sB, int wm, int wn, Hook&& hook) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int ch = ks * 2 + lh;
-    u32x4 bf[2], af[4];
-    if constexpr (!KN) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows(wn * 64 + j * 32 + l32, ch));
-    } else {
-      const int s = lane & 15, h = lane >> 4;
-      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
-        const int chunk = col >> 3, byte = (col & 7) * 2;
-        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows(wm * 128 + i * 32 + l32, ch));
-    hook(ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// ---- PIPE 3: direct-to-LDS ring of 32-k slabs (64-byte rows for k-contiguous
-// operands, 256-byte rows for the [k][col] operand). Each
-// global_load_lds_dwordx4 fills 1 KB of LDS: lane i writes base + 16 i, so
-// the XOR swizzle is applied by choosing which global chunk lane i fetches.
-__device__ __forceinline__ int off_rows64(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Issues the DMA of one 32-k slab: row operand R rows (k contiguous), column
-// operand either TN rows (k contiguous) or 32 k-rows x TN columns.
-template <bool KN>
-__device__ __forceinline__ void dma_slab(char* sA, char* sB, const char* opA, int64_t lda,
-                                         const char* opB, int64_t ldb, int64_t k0) {
-  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {  // A: 16 instructions of 16 rows x 64 B
-    const int I = w + 4 * q, row = 16 * I + (i >> 2), lch = (i & 3) ^ ((row >> 2) & 3);
-    __builtin_amdgcn_global_load_lds(opA + row * lda + k0 * 2 + lch * 16,
-                                     (lds_void_t*)(sA + I * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int I = w + 4 * q;
-    if constexpr (!KN) {  // 8 instructions of 16 rows x 64 B
-      const int row = 16 * I + (i >> 2), lch = (i & 3) ^ ((row >> 2) & 3);
-      __builtin_amdgcn_global_load_lds(opB + row * ldb + k0 * 2 + lch * 16,
-                                       (lds_void_t*)(sB + I * 1024), 16, 0, 0);
-    } else {              // 8 instructions of 4 k-rows x 256 B
-      const int kr = 4 * I + (i >> 4);
-      const int lch = (i & 15) ^ ((((kr ^ ((kr >> 3) << 2)) & 7)) << 1);
-      __builtin_amdgcn_global_load_lds(opB + (k0 + kr) * ldb + lch * 16,
-                                       (lds_void_t*)(sB + I * 1024), 16, 0, 0);
-    }
-  }
-}
-
-// One 32-k slab of this wave's 128 x 64 block (2 k-steps of 16).
-template <int OP, bool KN>
-__device__ __forceinline__ void mma_slab32(f32x16_t (&acc)[4][2], const char* sA, const char* sB,
-                                           int wm, int wn) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int ch = ks * 2 + lh;
-    u32x4 bf[2], af[4];
-    if constexpr (!KN) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(sB + off_rows64(wn * 64 + j * 32 + l32, ch));
-    } else {
-      const int s = lane & 15, h = lane >> 4;
-      const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
-        const int chunk = col >> 3, byte = (col & 7) * 2;
-        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow, chunk) + byte));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sB + off_kn(krow + 4, chunk) + byte));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        bf[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const u32x4*>(sA + off_rows64(wm * 128 + i * 32 + l32, ch));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(bf[j], af[i], acc[i][j]);
-  }
-}
-
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
 #define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 }  // namespace e16
 
-// bf16 sets. Item {mat, TI, TJ} of 256 x 128 tiles. GRAM/POLY: tiles that
-// reach the upper triangle (TJ >= 2 TI); each stored element (m <= n) is
-// mirrored to (n, m). UPDATE: X = a X + B X on all tiles.
+// bf16 sets. Item {mat, TI, TJ} of 256 x 256 tiles. GRAM/POLY: tiles on or
+// above the diagonal (TJ >= TI); each stored element (m <= n) is mirrored to
+// (n, m). UPDATE: X = a X + B X on all tiles.
 template <typename T, int OP, int KIND, bool LAST>
-__global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
+__global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
@@ -930,15 +849,7 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
   }
   constexpr bool KN = KIND == UPDATE;
 
-  // LDS: operand stages (PIPE 1: one, PIPE 2: two); reused by the epilogue.
-  constexpr int STAGE = (TM + TN) * 128;
-  constexpr int STAGE32 = (TM + TN) * 64;  // PIPE 3: 32-k slab
-  constexpr int LDS_BYTES = PIPE == 3 ? NST * STAGE32 : (PIPE == 1 ? 1 : 2) * STAGE;
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  char* const sA0 = lds;
-  char* const sB0 = lds + TM * 128;
-  char* const sA1 = lds + (PIPE == 1 ? 0 : STAGE);  // (PIPE 1/2/4)
-  char* const sB1 = sA1 + TM * 128;
 
   const int TI = it.a, TJ = it.b;
   const char* opA;
@@ -965,7 +876,7 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
   }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -974,432 +885,261 @@ __global__ __launch_bounds__(256, e16::WG_PER_CU) void gemm16_kernel(StepArgs P)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Two register sets hold the next two slabs, so each global load has two
-  // slabs of multiplies to land before its data is written to LDS.
-  u32x4 ra0[TM / 32], rb0[4], ra1[TM / 32], rb1[4];
-  auto load = [&](u32x4 (&ra)[TM / 32], u32x4 (&rb)[4], int64_t slab) {
-    const int64_t k0 = slab * 64;
-    load_rows<TM>(ra, opA, lda, k0 * 2);
-    if constexpr (KN) load_kn(rb, opB, ldb, k0);
-    else load_rows<TN>(rb, opB, ldb, k0 * 2);
-  };
-  auto store = [&](const u32x4 (&ra)[TM / 32], const u32x4 (&rb)[4], char* a, char* b) {
-    store_rows<TM>(a, ra);
-    if constexpr (KN) store_kn(b, rb);
-    else store_rows<TN>(b, rb);
-  };
-  // K is a multiple of 128: an even number (>= 2) of 64-element slabs.
-  // Loads past the last slab are clamped to it (valid, unused).
-  const int nslab = static_cast<int>(K >> 6);
-  if constexpr (PIPE == 4) {
-    // per-thread pieces of a slab: A rows in ra[0..7], B rows (or k-rows) in rb[0..3]
-    auto st_piece = [&](const u32x4 (&ra)[TM / 32], const u32x4 (&rb)[4], char* a, char* b, int q) {
-      const int t = threadIdx.x;
-      if (q < 8) {
-        *reinterpret_cast<u32x4*>(a + off_rows((t >> 3) + 32 * q, t & 7)) = ra[q];
-      } else {
-        const int r = q - 8;
-        if constexpr (KN) *reinterpret_cast<u32x4*>(b + off_kn((t >> 4) + 16 * r, t & 15)) = rb[r];
-        else *reinterpret_cast<u32x4*>(b + off_rows((t >> 3) + 32 * r, t & 7)) = rb[r];
-      }
-    };
-    auto ld_piece = [&](u32x4 (&ra)[TM / 32], u32x4 (&rb)[4], int64_t slab, int q) {
-      const int t = threadIdx.x;
-      const int64_t k0 = slab * 64;
-      if (q < 8) {
-        ra[q] = *reinterpret_cast<const u32x4*>(opA + int64_t((t >> 3) + 32 * q) * lda + k0 * 2 + (t & 7) * 16);
-      } else {
-        const int r = q - 8;
-        if constexpr (KN)
-          rb[r] = *reinterpret_cast<const u32x4*>(opB + (k0 + (t >> 4) + 16 * r) * ldb + (t & 15) * 16);
-        else
-          rb[r] = *reinterpret_cast<const u32x4*>(opB + int64_t((t >> 3) + 32 * r) * ldb + k0 * 2 + (t & 7) * 16);
-      }
-    };
-    load(ra0, rb0, 0);
-    store(ra0, rb0, sA0, sB0);
-    load(ra0, rb0, 1);
-    load(ra1, rb1, min(2, nslab - 1));
-    __syncthreads();
-    for (int t = 0; t < nslab - 2; t += 2) {
-      // slab t from stage 0; slab t+1 (ra0) -> stage 1; ra0 <- slab t+3
-      mma_slab_hooked<OP, KN>(acc, sA0, sB0, wm, wn, [&](int ks) {
+  // K is a multiple of 256 (at least 8 stages). Each stage is two k-steps;
+  // the fragments of the next k-step are read while the MFMAs of the current
+  // one run, and the ring barrier sits between the two k-steps of a stage:
+  //   mma(g, 0) | read (g, 1) | stage g+1 landed, barrier, DMA g+NS-1 into
+  //   the slot of g-1 | mma(g, 1) | read (g+1, 0)
+  // Every pass issues one stage, so the wait count is the same in every pass;
+  // past the end the DMA repeats the last stage (valid addresses, unused).
+  const int nst = static_cast<int>(K / KS);
 #pragma unroll
-        for (int q = 3 * ks; q < 3 * ks + 3; ++q) {
-          st_piece(ra0, rb0, sA1, sB1, q);
-          ld_piece(ra0, rb0, t + 3, q);
-        }
-      });
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // slab t+1 from stage 1; slab t+2 (ra1) -> stage 0; ra1 <- slab t+4
-      const int64_t s4 = min(t + 4, nslab - 1);
-      mma_slab_hooked<OP, KN>(acc, sA1, sB1, wm, wn, [&](int ks) {
-#pragma unroll
-        for (int q = 3 * ks; q < 3 * ks + 3; ++q) {
-          st_piece(ra1, rb1, sA0, sB0, q);
-          ld_piece(ra1, rb1, s4, q);
-        }
-      });
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    mma_slab_hooked<OP, KN>(acc, sA0, sB0, wm, wn, [&](int ks) {
-#pragma unroll
-      for (int q = 3 * ks; q < 3 * ks + 3; ++q) st_piece(ra0, rb0, sA1, sB1, q);
-    });
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
-  } else if constexpr (PIPE == 3) {
-    // ring of NST stages; slab t (32 k) lives in stage t % NST, NST-1 in flight
-    const int n32 = static_cast<int>(K >> 5);
-    auto stA = [&](int st) { return lds + st * STAGE32; };
-    auto stB = [&](int st) { return lds + st * STAGE32 + TM * 64; };
-#pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
-      dma_slab<KN>(stA(p), stB(p), opA, lda, opB, ldb, int64_t(min(p, n32 - 1)) * 32);
-    int st = 0;
-    for (int t = 0; t < n32; ++t) {
-      MUON_WAIT_VMCNT(6 * (NST - 2));  // this wave's loads of slab t are done
-      // Everyone's are, and slab t-1 is consumed. A bare s_barrier: the
-      // workgroup fence of __syncthreads would wait for all loads in flight;
-      // the memory clobber keeps the compiler from moving LDS accesses across.
-      asm volatile("s_barrier" ::: "memory");
-      const int stn = st == 0 ? NST - 1 : st - 1;  // stage of slab t+NST-1 (= t-1's)
-      dma_slab<KN>(stA(stn), stB(stn), opA, lda, opB, ldb,
-                   int64_t(min(t + NST - 1, n32 - 1)) * 32);  // past the end: a valid, unused slab
-      __builtin_amdgcn_sched_barrier(0);
-      mma_slab32<OP, KN>(acc, stA(st), stB(st), wm, wn);
-      st = st == NST - 1 ? 0 : st + 1;
-    }
-    MUON_WAIT_VMCNT(0);  // drain the trailing loads before the LDS is reused
-  } else if constexpr (PIPE == 1) {
-    load(ra0, rb0, 0);
-    for (int t = 0; t < nslab; ++t) {
-      __syncthreads();
-      store(ra0, rb0, sA0, sB0);
-      __syncthreads();
-      load(ra0, rb0, min(t + 1, nslab - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
-    }
-  } else {
-  load(ra0, rb0, 0);
-  store(ra0, rb0, sA0, sB0);
-  load(ra0, rb0, 1);
-  load(ra1, rb1, min(2, nslab - 1));
-  __syncthreads();
-  // sched_barrier(0) keeps the compiler from moving the loads past the
-  // multiplies that are meant to hide their latency.
-  for (int t = 0; t < nslab - 2; t += 2) {
-    mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
-    store(ra0, rb0, sA1, sB1);
-    __syncthreads();
-    load(ra0, rb0, t + 3);
+  for (int p = 0; p < NS - 1; ++p) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+  MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 2));  // stage 0 landed (this wave's pieces)
+  asm volatile("s_barrier" ::: "memory");
+  Frag f0, f1;
+  frag_load<KN>(f0, lds, 0, wm, wn);
+  int cur = 0;  // ring slot of stage g
+  for (int g = 0; g < nst; ++g) {
+    const int nxt = cur == NS - 1 ? 0 : cur + 1;  // slot of stage g+1
+    const int old = cur == 0 ? NS - 1 : cur - 1;  // slot of stage g-1 (unused for g = 0)
     __builtin_amdgcn_sched_barrier(0);
-    mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
-    store(ra1, rb1, sA0, sB0);
-    __syncthreads();
-    load(ra1, rb1, min(t + 4, nslab - 1));
+    frag_mma<OP>(acc, f0);
+    frag_load<KN>(f1, lds + cur * STAGE, 1, wm, wn);
+    interleave_mma_reads();
     __builtin_amdgcn_sched_barrier(0);
+    // This wave's pieces of stage g+1 have landed (stages up to g+NS-2 may
+    // still be in flight). A bare s_barrier: the workgroup fence of
+    // __syncthreads would also wait for those; the memory clobber keeps the
+    // compiler from moving LDS accesses across it.
+    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3));
+    asm volatile("s_barrier" ::: "memory");
+    // every wave has finished reading stage g-1: refill its slot
+    dma_stage<KN>(lds + old * STAGE, opA, lda, opB, ldb, int64_t(min(g + NS - 1, nst - 1)) * KS);
+    __builtin_amdgcn_sched_barrier(0);
+    frag_mma<OP>(acc, f1);
+    // (after the last stage this reads a stale slot; the values are unused)
+    frag_load<KN>(f0, lds + nxt * STAGE, 0, wm, wn);
+    interleave_mma_reads();
+    cur = nxt;
   }
-  mma_slab<OP, KN>(acc, sA0, sB0, wm, wn);
-  store(ra0, rb0, sA1, sB1);
-  __syncthreads();
-  mma_slab<OP, KN>(acc, sA1, sB1, wm, wn);
-  }
+  MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
 
   // ---------------------------------------------------------------- epilogue
   // acc[i][j][4 g + r] = C[m][n], m = mb + 32 i + l32, n = nb + 32 j + 8 g + 4 lh + r
-  // with mb = TI*256 + wm*128, nb = TJ*128 + wn*64. Each row group i (32 rows
-  // x 64 columns per wave) is staged through LDS (fp32, 68-float pitch) so
-  // global accesses are row-contiguous: "direct" reads 4 columns of a row,
-  // "transposed" reads 8 consecutive rows of one column.
+  // with mb = TI*256 + wm*128, nb = TJ*TN + wn*64. Results are staged as a
+  // 16-bit 256 x TN tile in LDS (the ring is free now) and written out from
+  // there: rows with 16-byte reads (whole 128-byte lines per store), columns
+  // (mirror, transposed output) with transposing reads, 8 rows per lane.
   const int l32 = lane & 31, lh = lane >> 5;
   constexpr bool F16 = OP == OP_F16;
-  constexpr int PITCH = 68;
-  const int mb = TI * TM + wm * 128, nb = TJ * TN + wn * 64;
-  float* const stg = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
+  constexpr int ROWB = TN * 2;   // bytes per staged row
+  constexpr int CPR = TN / 8;    // 16-byte chunks per staged row
+  const int m0 = TI * TM, n0 = TJ * TN;  // tile origin
+  const int mb = m0 + wm * 128, nb = n0 + wn * 64;
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // every wave is done reading the operand stages
 
-  auto stage_acc = [&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4_t*>(stg + l32 * PITCH + 32 * j + 8 * g + 4 * lh) =
-            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+  // Staged address of (row r, chunk c). The XOR gives 16 consecutive rows
+  // distinct chunk positions (accumulator-order writes) and keeps the four
+  // rows of a transposing read on distinct 32-byte pairs.
+  auto soff = [](int r, int c) {
+    const int x = ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+    return r * ROWB + ((c ^ x) << 4);
   };
-  // staging of a run-time row group (one small copy of the stores per group)
-  auto stage_acc_rt = [&](int i) {
-    switch (i) {
-      case 0: stage_acc(std::integral_constant<int, 0>{}); break;
-      case 1: stage_acc(std::integral_constant<int, 1>{}); break;
-      case 2: stage_acc(std::integral_constant<int, 2>{}); break;
-      default: stage_acc(std::integral_constant<int, 3>{}); break;
-    }
-  };
-  // direct access q (0..7): row 4 q + lane / 16 of the group, columns 4 (lane % 16)..+3
-  auto drow = [&](int q) { return 4 * q + (lane >> 4); };
-  const int dcol = 4 * (lane & 15);
-  // transposed access q (0..3): column (lane + 64 q) / 4, rows 8 ((lane + 64 q) % 4)..+7
-  auto tcol = [&](int q) { return (lane + 64 * q) >> 2; };
-  auto trow = [&](int q) { return 8 * ((lane + 64 * q) & 3); };
-
-  if (KIND == GRAM || KIND == POLY) {
-    char* C = P.ws + (KIND == GRAM ? M.a_off : M.b_off);
-    const char* Am = P.ws + M.a_off;
-    const int64_t ld = M.mp;
-    const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
-    auto round = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      stage_acc(ic);
-      __syncthreads();
-      const int m0 = mb + 32 * i;
-      // direct rows (POLY: bias loads first, then b A + c acc back into LDS)
-      u32x2 bias[8];
-      if (KIND == POLY) {
+  // acc (or values derived from it) -> staged 16-bit tile
+  auto stage16 = [&](bool f16) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          bias[q] = *reinterpret_cast<const u32x2*>(Am + (int64_t(m0 + drow(q)) * ld + nb + dcol) * 2);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int m = m0 + drow(q), n = nb + dcol;
-        f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
-        if (KIND == POLY) {
-          const u32x2 bq = bias[q];
-          const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
-                               Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = __fmaf_rn(P.c, v[r], P.b * a4[r]);
-          if constexpr (OP == OP_F16) {
-            // fp16 operands: B' = a I + b A + c A A, so the update is B' X
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
-          }
-          *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = v;
-        }
-        if (strict || m <= n) {
-          *reinterpret_cast<uint2*>(C + (int64_t(m) * ld + n) * 2) = pack4(v[0], v[1], v[2], v[3], F16);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (m <= n + r) Op<OP>::store(C, int64_t(m) * ld + n + r, v[r]);
-        }
-      }
-      if (KIND == POLY) __syncthreads();
-      // mirrored rows: C[n][m..m+7] = C[m..m+7][n]
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cc = tcol(q), rr = trow(q);
-        const int n = nb + cc, m = m0 + rr;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
-        if (strict || m + 7 < n) {
-          const uint2 lo = pack4(v[0], v[1], v[2], v[3], F16), hi = pack4(v[4], v[5], v[6], v[7], F16);
-          *reinterpret_cast<uint4*>(C + (int64_t(n) * ld + m) * 2) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (m + e < n) Op<OP>::store(C, int64_t(n) * ld + m + e, v[e]);
-        }
-      }
-      __syncthreads();
-    };
-    round(std::integral_constant<int, 0>{});
-    round(std::integral_constant<int, 1>{});
-    round(std::integral_constant<int, 2>{});
-    round(std::integral_constant<int, 3>{});
-  } else if constexpr (OP == OP_F16) {
-    // X' = B' hi + a 2^-11 lo  (B' = a I + B carries the a X term of the high
-    // part). lo lives in accumulator order, so no staging is needed.
-    const int64_t ldx = M.np;
-    uint16_t* lo = reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
-                   (((int64_t(TI) * (M.np >> 7) + TJ) * 4 + wave) * 32) * 256 + lane * 4;
-    char* xn = P.ws + M.xo_nxt;
-    const float a2 = P.a * (1.f / 2048.f);
-    auto round = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      u32x2 lv[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          lv[j][g] = *reinterpret_cast<const u32x2*>(lo + ((i * 2 + j) * 4 + g) * 256);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t lw[4] = {lv[j][g].x & 0xffffu, lv[j][g].x >> 16, lv[j][g].y & 0xffffu,
-                                  lv[j][g].y >> 16};
+          const int r = wm * 128 + 32 * i + l32, c = wn * 8 + 4 * j + g;
+          *reinterpret_cast<uint2*>(lds + soff(r, c) + lh * 8) =
+              e16::pack4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3], f16);
+        }
+  };
+  // Visits the staged tile by rows: fn(m, n, 16 bytes of n..n+7).
+  auto rows_out = [&](auto&& fn) {
+#pragma unroll 4
+    for (int q = 0; q < TM * CPR / NTHR; ++q) {
+      const int r = q * (NTHR / CPR) + threadIdx.x / CPR, c = threadIdx.x % CPR;
+      fn(m0 + r, n0 + 8 * c, *reinterpret_cast<const uint4*>(lds + soff(r, c)));
+    }
+  };
+  // Visits the staged tile by columns: fn(n, m, 16 bytes of rows m..m+7 of
+  // column n). A wave covers 16 columns x 32 rows per pass; 16-lane group h
+  // takes rows 8h..8h+7 of the block (two transposing reads of 4 rows).
+  auto cols_out = [&](auto&& fn) {
+    const int s = lane & 15, h = lane >> 4;
+#pragma unroll 4
+    for (int p = 0; p < (TM / 32) * (TN / 16) / NWAVE; ++p) {
+      const int P = wave + NWAVE * p, cb = P % (TN / 16), rb = P / (TN / 16);
+      const int r = rb * 32 + 8 * h + (s >> 2), col = cb * 16 + 4 * (s & 3);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(lds + soff(r, col >> 3) + (col & 7) * 2));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(lds + soff(r + 4, col >> 3) + (col & 7) * 2));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      fn(n0 + cb * 16 + s, m0 + rb * 32 + 8 * h, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    }
+  };
+  auto half = [](const uint4& v, int e) {  // 16-bit element e of 16 bytes
+    const uint32_t w = comp(v, e >> 1);
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+  };
+
+  if constexpr (KIND == GRAM || KIND == POLY) {
+    char* C = P.ws + (KIND == GRAM ? M.a_off : M.b_off);
+    const int64_t ld = M.mp;
+    const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
+    if constexpr (KIND == POLY) {
+      // B = c (A A) + b A (+ a I for fp16 operands, so that the update is
+      // B' X): the A tile is read in accumulator order, all loads first.
+      const char* Am = P.ws + M.a_off;
+      u32x2 bias[4][2][4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[i][j][4 * g + r] = __fmaf_rn(a2, Op<OP>::load16(lw[r]), acc[i][j][4 * g + r]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bias[i][j][g] = *reinterpret_cast<const u32x2*>(
+                Am + (int64_t(mb + 32 * i + l32) * ld + nb + 32 * j + 8 * g + 4 * lh) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 bq = bias[i][j][g];
+            const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
+                                 Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
+            const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float v = __fmaf_rn(P.c, acc[i][j][4 * g + r], P.b * a4[r]);
+              if constexpr (OP == OP_F16)
+                if (m == n + r && m < M.m) v += P.a;  // padding stays zero
+              acc[i][j][4 * g + r] = v;
+            }
+          }
+    }
+    stage16(F16);
+    __syncthreads();
+    // C[m][n..n+7] where m <= n
+    rows_out([&](int m, int n, const uint4& v) {
+      uint16_t* d = reinterpret_cast<uint16_t*>(C) + int64_t(m) * ld + n;
+      if (strict || m <= n) {
+        *reinterpret_cast<uint4*>(d) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (m <= n + e) d[e] = static_cast<uint16_t>(half(v, e));
+      }
+    });
+    // mirror: C[n][m..m+7] = C[m..m+7][n] where m < n
+    cols_out([&](int n, int m, const uint4& v) {
+      uint16_t* d = reinterpret_cast<uint16_t*>(C) + int64_t(n) * ld + m;
+      if (strict || m + 7 < n) {
+        *reinterpret_cast<uint4*>(d) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (m + e < n) d[e] = static_cast<uint16_t>(half(v, e));
+      }
+    });
+  } else {
+    // UPDATE. The low part of X is read (and, unless this is the last step,
+    // written back) in accumulator order for fp16 operands; for bf16
+    // operands it is row-major and read at the accumulator positions.
+    const int64_t ldx = M.np;
+    constexpr int64_t LO_TILE = int64_t(TM) * TN;
+    uint16_t* lo_t = reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
+                     (((int64_t(TI) * (M.np / TN) + TJ) * NWAVE + wave) * 32) * 256 + lane * 4;
+    const uint16_t* hi_cur = reinterpret_cast<const uint16_t*>(P.ws + M.xo_cur);
+    auto lo_ptr = [&](int i, int j, int g) -> uint16_t* {
+      if constexpr (F16) return lo_t + ((i * 2 + j) * 4 + g) * 256;
+      else
+        return reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
+               int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh;
+    };
+    (void)LO_TILE;
+    // all loads first (one latency for the tile)
+    u32x2 lv[4][2][4];
+    u32x2 hv[F16 ? 1 : 4][F16 ? 1 : 2][F16 ? 1 : 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
+          if constexpr (!F16)
+            hv[i][j][g] = *reinterpret_cast<const u32x2*>(
+                hi_cur + int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh);
+        }
+    const float a2 = F16 ? P.a * (1.f / 2048.f) : P.a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lw[4] = {lv[i][j][g].x & 0xffffu, lv[i][j][g].x >> 16,
+                                  lv[i][j][g].y & 0xffffu, lv[i][j][g].y >> 16};
+          if constexpr (F16) {
+            // X' = B' hi + a 2^-11 lo  (B' = a I + B carries a hi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][4 * g + r] = __fmaf_rn(a2, Op<OP>::load16(lw[r]), acc[i][j][4 * g + r]);
+          } else {
+            // X' = B hi + a (hi + lo)
+            const uint32_t hw[4] = {hv[i][j][g].x & 0xffffu, hv[i][j][g].x >> 16,
+                                    hv[i][j][g].y & 0xffffu, hv[i][j][g].y >> 16};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][4 * g + r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), acc[i][j][4 * g + r]);
+          }
           if constexpr (!LAST) {
-            const int m = mb + 32 * i + l32, n0 = nb + 32 * j + 8 * g + 4 * lh;
             uint32_t nh[4], nl[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) Op<OP>::split(acc[i][j][4 * g + r], nh[r], nl[r]);
-            *reinterpret_cast<uint2*>(xn + (int64_t(m) * ldx + n0) * 2) =
-                make_uint2(nh[0] | (nh[1] << 16), nh[2] | (nh[3] << 16));
-            *reinterpret_cast<uint2*>(lo + ((i * 2 + j) * 4 + g) * 256) =
+            *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) =
                 make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
           }
         }
-    };
-    round(std::integral_constant<int, 0>{});
-    round(std::integral_constant<int, 1>{});
-    round(std::integral_constant<int, 2>{});
-    round(std::integral_constant<int, 3>{});
-    if constexpr (LAST) {
-      // `out` in the caller's layout: stage X' through LDS
-      T* o = static_cast<T*>(M.out);
-      auto out_round = [&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        stage_acc(ic);
-        __syncthreads();
-        const int m0 = mb + 32 * i;
-        if (!M.tall) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int m = m0 + drow(q), n = nb + dcol;
-            if (m >= M.m) continue;
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
-            const int64_t co = int64_t(m) * M.ld + n;
-            if (M.vec_ok && n + 3 < M.n) {
-              if constexpr (sizeof(T) == 2)
-                *reinterpret_cast<uint2*>(o + co) = pack4(x[0], x[1], x[2], x[3], false);
-              else
-                *reinterpret_cast<f32x4_t*>(o + co) = x;
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (n + r < M.n) Elem<T>::store(o, co + r, x[r]);
-            }
-          }
+    if constexpr (!LAST) {
+      // the next high part (the operand of the next step), rows of the tile
+      stage16(F16);  // rounds each value to the operand format, as split does
+      __syncthreads();
+      uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
+      rows_out([&](int m, int n, const uint4& v) {
+        *reinterpret_cast<uint4*>(xn + int64_t(m) * ldx + n) = v;
+      });
+    } else {
+      // `out` in the caller's layout (bf16), transposed for tall matrices
+      stage16(false);
+      __syncthreads();
+      uint16_t* o = static_cast<uint16_t*>(M.out);
+      auto put = [&](int row, int col, int nrow, int ncol, const uint4& v) {
+        if (row >= nrow) return;
+        uint16_t* d = o + int64_t(row) * M.ld + col;
+        if (M.vec_ok && col + 7 < ncol) {
+          *reinterpret_cast<uint4*>(d) = v;
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cc = tcol(q), rr = trow(q);
-            const int n = nb + cc, m = m0 + rr;
-            if (n >= M.n) continue;
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
-            const int64_t co = int64_t(n) * M.ld + m;
-            if (M.vec_ok && m + 7 < M.m) {
-              if constexpr (sizeof(T) == 2) {
-                const uint2 l4 = pack4(v[0], v[1], v[2], v[3], false), h4 = pack4(v[4], v[5], v[6], v[7], false);
-                *reinterpret_cast<uint4*>(o + co) = make_uint4(l4.x, l4.y, h4.x, h4.y);
-              } else {
-                *reinterpret_cast<f32x4_t*>(o + co) = f32x4_t{v[0], v[1], v[2], v[3]};
-                *reinterpret_cast<f32x4_t*>(o + co + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (m + e < M.m) Elem<T>::store(o, co + e, v[e]);
-            }
-          }
+          for (int e = 0; e < 8; ++e)
+            if (col + e < ncol) d[e] = static_cast<uint16_t>(half(v, e));
         }
-        __syncthreads();
       };
-      out_round(std::integral_constant<int, 0>{});
-      out_round(std::integral_constant<int, 1>{});
-      out_round(std::integral_constant<int, 2>{});
-      out_round(std::integral_constant<int, 3>{});
+      if (!M.tall)
+        rows_out([&](int m, int n, const uint4& v) { put(m, n, M.m, M.n, v); });
+      else
+        cols_out([&](int n, int m, const uint4& v) { put(n, m, M.n, M.m, v); });
     }
-  } else {
-    const int64_t ldx = M.np;
-    const char* xh = P.ws + M.xo_cur;      // hi part of X (operand)
-    char* xl = P.ws + M.xl_off;                      // lo part, updated in place
-    char* xn = P.ws + M.xo_nxt;        // next hi part
-    T* o = static_cast<T*>(M.out);
-auto round = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      __builtin_amdgcn_sched_barrier(0);  // keep each round's loads inside it
-      stage_acc(ic);
-      __syncthreads();
-      const int m0 = mb + 32 * i;
-#pragma unroll
-      for (int qb = 0; qb < 8; qb += 4) {
-      u32x2 hv[8], lv[8];
-#pragma unroll
-      for (int q = qb; q < qb + 4; ++q) {
-        const int64_t off = int64_t(m0 + drow(q)) * ldx + nb + dcol;
-        hv[q] = *reinterpret_cast<const u32x2*>(xh + off * 2);
-        lv[q] = *reinterpret_cast<const u32x2*>(xl + off * 2);
-      }
-#pragma unroll
-      for (int q = qb; q < qb + 4; ++q) {
-        const int m = m0 + drow(q), n = nb + dcol;
-        const int64_t off = int64_t(m) * ldx + n;
-        f32x4_t x = *reinterpret_cast<const f32x4_t*>(stg + drow(q) * PITCH + dcol);
-        const uint32_t hw[4] = {hv[q].x & 0xffffu, hv[q].x >> 16, hv[q].y & 0xffffu, hv[q].y >> 16};
-        const uint32_t lw[4] = {lv[q].x & 0xffffu, lv[q].x >> 16, lv[q].y & 0xffffu, lv[q].y >> 16};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), x[r]);
-        if constexpr (!LAST) {
-          uint32_t nh[4], nl[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Op<OP>::split(x[r], nh[r], nl[r]);
-          *reinterpret_cast<uint2*>(xn + off * 2) = make_uint2(nh[0] | (nh[1] << 16), nh[2] | (nh[3] << 16));
-          *reinterpret_cast<uint2*>(xl + off * 2) = make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
-        } else if (!M.tall) {
-          // last step, rows<=cols matrix: `out` rows m, columns n..n+3
-          if (m < M.m) {
-            const int64_t co = int64_t(m) * M.ld + n;
-            if (M.vec_ok && n + 3 < M.n) {
-              if constexpr (sizeof(T) == 2)
-                *reinterpret_cast<uint2*>(o + co) = pack4(x[0], x[1], x[2], x[3], false);
-              else
-                *reinterpret_cast<f32x4_t*>(o + co) = x;
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (n + r < M.n) Elem<T>::store(o, co + r, x[r]);
-            }
-          }
-        } else {
-          *reinterpret_cast<f32x4_t*>(stg + drow(q) * PITCH + dcol) = x;  // for the transposed write
-        }
-      }
-      }
-      if (LAST && M.tall) {
-        __syncthreads();
-        // `out` is the transpose: out rows n, columns m..m+7
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cc = tcol(q), rr = trow(q);
-          const int n = nb + cc, m = m0 + rr;
-          if (n >= M.n) continue;
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = stg[(rr + e) * PITCH + cc];
-          const int64_t co = int64_t(n) * M.ld + m;
-          if (M.vec_ok && m + 7 < M.m) {
-            if constexpr (sizeof(T) == 2) {
-              const uint2 lo = pack4(v[0], v[1], v[2], v[3], false), hi = pack4(v[4], v[5], v[6], v[7], false);
-              *reinterpret_cast<uint4*>(o + co) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {
-              *reinterpret_cast<f32x4_t*>(o + co) = f32x4_t{v[0], v[1], v[2], v[3]};
-              *reinterpret_cast<f32x4_t*>(o + co + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (m + e < M.m) Elem<T>::store(o, co + e, v[e]);
-          }
-        }
-      }
-      __syncthreads();
-    };
-    round(std::integral_constant<int, 0>{});
-    round(std::integral_constant<int, 1>{});
-    round(std::integral_constant<int, 2>{});
-    round(std::integral_constant<int, 3>{});
   }
 }
 
@@ -1408,7 +1148,8 @@ auto round = [&](auto ic) {
 template <typename T, int OP>
 static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(grid), b(256);
+  const bool engine16 = OP != OP_F32 && kind >= MUON_K_GRAM;
+  dim3 g(grid), b(engine16 ? e16::NTHR : 256);
   switch (kind) {
     case MUON_K_MOMENTUM: hipLaunchKernelGGL(momentum_kernel<T>, g, b, 0, s, a); break;
     case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;

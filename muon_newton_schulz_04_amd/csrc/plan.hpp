@@ -13,8 +13,11 @@ namespace muon {
 
 // Tile sizes shared by the planner and the kernels.
 constexpr int kGemmTile = 128;         // output tile of the matrix-core kernels (fp32 sets)
-constexpr int kTileM16 = 256;          // 16-bit-operand engine (bf16 sets): 256 x 128 tiles
-constexpr int kTileN16 = 128;
+constexpr int kTileM16 = 256;          // 16-bit-operand engine (bf16 sets): 256 x 256 tiles
+#ifndef MUON_TILE_N
+#define MUON_TILE_N 256
+#endif
+constexpr int kTileN16 = MUON_TILE_N;
 constexpr int kNormTile = 64;          // tile of the normalise / layout kernel
 constexpr int kMomentumElems = 16384;  // target elements per momentum work item
 constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X

@@ -111,7 +111,8 @@ def expected_ws(shapes, dtype):
     off = ru(parts * 4, 256)
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
-        mp, np_ = ru(m, 256 if dtype == mu.MUON_BF16 else 128), ru(n, 128)
+        t = 256 if dtype == mu.MUON_BF16 else 128
+        mp, np_ = ru(m, t), ru(n, t)
         sizes = ([mp * np_ * 2, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
                  if dtype == mu.MUON_BF16 else
                  [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
@@ -138,8 +139,7 @@ SHAPE_SETS = {
 @pytest.mark.parametrize("setname", list(SHAPE_SETS))
 def test_schedules_cover_every_tile_exactly_once(lib, setname, dtype):
     shapes = SHAPE_SETS[setname]
-    tm = 256 if dtype == mu.MUON_BF16 else 128
-    tn = 128
+    tm = tn = 256 if dtype == mu.MUON_BF16 else 128
     scheds = [mu.muon_schedule_query(shapes, dtype, k) for k in range(5)]
     for k, s in enumerate(scheds):
         assert len(s) % 8 == 0, "grid is a multiple of the XCD count"
