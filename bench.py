@@ -7,9 +7,11 @@ A step is one muon_plan_step over all matrices of the workload (momentum,
 normalisation and k Newton-Schulz steps), inputs resident in HBM. `value` is
 algorithmic TFLOP/s of the whole step; `roofline` describes the kernel with
 the largest share of the step's time, timed with HIP events recorded around
-each launch on the step's stream in a second pass of the same length; the
+each launch in a second pass of the same length (in that pass the launches
+run one at a time on the step's stream, so each interval holds one launch;
+the timed pass runs large sets as two concurrent groups); the
 CPU baseline times the float64 oracle on a bounded sample of the same
-matrices. `roofline.traffic` is the dominant kernel's HBM bytes per launch
+matrices. `roofline.traffic` is the dominant kernel's HBM bytes per step
 from the committed rocprofv3 counter summary (null if that summary was taken
 on a different kernel source). Prints one JSON line.
 """
@@ -32,14 +34,14 @@ HBM_PEAK_GBS = 8000.0
 
 
 def kernel_work(shapes, steps, dtype):
-    """Algorithmic work per launch of each kernel: {kernel: (flops, bytes)}.
+    """Algorithmic work of each kernel per update step (all its launches):
+    {kernel: (flops, bytes)}.
 
     Bytes count each operand read once and each result written once, in the
     library's formats: bf16 sets keep X as two 16-bit halves (high part = the
     matrix-core operand, low part = the residual) and A, B as 16-bit; fp32
-    sets keep everything in fp32. The update's bytes are the average over the
-    `steps` launches of a step (the last one writes `out` instead of X's
-    halves)."""
+    sets keep everything in fp32. The Newton-Schulz kernels run `steps` times;
+    the last update writes `out` instead of X's halves."""
     es = 2 if dtype == "bf16" else 4
     xb = 4                                  # X per element: hi + lo halves, or fp32
     xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
@@ -49,23 +51,24 @@ def kernel_work(shapes, steps, dtype):
         mn, mm = float(m * n), float(m * m)
         w["momentum"][1] += 3 * es * mn          # read G, buf; write buf'
         w["normalize"][1] += 2 * es * mn + xb * mn   # read G, buf'; write X
-        w["gram"][0] += m * (m + 1) * n
-        w["gram"][1] += xop * mn + es * mm       # read X operand; write A
-        w["poly"][0] += m * m * (m + 1)
-        w["poly"][1] += 2 * es * mm              # read A; write B
-        w["update"][0] += 2 * m * m * n
+        w["gram"][0] += steps * m * (m + 1) * n
+        w["gram"][1] += steps * (xop * mn + es * mm)       # read X operand; write A
+        w["poly"][0] += steps * m * m * (m + 1)
+        w["poly"][1] += steps * 2 * es * mm                # read A; write B
+        w["update"][0] += steps * 2 * m * m * n
         reg = es * mm + xb * mn + xb * mn        # read B, X; write X
         last = es * mm + xb * mn + es * mn       # read B, X; write out
-        w["update"][1] += (reg * (steps - 1) + last) / steps if steps else 0.0
+        w["update"][1] += reg * (steps - 1) + last if steps else 0.0
     return {k: (v[0], v[1]) for k, v in w.items()}
 
 
-def roofline_of(flops, nbytes, avg_s, dtype):
-    """Both roofs for one kernel; the binding one (the larger lower bound on
-    the launch time) is the headline, the other is kept under `other`."""
-    mf = {"bound": "mfma", "achieved": flops / avg_s / 1e12, "peak": PEAK[dtype],
+def roofline_of(flops, nbytes, secs, dtype):
+    """Both roofs for one kernel's work in `secs`; the binding one (the larger
+    lower bound on the time) is the headline, the other is kept under
+    `other`."""
+    mf = {"bound": "mfma", "achieved": flops / secs / 1e12, "peak": PEAK[dtype],
           "unit": "TFLOP/s"}
-    hb = {"bound": "hbm", "achieved": nbytes / avg_s / 1e9, "peak": HBM_PEAK_GBS,
+    hb = {"bound": "hbm", "achieved": nbytes / secs / 1e9, "peak": HBM_PEAK_GBS,
           "unit": "GB/s"}
     for r in (mf, hb):
         r["frac"] = r["achieved"] / r["peak"]
@@ -79,9 +82,10 @@ def roofline_of(flops, nbytes, avg_s, dtype):
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or
-    None when it is missing or was taken on a different kernel source."""
+    """HBM bytes per update step of `kernel` (all its launches) from the
+    committed rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE scaled by a
+    plain-copy calibration), or None when it is missing or was taken on a
+    different kernel source."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     src = os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", "kernels.hip")
@@ -94,8 +98,7 @@ def measured_traffic(workload: str, kernel: str):
         return None
     if rec.get("kernel_source_sha256") != sha:
         return None
-    key = "update_step_average" if kernel == "update" else kernel
-    ent = rec.get("per_launch", {}).get(key)
+    ent = rec.get("per_step", {}).get(kernel)
     return None if ent is None else ent["traffic_bytes"]
 
 
@@ -208,20 +211,20 @@ def main():
     for name, (tot_ms, n) in kt.items():
         if n == 0:
             continue
-        avg = tot_ms / n
+        step_s = tot_ms / args.steps * 1e-3
         flops, nbytes = work[name]
-        ent = {"launches_per_step": n / args.steps, "avg_us": avg * 1e3,
-               "ms_per_step": tot_ms / args.steps,
-               "GB/s": nbytes / (avg * 1e-3) / 1e9}
+        ent = {"launches_per_step": n / args.steps, "us_per_step": step_s * 1e6,
+               "GB/s": nbytes / step_s / 1e9}
         if flops:
-            ent["TFLOP/s"] = flops / (avg * 1e-3) / 1e12
+            ent["TFLOP/s"] = flops / step_s / 1e12
         per_kernel[name] = ent
     dom = max(kt, key=lambda k: kt[k][0])
-    d_avg = kt[dom][0] / kt[dom][1]
-    roof = roofline_of(*work[dom], d_avg * 1e-3, wl.dtype)
+    d_step = kt[dom][0] / args.steps * 1e-3
+    roof = roofline_of(*work[dom], d_step, wl.dtype)
     roof["traffic"] = measured_traffic(wl.name, dom)
     roof["kernel"] = dom
-    roof["avg_launch_us"] = d_avg * 1e3
+    roof["us_per_step"] = d_step * 1e6
+    roof["launches_per_step"] = kt[dom][1] / args.steps
 
     line = {
         "metric": METRIC,

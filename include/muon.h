@@ -164,8 +164,10 @@ typedef enum {
   MUON_K_COUNT = 5
 } muon_kernel_kind;
 
-/* Host-only schedule query: the work items kernel `kind` runs for `mats`,
- * four int32 per item {matrix, a, b, c} (momentum: {matrix, first row,
+/* Host-only schedule query: the work items kernel `kind` runs for `mats`
+ * (for a plan split into groups, the groups' schedules one after the other,
+ * each a multiple of 8 items), four int32 per item {matrix, a, b, c}
+ * (momentum: {matrix, first row,
  * row count, partial slot}; normalise: {matrix, tile row, tile col, 0} of
  * 64 x 64 tiles of the rows<=cols orientation; gram/poly: {matrix, tile
  * row, tile col, 0} of the tiles on or above the diagonal; update: {matrix,
@@ -177,12 +179,16 @@ typedef enum {
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,
                                 int32_t kind, int32_t* items, int64_t cap, int64_t* count);
 
-/* Per-kernel timing with HIP events recorded on the step's stream around
- * each launch. Off by default; while on, every muon_plan_step records
- * events, and muon_plan_kernel_times (which synchronises the plan's last
- * stream) accumulates elapsed milliseconds and launch counts per
- * muon_kernel_kind into ms[MUON_K_COUNT] and launches[MUON_K_COUNT], summed
- * over the steps since timing was enabled or last read (reading resets). */
+/* Per-kernel timing. A plan may split a large set into groups of matrices
+ * whose kernels run concurrently on streams of the plan (joined back to the
+ * caller's stream before muon_plan_step's work ends). While timing is on,
+ * every muon_plan_step instead runs each kernel over the whole set in one
+ * launch on the step's stream, with HIP events recorded around each
+ * launch; the results are bitwise the same. muon_plan_kernel_times (which
+ * waits for the recorded events) accumulates elapsed milliseconds and
+ * launch counts per muon_kernel_kind into ms[MUON_K_COUNT] and
+ * launches[MUON_K_COUNT], summed over the steps since timing was enabled
+ * or last read (reading resets). Off by default. */
 muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable);
 muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches);
 

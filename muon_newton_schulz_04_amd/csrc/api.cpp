@@ -28,7 +28,12 @@ struct muon_plan_s {
   void* dmem = nullptr;                       // MatInfo table + schedules
   const MatInfo* d_mats = nullptr;
   const WorkItem* d_items[MUON_K_COUNT] = {};
-  int grid[MUON_K_COUNT] = {};
+  const WorkItem* d_whole[MUON_K_COUNT] = {};  // one-group schedules (timing)
+  // groups > 1: one stream per group (default priority) and the events that
+  // fork them from, and join them back to, the caller's stream
+  hipStream_t gstream[muon::kMaxGroups] = {};
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t join_ev[muon::kMaxGroups] = {};
   bool timing = false;
   std::vector<TimedLaunch> pending;           // recorded, not yet read
   std::vector<hipEvent_t> free_events;
@@ -46,11 +51,14 @@ muon_status upload(muon_plan_s* p) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_E_DEVICE;
   p->device = dev;
   size_t bytes = sizeof(MatInfo) * std::max<size_t>(1, p->host.info.size());
-  size_t offs[MUON_K_COUNT];
+  size_t offs[MUON_K_COUNT], woffs[MUON_K_COUNT];
   for (int k = 0; k < MUON_K_COUNT; ++k) {
     bytes = (bytes + 255) / 256 * 256;
     offs[k] = bytes;
     bytes += sizeof(WorkItem) * std::max<size_t>(1, p->host.sched[k].items.size());
+    bytes = (bytes + 255) / 256 * 256;
+    woffs[k] = bytes;
+    bytes += sizeof(WorkItem) * std::max<size_t>(1, p->host.whole[k].items.size());
   }
   std::vector<char> h(bytes, 0);
   if (!p->host.info.empty())
@@ -58,7 +66,19 @@ muon_status upload(muon_plan_s* p) {
   for (int k = 0; k < MUON_K_COUNT; ++k) {
     const auto& it = p->host.sched[k].items;
     if (!it.empty()) std::memcpy(h.data() + offs[k], it.data(), sizeof(WorkItem) * it.size());
-    p->grid[k] = static_cast<int>(it.size());
+    const auto& wt = p->host.whole[k].items;
+    if (!wt.empty()) std::memcpy(h.data() + woffs[k], wt.data(), sizeof(WorkItem) * wt.size());
+  }
+  if (p->host.ngroups > 1) {
+    auto fail = [&]() {
+      (void)hipGetLastError();
+      return MUON_E_ALLOC;
+    };
+    if (hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess) return fail();
+    for (int g = 0; g < p->host.ngroups; ++g) {
+      if (hipStreamCreateWithFlags(&p->gstream[g], hipStreamNonBlocking) != hipSuccess) return fail();
+      if (hipEventCreateWithFlags(&p->join_ev[g], hipEventDisableTiming) != hipSuccess) return fail();
+    }
   }
   if (hipMalloc(&p->dmem, bytes) != hipSuccess) {
     p->dmem = nullptr;
@@ -73,7 +93,10 @@ muon_status upload(muon_plan_s* p) {
   }
   char* base = static_cast<char*>(p->dmem);
   p->d_mats = reinterpret_cast<const MatInfo*>(base);
-  for (int k = 0; k < MUON_K_COUNT; ++k) p->d_items[k] = reinterpret_cast<const WorkItem*>(base + offs[k]);
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    p->d_items[k] = reinterpret_cast<const WorkItem*>(base + offs[k]);
+    p->d_whole[k] = reinterpret_cast<const WorkItem*>(base + woffs[k]);
+  }
   return MUON_OK;
 }
 
@@ -85,6 +108,11 @@ void release(muon_plan_s* p) {
     (void)hipEventDestroy(t.stop);
   }
   for (auto e : p->free_events) (void)hipEventDestroy(e);
+  for (int g = 0; g < muon::kMaxGroups; ++g) {
+    if (p->gstream[g]) (void)hipStreamDestroy(p->gstream[g]);
+    if (p->join_ev[g]) (void)hipEventDestroy(p->join_ev[g]);
+  }
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
   if (p->dmem) (void)hipFree(p->dmem);
   delete p;
 }
@@ -130,31 +158,67 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.use_mom = use_mom ? 1 : 0;
   a.direct = cfg->steps == 0 ? 1 : 0;
 
-  auto launch = [&](int kind) -> muon_status {
-    a.items = p->d_items[kind];
-    TimedLaunch t{kind, nullptr, nullptr};
-    if (p->timing) {
-      t.start = get_event(p);
-      t.stop = get_event(p);
-      if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
-    }
-    if (muon::launch_kernel(kind, H.dtype, cfg->precision, a, p->grid[kind], s) != hipSuccess) return MUON_E_LAUNCH;
-    if (p->timing) {
-      if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
-      p->pending.push_back(t);
+  // One launch of kernel `kind` for group g on stream `q`.
+  auto launch = [&](int kind, int g, hipStream_t q) -> muon_status {
+    const int32_t b = H.gbeg[g][kind], e = H.gbeg[g + 1][kind];
+    if (e == b) return MUON_OK;
+    a.items = p->d_items[kind] + b;
+    return muon::launch_kernel(kind, H.dtype, cfg->precision, a, e - b, q) == hipSuccess
+               ? MUON_OK
+               : MUON_E_LAUNCH;
+  };
+  // Per-kernel timing: kernel `kind` over the whole set in one launch on
+  // the caller's stream (the one-group schedule), bracketed by HIP events.
+  auto timed = [&](int kind) -> muon_status {
+    const int grid = static_cast<int>(H.whole[kind].items.size());
+    if (grid == 0) return MUON_OK;
+    TimedLaunch t{kind, get_event(p), get_event(p)};
+    if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
+    a.items = p->d_whole[kind];
+    if (muon::launch_kernel(kind, H.dtype, cfg->precision, a, grid, s) != hipSuccess)
+      return MUON_E_LAUNCH;
+    if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
+    p->pending.push_back(t);
+    return MUON_OK;
+  };
+  // The whole sequence of one group on stream q: momentum, normalise,
+  // k x (gram, poly, update).
+  auto sequence = [&](int g, hipStream_t q) -> muon_status {
+    muon_status r;
+    if ((r = launch(MUON_K_MOMENTUM, g, q)) != MUON_OK) return r;
+    if ((r = launch(MUON_K_NORMALIZE, g, q)) != MUON_OK) return r;
+    for (int t = 0; t < cfg->steps; ++t) {
+      a.cur = t & 1;
+      a.last = t == cfg->steps - 1 ? 1 : 0;
+      for (int kind : {MUON_K_GRAM, MUON_K_POLY, MUON_K_UPDATE})
+        if ((r = launch(kind, g, q)) != MUON_OK) return r;
     }
     return MUON_OK;
   };
 
-  if ((st = launch(MUON_K_MOMENTUM)) != MUON_OK) return st;
-  if ((st = launch(MUON_K_NORMALIZE)) != MUON_OK) return st;
-  for (int t = 0; t < cfg->steps; ++t) {
-    a.cur = t & 1;
-    a.last = t == cfg->steps - 1 ? 1 : 0;
-    if ((st = launch(MUON_K_GRAM)) != MUON_OK) return st;
-    if ((st = launch(MUON_K_POLY)) != MUON_OK) return st;
-    if ((st = launch(MUON_K_UPDATE)) != MUON_OK) return st;
+  if (p->timing) {
+    muon_status r;
+    if ((r = timed(MUON_K_MOMENTUM)) != MUON_OK) return r;
+    if ((r = timed(MUON_K_NORMALIZE)) != MUON_OK) return r;
+    for (int t = 0; t < cfg->steps; ++t) {
+      a.cur = t & 1;
+      a.last = t == cfg->steps - 1 ? 1 : 0;
+      for (int kind : {MUON_K_GRAM, MUON_K_POLY, MUON_K_UPDATE})
+        if ((r = timed(kind)) != MUON_OK) return r;
+    }
+    return MUON_OK;
   }
+  if (H.ngroups == 1) return sequence(0, s);
+  // several groups, no timing: each group runs its whole sequence on its
+  // own stream, forked once and joined once
+  if (hipEventRecord(p->fork_ev, s) != hipSuccess) return MUON_E_LAUNCH;
+  for (int g = 0; g < H.ngroups; ++g) {
+    if (hipStreamWaitEvent(p->gstream[g], p->fork_ev, 0) != hipSuccess) return MUON_E_LAUNCH;
+    if ((st = sequence(g, p->gstream[g])) != MUON_OK) return st;
+    if (hipEventRecord(p->join_ev[g], p->gstream[g]) != hipSuccess) return MUON_E_LAUNCH;
+  }
+  for (int g = 0; g < H.ngroups; ++g)
+    if (hipStreamWaitEvent(s, p->join_ev[g], 0) != hipSuccess) return MUON_E_LAUNCH;
   return MUON_OK;
 }
 

@@ -715,29 +715,36 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 // the row operand, TN/16 of the column operand): rows of the row operand at
 // opA + row * lda (bytes), k0 .. k0+31; the column operand either the same
 // way from opB, or k-rows k0 .. k0+31 of TN columns at opB + k * ldb.
-constexpr int DMA_PER_STAGE = (16 + TN / 16) / NWAVE;  // pieces per wave per stage
+#ifndef MUON_DMA_WAVES
+#define MUON_DMA_WAVES 0
+#endif
+// Waves that issue the DMA: all (0), the first half (1) or the second half (2).
+constexpr int NDW = MUON_DMA_WAVES == 0 ? NWAVE : NWAVE / 2;
+constexpr int DW0 = MUON_DMA_WAVES == 2 ? NWAVE / 2 : 0;
+constexpr int DMA_PER_STAGE = (16 + TN / 16) / NDW;  // pieces per issuing wave per stage
 template <bool KN>
 __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0) {
-  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+  const int w = (threadIdx.x >> 6) - DW0, i = threadIdx.x & 63;
+  if (NDW != NWAVE && (w < 0 || w >= NDW)) return;
   const uint32_t base = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + (w << 10));
 #pragma unroll
-  for (int q = 0; q < 16 / NWAVE; ++q) {
-    const int I = w + NWAVE * q;  // piece of the row operand
+  for (int q = 0; q < 16 / NDW; ++q) {
+    const int I = w + NDW * q;  // piece of the row operand
     const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    dma16(opA + row * lda + k0 * 2 + g * 16, base + q * NWAVE * 1024);
+    dma16(opA + row * lda + k0 * 2 + g * 16, base + q * NDW * 1024);
   }
 #pragma unroll
-  for (int q = 0; q < TN / 16 / NWAVE; ++q) {
-    const int I = w + NWAVE * q;  // piece of the column operand
+  for (int q = 0; q < TN / 16 / NDW; ++q) {
+    const int I = w + NDW * q;  // piece of the column operand
     if constexpr (!KN) {
       const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-      dma16(opB + row * ldb + k0 * 2 + g * 16, base + HALF_A + q * NWAVE * 1024);
+      dma16(opB + row * ldb + k0 * 2 + g * 16, base + HALF_A + q * NDW * 1024);
     } else {
       constexpr int RPP = 1024 / KROW;  // k-rows per piece
       const int kr = RPP * I + i / (64 / RPP), g = (i % (64 / RPP)) ^ ((kr & 3) << 2);
-      dma16(opB + (k0 + kr) * ldb + g * 16, base + HALF_A + q * NWAVE * 1024);
+      dma16(opB + (k0 + kr) * ldb + g * 16, base + HALF_A + q * NDW * 1024);
     }
   }
 }
@@ -997,37 +1004,47 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
     if constexpr (KIND == POLY) {
       // B = c (A A) + b A (+ a I for fp16 operands, so that the update is
-      // B' X): the A tile is read in accumulator order, all loads first.
+      // B' X). The A tile goes into the staging layout by DMA (whole rows,
+      // coalesced); each lane then reads its accumulator positions, combines
+      // and writes the result back to the same positions (no other lane
+      // touches them, so no barrier is needed in between).
       const char* Am = P.ws + M.a_off;
-      u32x2 bias[4][2][4];
+      constexpr int RPP = 1024 / ROWB;  // staged rows per 1 KB piece
+      constexpr int LPR = 64 / RPP;     // lanes per row
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            bias[i][j][g] = *reinterpret_cast<const u32x2*>(
-                Am + (int64_t(mb + 32 * i + l32) * ld + nb + 32 * j + 8 * g + 4 * lh) * 2);
+      for (int q = 0; q < TM * ROWB / 1024 / NWAVE; ++q) {
+        const int I = wave + NWAVE * q;
+        const int r = RPP * I + lane / LPR, sl = lane % LPR;
+        const int x = ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + I * 1024);
+        e16::dma16(Am + (int64_t(m0 + r) * ld + n0 + 8 * (sl ^ x)) * 2, base);
+      }
+      MUON_WAIT_VMCNT(0);
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const u32x2 bq = bias[i][j][g];
+            char* sp = lds + soff(wm * 128 + 32 * i + l32, wn * 8 + 4 * j + g) + lh * 8;
+            const u32x2 bq = *reinterpret_cast<const u32x2*>(sp);
             const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
                                  Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
             const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh;
+            float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float v = __fmaf_rn(P.c, acc[i][j][4 * g + r], P.b * a4[r]);
+              v[r] = __fmaf_rn(P.c, acc[i][j][4 * g + r], P.b * a4[r]);
               if constexpr (OP == OP_F16)
-                if (m == n + r && m < M.m) v += P.a;  // padding stays zero
-              acc[i][j][4 * g + r] = v;
+                if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
             }
+            *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], F16);
           }
+    } else {
+      stage16(F16);
     }
-    stage16(F16);
     __syncthreads();
     // C[m][n..n+7] where m <= n
     rows_out([&](int m, int n, const uint4& v) {
@@ -1056,7 +1073,6 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     // written back) in accumulator order for fp16 operands; for bf16
     // operands it is row-major and read at the accumulator positions.
     const int64_t ldx = M.np;
-    constexpr int64_t LO_TILE = int64_t(TM) * TN;
     uint16_t* lo_t = reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
                      (((int64_t(TI) * (M.np / TN) + TJ) * NWAVE + wave) * 32) * 256 + lane * 4;
     const uint16_t* hi_cur = reinterpret_cast<const uint16_t*>(P.ws + M.xo_cur);
@@ -1066,24 +1082,31 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
         return reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
                int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh;
     };
-    (void)LO_TILE;
-    // all loads first (one latency for the tile)
+    // fp16 operands: all loads first (one latency for the tile); bf16
+    // operands (two parts to read) load one row group at a time.
     u32x2 lv[4][2][4];
-    u32x2 hv[F16 ? 1 : 4][F16 ? 1 : 2][F16 ? 1 : 4];
+    if constexpr (F16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
-          if constexpr (!F16)
-            hv[i][j][g] = *reinterpret_cast<const u32x2*>(
+          for (int g = 0; g < 4; ++g) lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
+    }
+    const float a2 = P.a * (1.f / 2048.f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2 hv[2][4];
+      if constexpr (!F16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
+            hv[j][g] = *reinterpret_cast<const u32x2*>(
                 hi_cur + int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh);
-        }
-    const float a2 = F16 ? P.a * (1.f / 2048.f) : P.a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+          }
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1097,8 +1120,8 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
               acc[i][j][4 * g + r] = __fmaf_rn(a2, Op<OP>::load16(lw[r]), acc[i][j][4 * g + r]);
           } else {
             // X' = B hi + a (hi + lo)
-            const uint32_t hw[4] = {hv[i][j][g].x & 0xffffu, hv[i][j][g].x >> 16,
-                                    hv[i][j][g].y & 0xffffu, hv[i][j][g].y >> 16};
+            const uint32_t hw[4] = {hv[j][g].x & 0xffffu, hv[j][g].x >> 16, hv[j][g].y & 0xffffu,
+                                    hv[j][g].y >> 16};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               acc[i][j][4 * g + r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), acc[i][j][4 * g + r]);
@@ -1111,6 +1134,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
                 make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
           }
         }
+    }
     if constexpr (!LAST) {
       // the next high part (the operand of the next step), rows of the tile
       stage16(F16);  // rounds each value to the operand format, as split does

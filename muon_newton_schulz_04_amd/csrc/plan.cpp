@@ -218,7 +218,6 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
   if (!any) P.ws_bytes = 0;
 
   // Work items and their costs, per kernel.
-  double total_cost[MUON_K_COUNT] = {0, 0, 0, 0, 0};
   std::vector<std::vector<std::vector<WorkItem>>> per(MUON_K_COUNT,
                                                       std::vector<std::vector<WorkItem>>(n));
   std::vector<std::vector<std::vector<double>>> cost(MUON_K_COUNT,
@@ -258,17 +257,59 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
         per[MUON_K_UPDATE][i].push_back({i, ti, tj, 0});
         cost[MUON_K_UPDATE][i].push_back(area * I.mp);
       }
-    for (int k = 0; k < MUON_K_COUNT; ++k)
-      for (double c : cost[k][i]) total_cost[k] += c;
   }
-  for (int k = 0; k < MUON_K_COUNT; ++k) {
-    // chunks no larger than 1/32 of the total keep the XCD bins balanced even
-    // for sets with a few large matrices
-    const double max_cost = std::max(total_cost[k] / (4.0 * kNumXcd), 1.0);
+  // Groups: matrices by update cost, longest first, onto the lighter group.
+  int64_t upd_tiles = 0;
+  for (int32_t i = 0; i < n; ++i) upd_tiles += static_cast<int64_t>(per[MUON_K_UPDATE][i].size());
+  int32_t nonempty = 0;
+  for (int32_t i = 0; i < n; ++i) nonempty += P.info[i].m > 0;
+  P.ngroups = (upd_tiles >= kGroupMinTiles && nonempty >= 2) ? kMaxGroups : 1;
+  std::vector<int32_t> group(n, 0);
+  if (P.ngroups > 1) {
+    std::vector<int32_t> order(n);
+    std::iota(order.begin(), order.end(), 0);
+    auto work = [&](int32_t i) {
+      double w = 0;
+      for (int k = 0; k < MUON_K_COUNT; ++k)
+        for (double c : cost[k][i]) w += k >= MUON_K_GRAM ? c : 0.0;
+      return w;
+    };
+    std::vector<double> wi(n);
+    for (int32_t i = 0; i < n; ++i) wi[i] = work(i);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return wi[x] > wi[y]; });
+    std::vector<double> load(P.ngroups, 0.0);
+    for (int32_t i : order) {
+      int best = 0;
+      for (int g = 1; g < P.ngroups; ++g)
+        if (load[g] < load[best]) best = g;
+      group[i] = best;
+      load[best] += wi[i];
+    }
+  }
+  // Schedules of the matrices with group[i] == g (g < 0: all of them).
+  auto schedule_of = [&](int k, int g, double share) {
+    double gtotal = 0;
+    for (int32_t i = 0; i < n; ++i)
+      if (g < 0 || group[i] == g)
+        for (double c : cost[k][i]) gtotal += c;
+    // chunks no larger than 1/32 of the set's total keep the XCD bins
+    // balanced even for sets with a few large matrices
+    const double max_cost = std::max(gtotal / share / (4.0 * kNumXcd), 1.0);
     std::vector<Chunk> chunks;
     for (int32_t i = 0; i < n; ++i)
-      if (!per[k][i].empty()) add_matrix_chunks(chunks, i, per[k][i], cost[k][i], max_cost);
-    P.sched[k] = assign_xcd(std::move(chunks));
+      if ((g < 0 || group[i] == g) && !per[k][i].empty())
+        add_matrix_chunks(chunks, i, per[k][i], cost[k][i], max_cost);
+    return assign_xcd(std::move(chunks));
+  };
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    P.sched[k].items.clear();
+    for (int g = 0; g < P.ngroups; ++g) {
+      P.gbeg[g][k] = static_cast<int32_t>(P.sched[k].items.size());
+      const Schedule s = schedule_of(k, g, 1.0 / P.ngroups);
+      P.sched[k].items.insert(P.sched[k].items.end(), s.items.begin(), s.items.end());
+    }
+    P.gbeg[P.ngroups][k] = static_cast<int32_t>(P.sched[k].items.size());
+    P.whole[k] = P.ngroups == 1 ? P.sched[k] : schedule_of(k, -1, 1.0);
   }
   *out = std::move(P);
   return MUON_OK;

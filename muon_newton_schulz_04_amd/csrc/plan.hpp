@@ -52,11 +52,27 @@ struct Schedule {
   std::vector<WorkItem> items;  // launch order; block i runs items[i]; mat < 0 = empty
 };
 
+// Large sets are split into groups of matrices that run concurrently on
+// streams of their own, so one group's kernels fill the CUs that the other
+// group's tail (the last, partial wave of tiles) and launch gaps leave idle.
+#ifndef MUON_MAX_GROUPS
+#define MUON_MAX_GROUPS 2
+#endif
+constexpr int kMaxGroups = MUON_MAX_GROUPS;
+constexpr int kGroupMinTiles = 512;  // matrix-core tiles per update launch to split
+
 struct HostPlan {
   muon_dtype dtype = MUON_BF16;
   std::vector<muon_matrix> mats;
   std::vector<MatInfo> info;
+  // Schedules of all groups, concatenated: group g's items of kernel k are
+  // sched[k].items[gbeg[g][k] .. gbeg[g + 1][k]) (each a multiple of 8).
   Schedule sched[MUON_K_COUNT];
+  int32_t ngroups = 1;
+  int32_t gbeg[kMaxGroups + 1][MUON_K_COUNT] = {};
+  // The same work as one group (per-kernel timing runs each kernel over the
+  // whole set in one launch).
+  Schedule whole[MUON_K_COUNT];
   int32_t total_partials = 0;
   size_t ws_bytes = 0;
 };

@@ -196,6 +196,32 @@ def test_deterministic_odd_and_scale_invariant(dtype):
         assert rel(s, a) < (1e-5 if dtype == "fp32" else 5e-3)
 
 
+def test_grouped_concurrent_run_matches_timed_whole_set_run():
+    """Large sets run as concurrent groups; with per-kernel timing on, every
+    kernel runs over the whole set in one launch. Same kernels, same tiles:
+    the results must be bitwise equal (momentum buffers included)."""
+    wl = CONFIGS["gpt2_124m_matrix_set"]
+    grads = [g.to(DEV) for g in make_gradients(wl, step=9)]
+    res = []
+    for timing in (False, True):
+        bufs = [torch.zeros_like(g) for g in grads]
+        outs = [torch.empty_like(g) for g in grads]
+        plan = mu.MuonPlan(grads, bufs, outs)
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+        cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
+        plan.set_timing(timing)
+        for _ in range(2):
+            plan.step(cfg, ws)
+        torch.cuda.synchronize()
+        if timing:
+            ms, n = plan.kernel_times()["update"]
+            assert n == 2 * wl.steps and ms > 0
+        res.append(([o.clone() for o in outs], [b.clone() for b in bufs]))
+        plan.destroy()
+    for a, b in zip(res[0][0] + res[0][1], res[1][0] + res[1][1]):
+        assert torch.equal(a, b)
+
+
 def test_zero_matrix_empty_matrix_and_aliasing():
     g = [torch.zeros(130, 70, dtype=torch.bfloat16, device=DEV),
          torch.empty(0, 64, dtype=torch.bfloat16, device=DEV),
