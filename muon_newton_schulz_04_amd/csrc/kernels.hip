@@ -350,18 +350,49 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
         wlo[q] = l0 | (l1 << 16);
       }
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = whi;
-      uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
-      if constexpr (OP == OP_F16) {  // two runs of 4 in accumulator order
-        const int m = i0 + (v >> 3), n = j0 + (v & 7) * 8;
-        *reinterpret_cast<uint2*>(lo + lo_index(m, n, M.np)) = make_uint2(wlo[0], wlo[1]);
-        *reinterpret_cast<uint2*>(lo + lo_index(m, n + 4, M.np)) = make_uint2(wlo[2], wlo[3]);
-      } else {
+      if constexpr (OP != OP_F16) {
+        uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
         *reinterpret_cast<u32x4_t*>(lo + off) = wlo;
       }
     } else {
       float* x0 = reinterpret_cast<float*>(A.ws + M.xo_off[0]) + off;
       reinterpret_cast<f32x4_t*>(x0)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
       reinterpret_cast<f32x4_t*>(x0)[1] = f32x4_t{u[h][4], u[h][5], u[h][6], u[h][7]};
+    }
+  }
+  if constexpr (OP == OP_F16) {
+    // Low part in accumulator order. A 32-row x 64-column block (this tile
+    // holds two) is one contiguous 4 KB run of that layout; thread t writes
+    // its bytes 16 t .. 16 t + 15, which hold columns 32 j + 8 g + 4 h .. +3
+    // (q = j * 4 + g = t / 32, h = lane bit 5) of rows 2 t % 32 and the next.
+    __syncthreads();  // the tall path above has finished reading the tile
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[v >> 3][(v & 7) * 8 + e] = u[h][e];
+    }
+    __syncthreads();
+    uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
+    const int t = threadIdx.x, q = t >> 5, lane0 = (2 * t) & 63;
+    const int col = 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane0 >> 5);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uint32_t w[4];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int row = 32 * b + ((lane0 + d) & 31);
+        uint32_t l[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t hh;
+          Op<OP>::split(tile[row][col + r], hh, l[r]);
+        }
+        w[2 * d] = l[0] | (l[1] << 16);
+        w[2 * d + 1] = l[2] | (l[3] << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(lo + lo_index(i0 + 32 * b, j0, M.np) + 8 * t) =
+          u32x4_t{w[0], w[1], w[2], w[3]};
     }
   }
 }
