@@ -195,15 +195,18 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
 /* Workspace layout of matrix `idx` of a plan (byte offsets from the
  * workspace base; -1 where a buffer does not exist). All buffers use the
  * rows<=cols orientation, zero-padded to mp x np (X) or mp x mp (A, B),
- * row-major, with mp and np the tile multiples (256 for bf16 sets, 128 for
- * fp32 sets). bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
+ * with mp and np the tile multiples (256 for bf16 sets, 128 for fp32
+ * sets). bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
  * matrix-core operand, ping-pong between steps) and x_lo the low part in
  * the same format (X = hi + lo * 2^-11 for fp16 operands, hi + lo for bf16
- * operands); gram (A) and poly are 16-bit. With fp16 operands poly holds
- * a I + B (the a X term of the high part rides in the product) and x_lo is
- * stored in the update kernel's accumulator order rather than row-major.
- * fp32 sets: x_op0/x_op1 are fp32 X (ping-pong), gram/poly (B) fp32,
- * x_lo = -1. After a step of k iterations X is in x_op[k % 2]. */
+ * operands); gram (A) and poly are 16-bit. The three 16-bit operands
+ * (x_op0/x_op1, gram, poly) are stored in 32-column panels: element (r, c)
+ * is at element index ((c / 32) * mp + r) * 32 + c % 32. With fp16
+ * operands poly holds a I + B (the a X term of the high part rides in the
+ * product) and x_lo is stored in the update kernel's accumulator order;
+ * with bf16 operands x_lo is row-major. fp32 sets: x_op0/x_op1 are fp32 X
+ * (ping-pong), gram/poly (B) fp32, all row-major, x_lo = -1. After a step
+ * of k iterations X is in x_op[k % 2]. */
 typedef struct {
   int64_t m, n, mp, np;
   int64_t x_lo, x_op0, x_op1, gram, poly;

@@ -139,6 +139,17 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
+// The 16-bit matrix-core operands of bf16 sets (X's high part, A and B) are
+// stored in 32-column panels: panel p holds columns 32 p .. 32 p + 31 of
+// every row, 64 bytes per row, rows consecutive. Element (r, c) of a matrix
+// with `rows` (padded) rows is at this element index. A 32-k stage of 256
+// rows is then one contiguous 16 KB run, and 32 k-rows of a column block are
+// whole 128-byte lines, so every LDS DMA request of the engine is a full
+// cache line.
+__device__ __forceinline__ int64_t pidx(int r, int c, int rows) {
+  return (int64_t(c >> 5) * rows + r) * 32 + (c & 31);
+}
+
 // Offset of operand buffer `which` (0/1) without indexing the record's
 // array by a run-time value (which would move the record to scratch).
 __device__ __forceinline__ int64_t xo_sel(const MatInfo& M, int which) {
@@ -340,6 +351,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
     const int v = threadIdx.x + 256 * h;
     const int64_t off = int64_t(i0 + (v >> 3)) * M.np + j0 + (v & 7) * 8;
     if constexpr (OP != OP_F32) {
+      const int64_t poff = pidx(i0 + (v >> 3), j0 + (v & 7) * 8, M.mp);
       u32x4_t whi, wlo;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -349,7 +361,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
         whi[q] = h0 | (h1 << 16);
         wlo[q] = l0 | (l1 << 16);
       }
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + off) = whi;
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + poff) = whi;
       if constexpr (OP != OP_F16) {
         uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
         *reinterpret_cast<u32x4_t*>(lo + off) = wlo;
@@ -693,7 +705,10 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int KS = 32;                 // k per stage
 // Ring depth: 256 x 256 tiles run one workgroup per CU with four 32 KB
 // stages; 256 x 128 tiles run two per CU with three 24 KB stages each.
-constexpr int NS = TN == 256 ? 4 : 3;
+#ifndef MUON_RING_STAGES
+#define MUON_RING_STAGES (kTileN16 == 256 ? 4 : 3)
+#endif
+constexpr int NS = MUON_RING_STAGES;
 constexpr int WG_PER_CU = TN == 256 ? 1 : 2;
 constexpr int HALF_A = TM * KS * 2;    // row operand of one stage: 16 KB
 constexpr int HALF_B = TN * KS * 2;    // column operand of one stage
@@ -742,42 +757,43 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       : "memory", "m0");
 }
 
-// Issues this wave's share of the DMA of one stage (pieces of 1 KB: 16 of
-// the row operand, TN/16 of the column operand): rows of the row operand at
-// opA + row * lda (bytes), k0 .. k0+31; the column operand either the same
-// way from opB, or k-rows k0 .. k0+31 of TN columns at opB + k * ldb.
-#ifndef MUON_DMA_WAVES
-#define MUON_DMA_WAVES 0
+// DMA of one stage in pieces of 1 KB: 16 of the row operand, TN/16 of the
+// column operand. Operands are in 32-column panels (pidx) and lda / ldb are
+// panel strides in bytes: a row operand's stage (256 rows at opA, k0 ..
+// k0+31) is panel k0/32, 16 KB contiguous; the column operand is either the
+// same (opB) or k-rows k0 .. k0+31 of TN columns (TN/32 panels from opB,
+// 64 bytes per k-row in each). Wave w issues pieces w, w + NWAVE, ...; its
+// q-th piece is dma_piece(q).
+constexpr int DMA_PER_STAGE = (16 + TN / 16) / NWAVE;  // pieces per wave per stage
+#ifndef MUON_SPLIT_DMA
+#define MUON_SPLIT_DMA 1
 #endif
-// Waves that issue the DMA: all (0), the first half (1) or the second half (2).
-constexpr int NDW = MUON_DMA_WAVES == 0 ? NWAVE : NWAVE / 2;
-constexpr int DW0 = MUON_DMA_WAVES == 2 ? NWAVE / 2 : 0;
-constexpr int DMA_PER_STAGE = (16 + TN / 16) / NDW;  // pieces per issuing wave per stage
+constexpr bool SPLIT_DMA = MUON_SPLIT_DMA;
+template <bool KN>
+__device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda, const char* opB,
+                                          int64_t ldb, int64_t k0, int q) {
+  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+  constexpr int QA = 16 / NWAVE;  // row-operand pieces per wave
+  const int I = w + NWAVE * (q < QA ? q : q - QA);
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + (q < QA ? 0 : HALF_A) + I * 1024);
+  if (q < QA) {
+    const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    dma16(opA + (k0 >> 5) * lda + row * 64 + g * 16, dst);
+  } else if constexpr (!KN) {
+    const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    dma16(opB + (k0 >> 5) * ldb + row * 64 + g * 16, dst);
+  } else {
+    constexpr int RPP = 1024 / KROW;  // k-rows per piece
+    const int kr = RPP * I + i / (64 / RPP), g = (i % (64 / RPP)) ^ ((kr & 3) << 2);
+    dma16(opB + (g >> 2) * ldb + (k0 + kr) * 64 + (g & 3) * 16, dst);
+  }
+}
 template <bool KN>
 __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0) {
-  const int w = (threadIdx.x >> 6) - DW0, i = threadIdx.x & 63;
-  if (NDW != NWAVE && (w < 0 || w >= NDW)) return;
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + (w << 10));
 #pragma unroll
-  for (int q = 0; q < 16 / NDW; ++q) {
-    const int I = w + NDW * q;  // piece of the row operand
-    const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    dma16(opA + row * lda + k0 * 2 + g * 16, base + q * NDW * 1024);
-  }
-#pragma unroll
-  for (int q = 0; q < TN / 16 / NDW; ++q) {
-    const int I = w + NDW * q;  // piece of the column operand
-    if constexpr (!KN) {
-      const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-      dma16(opB + row * ldb + k0 * 2 + g * 16, base + HALF_A + q * NDW * 1024);
-    } else {
-      constexpr int RPP = 1024 / KROW;  // k-rows per piece
-      const int kr = RPP * I + i / (64 / RPP), g = (i % (64 / RPP)) ^ ((kr & 3) << 2);
-      dma16(opB + (k0 + kr) * ldb + g * 16, base + HALF_A + q * NDW * 1024);
-    }
-  }
+  for (int q = 0; q < DMA_PER_STAGE; ++q) dma_piece<KN>(st, opA, lda, opB, ldb, k0, q);
 }
 
 template <int OP>
@@ -796,36 +812,40 @@ struct Frag {
   u32x4 b[2];  // column operand: columns wn*64 + 32 j + l%32
 };
 
-// Reads the fragments of k-step ks (0/1) of the stage at `st`; the reads
-// stay in flight until the MFMAs that use them.
+// Fragment reads of k-step ks (0/1) of the stage at `st`: row-operand block
+// i, column-operand block j. The reads stay in flight until the MFMAs that
+// use them.
+__device__ __forceinline__ void frag_load_a(Frag& f, const char* st, int ks, int wm, int i) {
+  const int lane = threadIdx.x & 63;
+  const int ch = ks * 2 + (lane >> 5);  // 16-byte k chunk of this lane half
+  f.a[i] = *reinterpret_cast<const u32x4*>(st + off_r(wm * 128 + i * 32 + (lane & 31), ch));
+}
 template <bool KN>
-__device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int wm, int wn) {
-  const char* sA = st;
+__device__ __forceinline__ void frag_load_b(Frag& f, const char* st, int ks, int wn, int j) {
   const char* sB = st + HALF_A;
-  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
-  const int ch = ks * 2 + lh;  // 16-byte k chunk of this lane half
+  const int lane = threadIdx.x & 63;
   if constexpr (KN) {
     const int s = lane & 15, h = lane >> 4;  // 16-lane group h
     const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
-      const int chunk = col >> 3, byte = (col & 7) * 2;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_t*)(sB + off_k(krow, chunk) + byte));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_t*)(sB + off_k(krow + 4, chunk) + byte));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      f.b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-    }
+    const int col = wn * 64 + j * 32 + (h & 1) * 16 + 4 * (s & 3);
+    const int chunk = col >> 3, byte = (col & 7) * 2;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(sB + off_k(krow, chunk) + byte));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(sB + off_k(krow + 4, chunk) + byte));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    f.b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
   } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      f.b[j] = *reinterpret_cast<const u32x4*>(sB + off_r(wn * 64 + j * 32 + l32, ch));
+    const int ch = ks * 2 + (lane >> 5);
+    f.b[j] = *reinterpret_cast<const u32x4*>(sB + off_r(wn * 64 + j * 32 + (lane & 31), ch));
   }
+}
+template <bool KN>
+__device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int wm, int wn) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const u32x4*>(sA + off_r(wm * 128 + i * 32 + l32, ch));
+  for (int j = 0; j < 2; ++j) frag_load_b<KN>(f, st, ks, wn, j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) frag_load_a(f, st, ks, wm, i);
 }
 
 // Scheduling hint for a region holding one k-step of MFMAs (8) and the LDS
@@ -837,6 +857,43 @@ __device__ __forceinline__ void interleave_mma_reads() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
+}
+
+// One k-step with DMA spread over it: the 8 MFMAs of fragment set fm, the
+// LDS reads of fragment set fl (k-step ks of the stage at `st`) and NCH DMA
+// pieces, dma(c) at the start of chunk c. Each chunk takes 4 / NCH row
+// blocks of MFMAs with their share of the reads, so a wave never has more
+// than one DMA in front of its next MFMAs and the address unit drains
+// between the chunks.
+template <int OP, bool KN, int NCH, typename D>
+__device__ __forceinline__ void kstep_dma(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
+                                          const char* st, int ks, int wm, int wn, D&& dma) {
+  static_assert(4 % NCH == 0, "row blocks per chunk");
+  constexpr int IPC = 4 / NCH;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    dma(c);
+#pragma unroll
+    for (int ii = 0; ii < IPC; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[c * IPC + ii][j] = mfma<OP>(fm.b[j], fm.a[c * IPC + ii], acc[c * IPC + ii][j]);
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) frag_load_b<KN>(fl, st, ks, wn, j);
+    }
+#pragma unroll
+    for (int ii = 0; ii < IPC; ++ii) frag_load_a(fl, st, ks, wm, c * IPC + ii);
+    constexpr int NM = 2 * IPC;
+    const int nr = IPC + (c == 0 ? (KN ? 4 : 2) : 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (k < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int OP>
@@ -859,8 +916,32 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
   return r;
 }
 
+// POLY: acc[i][J] += f A[m][n] at this lane's accumulator positions of
+// column block J, read from the row-operand half of the stage at `st`, which
+// holds A[m][k] for the 32 k that are these n (the caller picks the stage).
+template <int OP, int J>
+__device__ __forceinline__ void fold_bias(f32x16_t (&acc)[4][2], const char* st, int wm, float f) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x2 v[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      v[g] = *reinterpret_cast<const u32x2*>(st + off_r(wm * 128 + 32 * i + l32, g) + lh * 8);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t w[4] = {v[g].x & 0xffffu, v[g].x >> 16, v[g].y & 0xffffu, v[g].y >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[i][J][4 * g + r] = __fmaf_rn(f, Op<OP>::load16(w[r]), acc[i][J][4 * g + r]);
+    }
+  }
+}
+
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
 #define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+
 
 }  // namespace e16
 
@@ -893,27 +974,25 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   const char* opA;
   const char* opB;
   int64_t lda, ldb, K;
+  // Every operand has mp rows, so one panel stride serves both.
+  lda = ldb = int64_t(M.mp) * 64;
   if (KIND == GRAM) {
     const char* X = P.ws + M.xo_cur;
-    lda = ldb = int64_t(M.np) * 2;
-    opA = X + int64_t(TI) * TM * lda;
-    opB = X + int64_t(TJ) * TN * ldb;
+    opA = X + int64_t(TI) * TM * 64;
+    opB = X + int64_t(TJ) * TN * 64;
     K = M.np;
   } else if (KIND == POLY) {
     const char* Am = P.ws + M.a_off;
-    lda = ldb = int64_t(M.mp) * 2;
-    opA = Am + int64_t(TI) * TM * lda;
-    opB = Am + int64_t(TJ) * TN * ldb;
+    opA = Am + int64_t(TI) * TM * 64;
+    opB = Am + int64_t(TJ) * TN * 64;
     K = M.mp;
   } else {
-    lda = int64_t(M.mp) * 2;
-    ldb = int64_t(M.np) * 2;
-    opA = P.ws + M.b_off + int64_t(TI) * TM * lda;
-    opB = P.ws + M.xo_cur + int64_t(TJ) * TN * 2;
+    opA = P.ws + M.b_off + int64_t(TI) * TM * 64;
+    opB = P.ws + M.xo_cur + int64_t(TJ) * (TN / 32) * ldb;
     K = M.mp;
   }
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave / WN, wn = wave % WN;
   f32x16_t acc[4][2];
 #pragma unroll
@@ -931,34 +1010,82 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   // Every pass issues one stage, so the wait count is the same in every pass;
   // past the end the DMA repeats the last stage (valid addresses, unused).
   const int nst = static_cast<int>(K / KS);
+  const bool fold = KIND == POLY && P.c != 0.f;
+  constexpr bool SPLIT = SPLIT_DMA && NS >= 4 && DMA_PER_STAGE % 2 == 0 && 4 % (DMA_PER_STAGE / 2) == 0;
+  constexpr int H = DMA_PER_STAGE / 2;  // pieces per k-step (split issue)
+  if constexpr (SPLIT) {
+    // stages 0 .. NS-3 and the first half of stage NS-2 (its second half
+    // goes out with the first k-step of stage 0)
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
-  MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 2));  // stage 0 landed (this wave's pieces)
+    for (int p = 0; p < NS - 2; ++p) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+#pragma unroll
+    for (int q = 0; q < H; ++q)
+      dma_piece<KN>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
+    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
+  } else {
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 2));  // stage 0 landed (this wave's pieces)
+  }
   asm volatile("s_barrier" ::: "memory");
+  // POLY with c != 0 folds the b A term into the accumulators on the way:
+  // acc = A A + (b / c) A, and the epilogue scales by c. Column n of this
+  // wave's block j is k = n of the row operand, which is in stage
+  // bias0 + j (the A tile of rows TI and columns TJ passes through LDS).
+  const int bias0 = fold ? TJ * (TN / KS) + wn * (64 / KS) : -2;
+  const float fb = fold ? P.b / P.c : 0.f;
   Frag f0, f1;
   frag_load<KN>(f0, lds, 0, wm, wn);
   int cur = 0;  // ring slot of stage g
   for (int g = 0; g < nst; ++g) {
     const int nxt = cur == NS - 1 ? 0 : cur + 1;  // slot of stage g+1
     const int old = cur == 0 ? NS - 1 : cur - 1;  // slot of stage g-1 (unused for g = 0)
-    __builtin_amdgcn_sched_barrier(0);
-    frag_mma<OP>(acc, f0);
-    frag_load<KN>(f1, lds + cur * STAGE, 1, wm, wn);
-    interleave_mma_reads();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SPLIT) {
+      // second half of stage g+NS-2 (its slot was freed at the previous
+      // barrier; the first half went out then)
+      const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
+      const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
+      kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, [&](int c) {
+        dma_piece<KN>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
+      });
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      frag_mma<OP>(acc, f0);
+      frag_load<KN>(f1, lds + cur * STAGE, 1, wm, wn);
+      interleave_mma_reads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // This wave's pieces of stage g+1 have landed (stages up to g+NS-2 may
     // still be in flight). A bare s_barrier: the workgroup fence of
     // __syncthreads would also wait for those; the memory clobber keeps the
     // compiler from moving LDS accesses across it.
     MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3));
     asm volatile("s_barrier" ::: "memory");
-    // every wave has finished reading stage g-1: refill its slot
-    dma_stage<KN>(lds + old * STAGE, opA, lda, opB, ldb, int64_t(min(g + NS - 1, nst - 1)) * KS);
-    __builtin_amdgcn_sched_barrier(0);
-    frag_mma<OP>(acc, f1);
-    // (after the last stage this reads a stale slot; the values are unused)
-    frag_load<KN>(f0, lds + nxt * STAGE, 0, wm, wn);
-    interleave_mma_reads();
+    // every wave has finished reading stage g-1: refill its slot (with the
+    // split issue, the first half of stage g+NS-1 now and the second half
+    // with the next k-step)
+    // (after the last stage the fragment reads come from a stale slot; the
+    // values are unused)
+    if constexpr (SPLIT) {
+      const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
+      kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, [&](int c) {
+        dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
+      });
+    } else {
+      dma_stage<KN>(lds + old * STAGE, opA, lda, opB, ldb, int64_t(min(g + NS - 1, nst - 1)) * KS);
+      __builtin_amdgcn_sched_barrier(0);
+      frag_mma<OP>(acc, f1);
+      frag_load<KN>(f0, lds + nxt * STAGE, 0, wm, wn);
+      interleave_mma_reads();
+    }
+    if constexpr (KIND == POLY) {
+      // (stage g stays in its slot until every wave has passed the next
+      // barrier)
+      __builtin_amdgcn_sched_barrier(0);
+      const int jb = g - bias0;
+      if (jb == 0) fold_bias<OP, 0>(acc, lds + cur * STAGE, wm, fb);
+      else if (jb == 1) fold_bias<OP, 1>(acc, lds + cur * STAGE, wm, fb);
+    }
     cur = nxt;
   }
   MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
@@ -1031,11 +1158,31 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
 
   if constexpr (KIND == GRAM || KIND == POLY) {
     char* C = P.ws + (KIND == GRAM ? M.a_off : M.b_off);
-    const int64_t ld = M.mp;
+    const int mp = M.mp;
     const bool strict = TJ * TN >= (TI + 1) * TM;  // every element above the diagonal
     if constexpr (KIND == POLY) {
       // B = c (A A) + b A (+ a I for fp16 operands, so that the update is
-      // B' X). The A tile goes into the staging layout by DMA (whole rows,
+      // B' X).
+      if (fold) {
+        // acc = A A + (b / c) A already
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float v = P.c * acc[i][j][4 * g + r];
+                if constexpr (OP == OP_F16) {
+                  const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh + r;
+                  if (m == n && m < M.m) v += P.a;  // padding stays zero
+                }
+                acc[i][j][4 * g + r] = v;
+              }
+        stage16(F16);
+      } else {
+      // c = 0: the A tile goes into the staging layout by DMA (whole rows,
       // coalesced); each lane then reads its accumulator positions, combines
       // and writes the result back to the same positions (no other lane
       // touches them, so no barrier is needed in between).
@@ -1049,7 +1196,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
         const int x = ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
         const uint32_t base = __builtin_amdgcn_readfirstlane(
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + I * 1024);
-        e16::dma16(Am + (int64_t(m0 + r) * ld + n0 + 8 * (sl ^ x)) * 2, base);
+        e16::dma16(Am + pidx(m0 + r, n0 + 8 * (sl ^ x), mp) * 2, base);
       }
       MUON_WAIT_VMCNT(0);
       __syncthreads();
@@ -1073,13 +1220,14 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
             }
             *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], F16);
           }
+      }
     } else {
       stage16(F16);
     }
     __syncthreads();
     // C[m][n..n+7] where m <= n
     rows_out([&](int m, int n, const uint4& v) {
-      uint16_t* d = reinterpret_cast<uint16_t*>(C) + int64_t(m) * ld + n;
+      uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(m, n, mp);
       if (strict || m <= n) {
         *reinterpret_cast<uint4*>(d) = v;
       } else {
@@ -1090,7 +1238,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     });
     // mirror: C[n][m..m+7] = C[m..m+7][n] where m < n
     cols_out([&](int n, int m, const uint4& v) {
-      uint16_t* d = reinterpret_cast<uint16_t*>(C) + int64_t(n) * ld + m;
+      uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(n, m, mp);
       if (strict || m + 7 < n) {
         *reinterpret_cast<uint4*>(d) = v;
       } else {
@@ -1135,7 +1283,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
           for (int g = 0; g < 4; ++g) {
             lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
             hv[j][g] = *reinterpret_cast<const u32x2*>(
-                hi_cur + int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh);
+                hi_cur + pidx(mb + 32 * i + l32, nb + 32 * j + 8 * g + 4 * lh, M.mp));
           }
       }
 #pragma unroll
@@ -1172,7 +1320,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
       __syncthreads();
       uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
       rows_out([&](int m, int n, const uint4& v) {
-        *reinterpret_cast<uint4*>(xn + int64_t(m) * ldx + n) = v;
+        *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
       });
     } else {
       // `out` in the caller's layout (bf16), transposed for tall matrices

@@ -151,6 +151,12 @@ def test_plain_momentum_and_no_momentum(dtype):
 
 # ------------------------------------------------------------ GPU invariants
 
+def unpanel(flat, rows, cols):
+    """Row-major view of a 16-bit operand stored in 32-column panels
+    (element (r, c) at ((c // 32) * rows + r) * 32 + c % 32)."""
+    return flat.view(cols // 32, rows, 32).permute(1, 0, 2).reshape(rows, cols)
+
+
 def test_gram_is_bitwise_symmetric_and_padding_zero():
     shapes = [(200, 333), (333, 200), (256, 512)]
     grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=5, shapes=shapes)]
@@ -163,12 +169,12 @@ def test_gram_is_bitwise_symmetric_and_padding_zero():
         mp, m = info["mp"], info["m"]
         for key in ("gram", "poly"):
             off = info[key]
-            A = ws[off: off + mp * mp * 2].view(torch.float16).view(mp, mp).float().cpu()
+            A = unpanel(ws[off: off + mp * mp * 2].view(torch.float16), mp, mp).float().cpu()
             assert torch.equal(A, A.t()), key
             assert torch.count_nonzero(A[m:, :]) == 0 and torch.count_nonzero(A[:, m:]) == 0
         # trace(A) = ||X0||_F^2 = (||u|| / (||u|| + eps))^2 ~ 1
         off = info["gram"]
-        A = ws[off: off + mp * mp * 2].view(torch.float16).view(mp, mp).double().cpu()
+        A = unpanel(ws[off: off + mp * mp * 2].view(torch.float16), mp, mp).double().cpu()
         assert abs(float(torch.trace(A)) - 1.0) < 1e-2
     plan.destroy()
 
