@@ -204,6 +204,36 @@ def main():
     kt = plan.kernel_times()
     plan.set_timing(False)
 
+    # the next row beside the path: the same step with the weight application
+    # fused into the last update (W read and written instead of out written)
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    weights = [(0.02 * torch.randn(g.shape, generator=gen)).to(g.dtype).to(dev) for g in grads]
+    plan.set_weights(weights)
+    n_apply = max(5, args.steps // 5)
+
+    def block(fn):  # mean ms of n_apply calls, events on the step's stream
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(n_apply):
+            fn()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / n_apply
+
+    def plain():
+        plan.step(cfg, ws, stream)
+
+    def fused():
+        plan.step_apply(cfg, 1e-3, 0.1, ws, stream)
+
+    fused()
+    plain()
+    torch.cuda.synchronize()
+    pairs = [(block(plain), block(fused)) for _ in range(3)]  # alternating blocks
+    ms_plain_b = float(np.median([p for p, _ in pairs]))
+    ms_apply = float(np.median([f for _, f in pairs]))
+    del weights
+
     falg = wl.falg_flops()
     value = falg / (ms * 1e-3) / 1e12
     work = kernel_work(wl.shapes, wl.steps, wl.dtype)
@@ -249,6 +279,11 @@ def main():
         "wall_s_timed": wall,
         "kernels": per_kernel,
         "roofline": roof,
+        "next": {"weight_apply": {
+            "ms_per_step": ms_apply, "steps": 3 * n_apply,
+            "plain_ms_per_step_same_blocks": ms_plain_b,
+            "extra_us_vs_plain_step": (ms_apply - ms_plain_b) * 1e3,
+            "note": "muon_plan_step_apply: W <- W(1 - lr wd) - lr X fused into the last update"}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

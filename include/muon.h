@@ -151,6 +151,54 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
                                const muon_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* ---- weight application fused into the last update ---------------------
+ *
+ * The step after the orthogonalised update: the weight matrix W of each
+ * parameter moves against it with decoupled weight decay,
+ *
+ *   W <- W * (1 - lr * wd * wd_mul) - lr * lr_mul * X
+ *
+ * where X is the Muon result (what muon_plan_step writes to `out`), lr and wd
+ * are per call and lr_mul, wd_mul per matrix (mhpq.cn, modded-nanogpt
+ * track_1_short technical guide, section 6.2, training hyper-parameters:
+ * every parameter group carries its own lr and weight-decay multipliers;
+ * yongjin360.com, Modded-NanoGPT green-AI article, hyper-parameter
+ * paragraph: weight decay is part of the recipe). The pages give no
+ * learning-rate schedule or shape rule, so all four scalars come from the
+ * caller. The product runs in fp32 on X before any rounding to the set's
+ * dtype (the 16-bit path stages X as fp16 first), and W' is stored at the
+ * set's dtype, round to nearest even. */
+
+/* W of matrix i of a plan: same rows, cols and dtype as its grad,
+ * row-major with leading dimension ld >= cols, aligned to the element size.
+ * W must not overlap any grad, momentum, out or other W of the set. */
+typedef struct {
+  void* weight;
+  int64_t ld;
+  float lr_mul;
+  float wd_mul;
+} muon_weight;
+
+/* Per-call scalars of a weight application; both finite. */
+typedef struct {
+  float lr;
+  float wd;
+} muon_apply;
+
+/* Attaches the weights to a plan: w[i] for matrix i, n must equal the
+ * plan's matrix count (records of empty matrices are ignored, their weight
+ * may be NULL). Waits for the device, then updates the plan's device table
+ * (do not call while work of this plan is in flight on another thread).
+ * On error the plan keeps its previous weights. */
+muon_status muon_plan_set_weights(muon_plan* plan, const muon_weight* w, int32_t n);
+
+/* muon_plan_step, except that the last update writes W' (above) into each
+ * matrix's weight instead of writing `out` (which is left untouched); with
+ * cfg->steps == 0 the normalised X0 is applied. MUON_E_INVALID if the plan
+ * has no weights. Momentum buffers are updated as in muon_plan_step. */
+muon_status muon_plan_step_apply(muon_plan* plan, const muon_config* cfg, const muon_apply* ap,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- introspection (tests, benchmarks, profiling) ---------------------- */
 
 /* Kernels of one step, in launch order: momentum, normalise, then per

@@ -19,6 +19,7 @@ __all__ = [
     "muon_workspace_bytes", "muon_plan_create", "muon_plan_step", "muon_plan_destroy",
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
+    "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
     "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT", "MUON_PRECISION_BF16_OPERANDS",
 ]
 
@@ -46,6 +47,15 @@ class MuonConfig(ctypes.Structure):
                 ("steps", ctypes.c_int32), ("momentum", ctypes.c_float),
                 ("nesterov", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("precision", ctypes.c_int32)]
+
+
+class MuonWeight(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("ld", ctypes.c_int64),
+                ("lr_mul", ctypes.c_float), ("wd_mul", ctypes.c_float)]
+
+
+class MuonApply(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("wd", ctypes.c_float)]
 
 
 class MuonBufferInfo(ctypes.Structure):
@@ -80,6 +90,8 @@ def load_library(path: str = LIB_PATH):
         "muon_plan_set_timing": (i32, [vp, i32]),
         "muon_plan_kernel_times": (i32, [vp, P(ctypes.c_double), P(i64)]),
         "muon_plan_buffer_info": (i32, [vp, i32, P(MuonBufferInfo)]),
+        "muon_plan_set_weights": (i32, [vp, P(MuonWeight), i32]),
+        "muon_plan_step_apply": (i32, [vp, P(MuonConfig), P(MuonApply), vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -244,6 +256,37 @@ class MuonPlan:
                "muon_plan_step")
         return ws
 
+    def set_weights(self, weights, lr_mul=None, wd_mul=None):
+        """Attaches one weight tensor per matrix (same shape and dtype as its
+        grad, row-major); lr_mul / wd_mul: per-matrix multipliers (default 1)."""
+        n = self.n
+        if len(weights) != n:
+            raise ValueError("one weight per matrix")
+        lr_mul = [1.0] * n if lr_mul is None else list(lr_mul)
+        wd_mul = [1.0] * n if wd_mul is None else list(wd_mul)
+        arr = (MuonWeight * max(n, 1))()
+        grads = self._keep[0]
+        for i, w in enumerate(weights):
+            if w is None:
+                arr[i] = MuonWeight(None, 0, lr_mul[i], wd_mul[i])
+                continue
+            if w.shape != grads[i].shape or _dtype_code(w) != self.dtype:
+                raise ValueError("weight must match its grad's shape and dtype")
+            arr[i] = MuonWeight(_ptr(w), _ld(w), float(lr_mul[i]), float(wd_mul[i]))
+        _check(load_library().muon_plan_set_weights(self.handle, arr, n), "muon_plan_set_weights")
+        self._weights = list(weights)
+
+    def step_apply(self, cfg: MuonConfig, lr: float, wd: float, workspace=None, stream=None):
+        """One Muon update whose last step writes W <- W (1 - lr wd wd_mul) - lr lr_mul X
+        into the attached weights (``out`` is not written)."""
+        ws = _workspace(self.workspace_bytes, self.device, workspace)
+        ap = MuonApply(float(lr), float(wd))
+        _check(load_library().muon_plan_step_apply(self.handle, ctypes.byref(cfg), ctypes.byref(ap),
+                                                   ws.data_ptr(), ws.numel(),
+                                                   _stream_handle(stream)),
+               "muon_plan_step_apply")
+        return ws
+
     def set_timing(self, on: bool):
         _check(load_library().muon_plan_set_timing(self.handle, 1 if on else 0),
                "muon_plan_set_timing")
@@ -283,6 +326,15 @@ def muon_plan_step(plan: MuonPlan, cfg: MuonConfig, workspace=None, stream=None)
 
 def muon_plan_destroy(plan: MuonPlan):
     plan.destroy()
+
+
+def muon_plan_set_weights(plan: MuonPlan, weights, lr_mul=None, wd_mul=None):
+    plan.set_weights(weights, lr_mul, wd_mul)
+
+
+def muon_plan_step_apply(plan: MuonPlan, cfg: MuonConfig, lr: float, wd: float, workspace=None,
+                         stream=None):
+    return plan.step_apply(cfg, lr, wd, workspace, stream)
 
 
 def muon_plan_set_timing(plan: MuonPlan, on: bool):

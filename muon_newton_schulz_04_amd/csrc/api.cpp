@@ -39,6 +39,7 @@ struct muon_plan_s {
   std::vector<hipEvent_t> free_events;
   double acc_ms[MUON_K_COUNT] = {};
   int64_t acc_n[MUON_K_COUNT] = {};
+  bool has_weights = false;                   // muon_plan_set_weights succeeded
 };
 
 namespace {
@@ -129,7 +130,7 @@ hipEvent_t get_event(muon_plan_s* p) {
 }
 
 muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t ws_bytes,
-                      void* stream, bool orthogonalize_only) {
+                      void* stream, bool orthogonalize_only, const muon_apply* ap = nullptr) {
   if (p == nullptr) return MUON_E_INVALID;
   muon_status st = muon::validate_config(cfg);
   if (st != MUON_OK) return st;
@@ -157,6 +158,11 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.nesterov = cfg->nesterov;
   a.use_mom = use_mom ? 1 : 0;
   a.direct = cfg->steps == 0 ? 1 : 0;
+  if (ap) {
+    a.apply = 1;
+    a.lr = ap->lr;
+    a.wd = ap->wd;
+  }
 
   // One launch of kernel `kind` for group g on stream `q`.
   auto launch = [&](int kind, int g, hipStream_t q) -> muon_status {
@@ -330,6 +336,45 @@ muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtyp
 muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
                            size_t workspace_bytes, void* stream) {
   return step_impl(plan, cfg, workspace, workspace_bytes, stream, false);
+}
+
+muon_status muon_plan_set_weights(muon_plan* plan, const muon_weight* w, int32_t n) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  muon_status st = muon::validate_weights(plan->host, w, n);
+  if (st != MUON_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return MUON_E_DEVICE;
+  std::vector<MatInfo> info = plan->host.info;
+  const size_t es = muon::elem_size(plan->host.dtype);
+  for (int32_t i = 0; i < n; ++i) {
+    MatInfo& I = info[i];
+    if (I.m == 0) continue;
+    I.w = w[i].weight;
+    I.wld = w[i].ld;
+    I.lr_mul = w[i].lr_mul;
+    I.wd_mul = w[i].wd_mul;
+    I.w_vec_ok = reinterpret_cast<uintptr_t>(w[i].weight) % 16 == 0 && (w[i].ld * es) % 16 == 0 &&
+                 (static_cast<size_t>(plan->host.mats[i].cols) * es) % 16 == 0;
+  }
+  // the table is read by the plan's kernels: let earlier work finish first
+  if (hipDeviceSynchronize() != hipSuccess) return MUON_E_DEVICE;
+  if (!info.empty() && hipMemcpy(plan->dmem, info.data(), sizeof(MatInfo) * info.size(),
+                                 hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipGetLastError();
+    return MUON_E_DEVICE;
+  }
+  plan->host.info = info;
+  plan->has_weights = true;
+  return MUON_OK;
+}
+
+muon_status muon_plan_step_apply(muon_plan* plan, const muon_config* cfg, const muon_apply* ap,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  muon_status st = muon::validate_apply(ap);
+  if (st != MUON_OK) return st;
+  if (!plan->has_weights) return MUON_E_INVALID;
+  return step_impl(plan, cfg, workspace, workspace_bytes, stream, false, ap);
 }
 
 void muon_plan_destroy(muon_plan* plan) { release(plan); }

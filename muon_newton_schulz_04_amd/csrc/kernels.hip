@@ -156,6 +156,16 @@ __device__ __forceinline__ int64_t xo_sel(const MatInfo& M, int which) {
   return which ? M.xo_off[1] : M.xo_off[0];
 }
 
+// Weight application: W' = W (1 - lr wd wd_mul) - lr lr_mul x, in fp32.
+struct WApply {
+  float keep, step;  // 1 - lr wd wd_mul, lr lr_mul
+  __device__ __forceinline__ WApply(const StepArgs& A, const MatInfo& M)
+      : keep(1.f - A.lr * A.wd * M.wd_mul), step(A.lr * M.lr_mul) {}
+  __device__ __forceinline__ float operator()(float w, float x) const {
+    return __fmaf_rn(-step, x, w * keep);
+  }
+};
+
 // u from the gradient and the already-updated buffer (same expression in
 // both elementwise kernels so u is bitwise identical).
 __device__ __forceinline__ float form_u(float g, float nb, const StepArgs& A) {
@@ -316,15 +326,22 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   }
 
   if (A.direct) {  // zero steps: X0 is the result, in the caller's layout
-    T* o = static_cast<T*>(M.out);
+    const WApply wa(A, M);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int v = threadIdx.x + 256 * h;
       const int32_t cr = cr0 + (v >> 3), cc = cc0 + (v & 7) * 8;
       if (cr >= M.rows) continue;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (cc + e < M.cols) Elem<T>::store(o, int64_t(cr) * M.ld + cc + e, u[h][e]);
+      for (int e = 0; e < 8; ++e) {
+        if (cc + e >= M.cols) continue;
+        if (A.apply) {
+          const int64_t wi = int64_t(cr) * M.wld + cc + e;
+          Elem<T>::store(M.w, wi, wa(Elem<T>::load(M.w, wi), u[h][e]));
+        } else {
+          Elem<T>::store(M.out, int64_t(cr) * M.ld + cc + e, u[h][e]);
+        }
+      }
     }
     return;
   }
@@ -652,6 +669,7 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
       // last step: out in the caller's layout and dtype, valid region only
       const float* xsrc = reinterpret_cast<const float*>(P.ws + xo_sel(M, P.cur));
       char* o = static_cast<char*>(M.out);
+      const WApply wa(P, M);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -663,8 +681,13 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
             const int gi = gi0 + r;
             if (gi < M.m && gj < M.n) {
               const float v = __fmaf_rn(P.a, xsrc[int64_t(gi) * ldx + gj], acc[i][j][r]);
-              const int64_t co = M.tall ? int64_t(gj) * M.ld + gi : int64_t(gi) * M.ld + gj;
-              Elem<T>::store(o, co, v);
+              if (P.apply) {
+                const int64_t wi = M.tall ? int64_t(gj) * M.wld + gi : int64_t(gi) * M.wld + gj;
+                Elem<T>::store(M.w, wi, wa(Elem<T>::load(M.w, wi), v));
+              } else {
+                const int64_t co = M.tall ? int64_t(gj) * M.ld + gi : int64_t(gi) * M.ld + gj;
+                Elem<T>::store(o, co, v);
+              }
             }
           }
         }
@@ -956,15 +979,20 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   // Matrix record fields read once into registers: re-reading them after a
   // global store would force a reload (the compiler cannot rule out aliasing).
   struct {
-    int32_t m, n, mp, np, tall, vec_ok;
-    int64_t ld, a_off, b_off, xl_off, xo_cur, xo_nxt;
+    int32_t m, n, mp, np, tall, vec_ok, w_vec_ok;
+    int64_t ld, a_off, b_off, xl_off, xo_cur, xo_nxt, wld;
     void* out;
+    void* w;
+    float keep, step;  // weight application (see WApply)
   } M;
   {
     const MatInfo& R = P.mats[it.mat];
     M.m = R.m; M.n = R.n; M.mp = R.mp; M.np = R.np; M.tall = R.tall; M.vec_ok = R.vec_ok;
     M.ld = R.ld; M.a_off = R.a_off; M.b_off = R.b_off; M.xl_off = R.xl_off;
     M.xo_cur = xo_sel(R, P.cur); M.xo_nxt = xo_sel(R, P.cur ^ 1); M.out = R.out;
+    M.w = R.w; M.wld = R.wld; M.w_vec_ok = R.w_vec_ok;
+    const WApply wa(P, R);
+    M.keep = wa.keep; M.step = wa.step;
   }
   constexpr bool KN = KIND == UPDATE;
 
@@ -1322,6 +1350,40 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
       rows_out([&](int m, int n, const uint4& v) {
         *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
       });
+    } else if (P.apply) {
+      // weight application: W' = W keep - step X in the caller's layout
+      // (transposed for tall matrices); X is staged as fp16, three more
+      // significant bits than the set's bf16
+      stage16(true);
+      __syncthreads();
+      uint16_t* wm16 = static_cast<uint16_t*>(M.w);
+      const float keep = M.keep, step = M.step;
+      auto putw = [&](int row, int col, int nrow, int ncol, const uint4& v) {
+        if (row >= nrow) return;
+        uint16_t* d = wm16 + int64_t(row) * M.wld + col;
+        if (M.w_vec_ok && col + 7 < ncol) {
+          const uint4 wv = *reinterpret_cast<const uint4*>(d);
+          uint32_t r[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x0 = Op<OP_F16>::load16(half(v, 2 * q)), x1 = Op<OP_F16>::load16(half(v, 2 * q + 1));
+            const float w0 = bf2f(static_cast<uint16_t>(half(wv, 2 * q)));
+            const float w1 = bf2f(static_cast<uint16_t>(half(wv, 2 * q + 1)));
+            r[q] = uint32_t(f2bf(__fmaf_rn(-step, x0, w0 * keep))) |
+                   (uint32_t(f2bf(__fmaf_rn(-step, x1, w1 * keep))) << 16);
+          }
+          *reinterpret_cast<uint4*>(d) = make_uint4(r[0], r[1], r[2], r[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < ncol)
+              d[e] = f2bf(__fmaf_rn(-step, Op<OP_F16>::load16(half(v, e)), bf2f(d[e]) * keep));
+        }
+      };
+      if (!M.tall)
+        rows_out([&](int m, int n, const uint4& v) { putw(m, n, M.m, M.n, v); });
+      else
+        cols_out([&](int n, int m, const uint4& v) { putw(n, m, M.n, M.m, v); });
     } else {
       // `out` in the caller's layout (bf16), transposed for tall matrices
       stage16(false);

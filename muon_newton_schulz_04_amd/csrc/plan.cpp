@@ -81,6 +81,52 @@ muon_status validate_config(const muon_config* cfg) {
 }
 
 namespace {
+// True if any interval that is written overlaps another interval.
+bool overlaps(std::vector<Interval>& iv) {
+  std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) { return x.lo < y.lo; });
+  uintptr_t max_hi_any = 0, max_hi_w = 0;
+  for (const Interval& x : iv) {
+    if (x.lo < max_hi_w) return true;
+    if (x.write && x.lo < max_hi_any) return true;
+    max_hi_any = std::max(max_hi_any, x.hi);
+    if (x.write) max_hi_w = std::max(max_hi_w, x.hi);
+  }
+  return false;
+}
+}  // namespace
+
+muon_status validate_weights(const HostPlan& plan, const muon_weight* w, int32_t n) {
+  if (n != static_cast<int32_t>(plan.mats.size())) return MUON_E_SHAPE;
+  if (n > 0 && w == nullptr) return MUON_E_INVALID;
+  const size_t es = elem_size(plan.dtype);
+  std::vector<Interval> iv;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_matrix& M = plan.mats[i];
+    if (M.rows == 0 || M.cols == 0) continue;
+    const muon_weight& W = w[i];
+    if (W.weight == nullptr) return MUON_E_INVALID;
+    if (W.ld < M.cols || W.ld > (int64_t(1) << 40)) return MUON_E_SHAPE;
+    if (reinterpret_cast<uintptr_t>(W.weight) % es != 0) return MUON_E_ALIGN;
+    if (!std::isfinite(W.lr_mul) || !std::isfinite(W.wd_mul)) return MUON_E_INVALID;
+    auto add = [&](const void* p, int64_t ld, bool wr) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      iv.push_back({lo, lo + static_cast<uintptr_t>(((M.rows - 1) * ld + M.cols) * es), wr, i});
+    };
+    add(W.weight, W.ld, true);
+    add(M.out, M.ld, true);
+    if (M.momentum) add(M.momentum, M.ld, true);
+    if (M.grad != M.out) add(M.grad, M.ld, false);
+  }
+  return overlaps(iv) ? MUON_E_INVALID : MUON_OK;
+}
+
+muon_status validate_apply(const muon_apply* ap) {
+  if (ap == nullptr) return MUON_E_INVALID;
+  if (!std::isfinite(ap->lr) || !std::isfinite(ap->wd)) return MUON_E_INVALID;
+  return MUON_OK;
+}
+
+namespace {
 
 // A run of consecutive work items of one matrix, with its summed cost.
 struct Chunk {

@@ -42,6 +42,13 @@ struct MatInfo {
   int64_t b_off;     // B = b A + c A A
   int32_t part_off;  // first slot of this matrix's sum-of-squares partials
   int32_t part_cnt;
+  // Weight application (muon_plan_step_apply): W in the caller's dtype and
+  // orientation, row-major with leading dimension wld; lr and wd multipliers.
+  void* w;
+  int64_t wld;
+  float lr_mul, wd_mul;
+  int32_t w_vec_ok;  // 16-byte vector access legal for W
+  int32_t pad_;
 };
 
 struct WorkItem {
@@ -82,6 +89,11 @@ muon_status validate_matrices(const muon_matrix* mats, int32_t n, muon_dtype dty
                               bool need_momentum);
 // Validates per-call scalars.
 muon_status validate_config(const muon_config* cfg);
+// Validates the weights of a plan's matrices (one record per matrix; empty
+// matrices' records are ignored) against the set's buffers.
+muon_status validate_weights(const HostPlan& plan, const muon_weight* w, int32_t n);
+// Validates the scalars of a weight application.
+muon_status validate_apply(const muon_apply* ap);
 // Builds the full host plan (no device calls). need_momentum: momentum
 // pointers are part of the set (false for orthogonalisation-only plans).
 muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, HostPlan* out);

@@ -14,5 +14,6 @@ from .muon_oracle import (  # noqa: F401
     orthogonalize,
     muon_update,
     muon_update_set,
+    apply_weight,
     falg_flops,
 )

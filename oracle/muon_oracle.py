@@ -43,6 +43,7 @@ __all__ = [
     "orthogonalize",
     "muon_update",
     "muon_update_set",
+    "apply_weight",
     "falg_flops",
 ]
 
@@ -179,6 +180,30 @@ def muon_update_set(grads, bufs, **cfg):
         outs.append(o)
         new_bufs.append(nb)
     return outs, new_bufs
+
+
+def apply_weight(w, x, *, lr: float, wd: float, lr_mul: float = 1.0, wd_mul: float = 1.0,
+                 dtype: str = "bf16") -> np.ndarray:
+    """Moves the weight against the orthogonalised update, with decoupled
+    weight decay:  W' = W * (1 - lr*wd*wd_mul) - lr*lr_mul * X,  in float64,
+    then stored at the weight's dtype (round to nearest even).
+
+    Sources: mhpq.cn, modded-nanogpt track_1_short technical guide, section
+    6.2 (training hyper-parameters): each parameter group has its own
+    learning-rate and weight-decay multipliers (lr_mul, wd_mul);
+    yongjin360.com, Modded-NanoGPT green-AI article, hyper-parameter
+    paragraph: weight decay is part of the training recipe. The pages state
+    neither the schedule nor the form of the decay; the plainest reading is
+    the decoupled form above with every scalar supplied by the caller.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    res = w * (1.0 - float(lr) * float(wd) * float(wd_mul)) - float(lr) * float(lr_mul) * x
+    if dtype == "bf16":
+        return bf16_round(res)
+    if dtype == "fp32":
+        return fp32_round(res)
+    return res
 
 
 def falg_flops(rows: int, cols: int, steps: int) -> int:

@@ -260,6 +260,45 @@ def pin_bf16_rounding(impl):
     assert np.isnan(impl.bf16_round(np.array([np.nan]))[0])
 
 
+def pin_apply_weight(impl):
+    """Weight application W' = W (1 - lr wd wd_mul) - lr lr_mul X, pinned by
+    special cases with exact answers (dyadic scalars keep float64 exact)."""
+    rng = np.random.default_rng(23)
+    W = impl.bf16_round(rng.standard_normal((6, 10)))
+    X = rng.standard_normal((6, 10))
+    # lr = 0: the weight is untouched, bit for bit, whatever X and wd are
+    for dt in ("bf16", "fp32", "f64"):
+        assert np.array_equal(impl.apply_weight(W, X, lr=0.0, wd=3.0, lr_mul=2.0, wd_mul=5.0,
+                                                dtype=dt), W)
+    # step equal to the kept fraction and X = W: the result is exactly zero.
+    # keep = 1 - 0.5 * 0.25 * 2 = 0.75 and step = 0.5 * 1.5 = 0.75; ignoring
+    # wd_mul, ignoring lr_mul, swapping them or flipping a sign all miss 0
+    Z = impl.apply_weight(W, W, lr=0.5, wd=0.25, lr_mul=1.5, wd_mul=2.0, dtype="f64")
+    assert np.array_equal(Z, np.zeros_like(W))
+    # pure decay (X = 0) applied k times: the exact geometric sequence
+    # (1 - 1/8)^k W, checked in rational arithmetic on dyadic entries
+    Wd = np.array([[0.5, -1.25], [3.0, 0.0]])
+    cur = Wd.copy()
+    for _ in range(4):
+        cur = impl.apply_weight(cur, np.zeros_like(Wd), lr=0.25, wd=0.5, lr_mul=7.0, dtype="f64")
+    want = [[float(Fraction(7, 8) ** 4 * Fraction(v)) for v in row] for row in Wd.tolist()]
+    assert np.array_equal(cur, np.array(want))
+    # no decay: the step is -lr*lr_mul*X exactly (dyadic values)
+    Xd = np.array([[1.0, -2.0], [0.25, 4.0]])
+    got = impl.apply_weight(Wd, Xd, lr=0.125, wd=0.0, lr_mul=2.0, wd_mul=9.0, dtype="f64")
+    assert np.array_equal(got - Wd, -0.25 * Xd)
+    # affine in (W, X) separately: superposition of the two parts
+    a1 = impl.apply_weight(W, X, lr=0.3, wd=0.7, lr_mul=1.1, wd_mul=0.9, dtype="f64")
+    a2 = impl.apply_weight(W, np.zeros_like(X), lr=0.3, wd=0.7, lr_mul=1.1, wd_mul=0.9, dtype="f64")
+    a3 = impl.apply_weight(np.zeros_like(W), X, lr=0.3, wd=0.7, lr_mul=1.1, wd_mul=0.9, dtype="f64")
+    assert np.allclose(a1, a2 + a3, rtol=0, atol=1e-14)
+    # stored at the weight's dtype: bf16 / fp32 rounding of the float64 value
+    b = impl.apply_weight(W, X, lr=0.3, wd=0.7, lr_mul=1.1, wd_mul=0.9, dtype="bf16")
+    assert np.array_equal(b, torch.from_numpy(a1).float().to(torch.bfloat16).double().numpy()) or \
+        np.max(np.abs(b - a1) / np.maximum(np.abs(a1), 1e-30)) <= 2.0 ** -9
+    assert np.array_equal(impl.bf16_round(b), b)
+
+
 ALL_PINS = [pin_closed_form, pin_closed_form_with_momentum, pin_momentum_bf16_state,
             pin_polar_limit, pin_equal_singular_values, pin_golden_diagonal, pin_brute_force,
-            pin_invariants, pin_bf16_rounding]
+            pin_invariants, pin_bf16_rounding, pin_apply_weight]
