@@ -156,7 +156,7 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
  * The step after the orthogonalised update: the weight matrix W of each
  * parameter moves against it with decoupled weight decay,
  *
- *   W <- W * (1 - lr * wd * wd_mul) - lr * lr_mul * X
+ *   W <- W * (1 - lr' * wd') - lr' * X,   lr' = lr * lr_mul,  wd' = wd * wd_mul
  *
  * where X is the Muon result (what muon_plan_step writes to `out`), lr and wd
  * are per call and lr_mul, wd_mul per matrix (mhpq.cn, modded-nanogpt
@@ -165,7 +165,8 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
  * yongjin360.com, Modded-NanoGPT green-AI article, hyper-parameter
  * paragraph: weight decay is part of the recipe). The pages give no
  * learning-rate schedule or shape rule, so all four scalars come from the
- * caller. The product runs in fp32 on X before any rounding to the set's
+ * caller; the multipliers scale the learning rate and the decay wherever
+ * they appear (decoupled decay, proportional to the effective rate). The product runs in fp32 on X before any rounding to the set's
  * dtype (the 16-bit path stages X as fp16 first), and W' is stored at the
  * set's dtype, round to nearest even. */
 

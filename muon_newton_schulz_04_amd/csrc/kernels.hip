@@ -156,11 +156,12 @@ __device__ __forceinline__ int64_t xo_sel(const MatInfo& M, int which) {
   return which ? M.xo_off[1] : M.xo_off[0];
 }
 
-// Weight application: W' = W (1 - lr wd wd_mul) - lr lr_mul x, in fp32.
+// Weight application: W' = W (1 - lr' wd') - lr' x with lr' = lr lr_mul and
+// wd' = wd wd_mul, in fp32.
 struct WApply {
-  float keep, step;  // 1 - lr wd wd_mul, lr lr_mul
+  float keep, step;  // 1 - lr' wd', lr'
   __device__ __forceinline__ WApply(const StepArgs& A, const MatInfo& M)
-      : keep(1.f - A.lr * A.wd * M.wd_mul), step(A.lr * M.lr_mul) {}
+      : keep(1.f - (A.lr * M.lr_mul) * (A.wd * M.wd_mul)), step(A.lr * M.lr_mul) {}
   __device__ __forceinline__ float operator()(float w, float x) const {
     return __fmaf_rn(-step, x, w * keep);
   }

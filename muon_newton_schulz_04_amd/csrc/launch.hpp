@@ -19,7 +19,7 @@ struct StepArgs {
   int32_t cur;      // which operand buffer holds the current X
   int32_t last;     // last Newton-Schulz step: write `out`
   int32_t direct;   // zero steps: the normalise kernel writes `out`
-  int32_t apply;    // write W <- W (1 - lr wd wd_mul) - lr lr_mul X instead of `out`
+  int32_t apply;    // write W <- W (1 - lr' wd') - lr' X instead of `out` (lr' = lr lr_mul, wd' = wd wd_mul)
   float lr, wd;
 };
 

@@ -185,8 +185,9 @@ def muon_update_set(grads, bufs, **cfg):
 def apply_weight(w, x, *, lr: float, wd: float, lr_mul: float = 1.0, wd_mul: float = 1.0,
                  dtype: str = "bf16") -> np.ndarray:
     """Moves the weight against the orthogonalised update, with decoupled
-    weight decay:  W' = W * (1 - lr*wd*wd_mul) - lr*lr_mul * X,  in float64,
-    then stored at the weight's dtype (round to nearest even).
+    weight decay:  W' = W * (1 - lr' * wd') - lr' * X  where lr' = lr*lr_mul
+    and wd' = wd*wd_mul, in float64, then stored at the weight's dtype (round
+    to nearest even).
 
     Sources: mhpq.cn, modded-nanogpt track_1_short technical guide, section
     6.2 (training hyper-parameters): each parameter group has its own
@@ -194,11 +195,14 @@ def apply_weight(w, x, *, lr: float, wd: float, lr_mul: float = 1.0, wd_mul: flo
     yongjin360.com, Modded-NanoGPT green-AI article, hyper-parameter
     paragraph: weight decay is part of the training recipe. The pages state
     neither the schedule nor the form of the decay; the plainest reading is
-    the decoupled form above with every scalar supplied by the caller.
+    the decoupled form above (the decay proportional to the effective rate,
+    as in decoupled-decay Adam) with every scalar supplied by the caller.
     """
     w = np.asarray(w, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
-    res = w * (1.0 - float(lr) * float(wd) * float(wd_mul)) - float(lr) * float(lr_mul) * x
+    lr_eff = float(lr) * float(lr_mul)
+    wd_eff = float(wd) * float(wd_mul)
+    res = w * (1.0 - lr_eff * wd_eff) - lr_eff * x
     if dtype == "bf16":
         return bf16_round(res)
     if dtype == "fp32":

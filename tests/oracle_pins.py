@@ -261,8 +261,9 @@ def pin_bf16_rounding(impl):
 
 
 def pin_apply_weight(impl):
-    """Weight application W' = W (1 - lr wd wd_mul) - lr lr_mul X, pinned by
-    special cases with exact answers (dyadic scalars keep float64 exact)."""
+    """Weight application W' = W (1 - lr' wd') - lr' X (lr' = lr lr_mul,
+    wd' = wd wd_mul), pinned by special cases with exact answers (dyadic
+    scalars keep float64 exact)."""
     rng = np.random.default_rng(23)
     W = impl.bf16_round(rng.standard_normal((6, 10)))
     X = rng.standard_normal((6, 10))
@@ -271,16 +272,19 @@ def pin_apply_weight(impl):
         assert np.array_equal(impl.apply_weight(W, X, lr=0.0, wd=3.0, lr_mul=2.0, wd_mul=5.0,
                                                 dtype=dt), W)
     # step equal to the kept fraction and X = W: the result is exactly zero.
-    # keep = 1 - 0.5 * 0.25 * 2 = 0.75 and step = 0.5 * 1.5 = 0.75; ignoring
-    # wd_mul, ignoring lr_mul, swapping them or flipping a sign all miss 0
-    Z = impl.apply_weight(W, W, lr=0.5, wd=0.25, lr_mul=1.5, wd_mul=2.0, dtype="f64")
+    # lr' = 0.25 * 2 = 0.5, wd' = 0.25 * 4 = 1: keep = 1 - 0.5 = 0.5 = lr';
+    # ignoring wd_mul or lr_mul, swapping them, leaving lr out of the decay
+    # or flipping a sign all miss 0
+    Z = impl.apply_weight(W, W, lr=0.25, wd=0.25, lr_mul=2.0, wd_mul=4.0, dtype="f64")
     assert np.array_equal(Z, np.zeros_like(W))
     # pure decay (X = 0) applied k times: the exact geometric sequence
-    # (1 - 1/8)^k W, checked in rational arithmetic on dyadic entries
+    # (1 - 1/8)^k W (lr' wd' = 0.25 * 0.5), in rational arithmetic on dyadic
+    # entries
     Wd = np.array([[0.5, -1.25], [3.0, 0.0]])
     cur = Wd.copy()
     for _ in range(4):
-        cur = impl.apply_weight(cur, np.zeros_like(Wd), lr=0.25, wd=0.5, lr_mul=7.0, dtype="f64")
+        cur = impl.apply_weight(cur, np.zeros_like(Wd), lr=0.125, wd=0.25, lr_mul=2.0,
+                                wd_mul=2.0, dtype="f64")
     want = [[float(Fraction(7, 8) ** 4 * Fraction(v)) for v in row] for row in Wd.tolist()]
     assert np.array_equal(cur, np.array(want))
     # no decay: the step is -lr*lr_mul*X exactly (dyadic values)

@@ -36,11 +36,14 @@ MUTATIONS = {
                     "np.rint(np.ldexp(f[normal], 7)), e[normal] - 7)"),
     "bf16_truncate": ("np.rint(np.ldexp(f[normal], 8))", "np.trunc(np.ldexp(f[normal], 8))"),
     "bf16_half_up": ("np.rint(np.ldexp(f[normal], 8))", "np.floor(np.ldexp(f[normal], 8) + 0.5)"),
-    "apply_sign": ("- float(lr) * float(lr_mul) * x", "+ float(lr) * float(lr_mul) * x"),
-    "apply_no_wd_mul": ("(1.0 - float(lr) * float(wd) * float(wd_mul))", "(1.0 - float(lr) * float(wd))"),
-    "apply_no_lr_mul": ("- float(lr) * float(lr_mul) * x", "- float(lr) * x"),
-    "apply_decay_no_lr": ("(1.0 - float(lr) * float(wd) * float(wd_mul))",
-                          "(1.0 - float(wd) * float(wd_mul))"),
+    "apply_sign": ("res = w * (1.0 - lr_eff * wd_eff) - lr_eff * x",
+                   "res = w * (1.0 - lr_eff * wd_eff) + lr_eff * x"),
+    "apply_no_wd_mul": ("wd_eff = float(wd) * float(wd_mul)", "wd_eff = float(wd)"),
+    "apply_no_lr_mul": ("lr_eff = float(lr) * float(lr_mul)", "lr_eff = float(lr)"),
+    "apply_decay_no_lr": ("res = w * (1.0 - lr_eff * wd_eff) - lr_eff * x",
+                          "res = w * (1.0 - wd_eff) - lr_eff * x"),
+    "apply_multipliers_swapped": ("lr_eff = float(lr) * float(lr_mul)\n    wd_eff = float(wd) * float(wd_mul)",
+                                  "lr_eff = float(lr) * float(wd_mul)\n    wd_eff = float(wd) * float(lr_mul)"),
     "apply_not_rounded": ("        return bf16_round(res)\n    if dtype == \"fp32\"",
                           "        return res\n    if dtype == \"fp32\""),
 }
