@@ -234,6 +234,29 @@ def main():
     ms_apply = float(np.median([f for _, f in pairs]))
     del weights
 
+    # the other half of the optimizer step: Adam over GPT-2 124M's parameters
+    # off the Muon path (bf16 parameters, fp32 moments), one launch per step
+    from workloads import gpt2_124m_adam_multipliers, gpt2_124m_adam_shapes, make_adam_state
+    a_shapes = gpt2_124m_adam_shapes()
+    a_lrm, a_wdm = gpt2_124m_adam_multipliers(a_shapes)
+    ap, ag, am, av = make_adam_state(a_shapes, torch.bfloat16, 7, dev)
+    aplan = mu.AdamPlan(ap, ag, am, av, a_lrm, a_wdm)
+    a_steps = max(10, args.steps // 2)
+    for t in range(1, 4):
+        aplan.step(1e-3, 0.9, 0.99, 1e-8, 0.1, t, stream)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for t in range(4, 4 + a_steps):
+        aplan.step(1e-3, 0.9, 0.99, 1e-8, 0.1, t, stream)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    a_us = c0.elapsed_time(c1) / a_steps * 1e3
+    a_elems = sum(p.numel() for p in ap)
+    a_bytes = a_elems * (2 + 2 + 4 + 4 + 2 + 4 + 4)  # read p, g, m, v; write p, m, v
+    aplan.destroy()
+    del ap, ag, am, av
+
     falg = wl.falg_flops()
     value = falg / (ms * 1e-3) / 1e12
     work = kernel_work(wl.shapes, wl.steps, wl.dtype)
@@ -283,7 +306,14 @@ def main():
             "ms_per_step": ms_apply, "steps": 3 * n_apply,
             "plain_ms_per_step_same_blocks": ms_plain_b,
             "extra_us_vs_plain_step": (ms_apply - ms_plain_b) * 1e3,
-            "note": "muon_plan_step_apply: W <- W(1 - lr wd) - lr X fused into the last update"}},
+            "note": "muon_plan_step_apply: W <- W(1 - lr wd) - lr X fused into the last update"},
+            "adam": {
+                "workload": "gpt2_124m_non_matrix_params", "tensors": len(a_shapes),
+                "elements": a_elems, "us_per_step": a_us, "steps": a_steps,
+                "roofline": {"bound": "hbm", "achieved": a_bytes / (a_us * 1e-6) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             "bytes_per_step": a_bytes}}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

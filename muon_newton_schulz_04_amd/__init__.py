@@ -20,6 +20,8 @@ __all__ = [
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
     "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
+    "MuonAdamTensor", "MuonAdamConfig", "AdamPlan", "muon_adam_plan_create",
+    "muon_adam_plan_step", "muon_adam_plan_destroy", "muon_adam_work_items",
     "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT", "MUON_PRECISION_BF16_OPERANDS",
 ]
 
@@ -58,6 +60,17 @@ class MuonApply(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("wd", ctypes.c_float)]
 
 
+class MuonAdamTensor(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("lr_mul", ctypes.c_float), ("wd_mul", ctypes.c_float)]
+
+
+class MuonAdamConfig(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("wd", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
 class MuonBufferInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("m", "n", "mp", "np", "x_lo", "x_op0", "x_op1", "gram", "poly")]
@@ -92,6 +105,10 @@ def load_library(path: str = LIB_PATH):
         "muon_plan_buffer_info": (i32, [vp, i32, P(MuonBufferInfo)]),
         "muon_plan_set_weights": (i32, [vp, P(MuonWeight), i32]),
         "muon_plan_step_apply": (i32, [vp, P(MuonConfig), P(MuonApply), vp, sz, vp]),
+        "muon_adam_plan_create": (i32, [P(MuonAdamTensor), i32, i32, P(vp)]),
+        "muon_adam_plan_step": (i32, [vp, P(MuonAdamConfig), vp]),
+        "muon_adam_plan_destroy": (None, [vp]),
+        "muon_adam_work_items": (i32, [P(MuonAdamTensor), i32, i32, P(i64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -372,3 +389,86 @@ def muon_orthogonalize(grads: List, outs: List, cfg: MuonConfig, workspace=None,
     _check(lib.muon_orthogonalize(arr, n, dt, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
                                   _stream_handle(stream)), "muon_orthogonalize")
     return ws
+
+
+# ------------------------------------------------------------------ Adam branch
+
+def _adam_tensors(params, grads, exp_avgs, exp_avg_sqs, lr_mul=None, wd_mul=None):
+    """muon_adam_tensor array (and dtype code) from lists of torch tensors
+    (each contiguous; moments float32)."""
+    import torch
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads and the two moment lists must have the same length")
+    lr_mul = [1.0] * n if lr_mul is None else list(lr_mul)
+    wd_mul = [1.0] * n if wd_mul is None else list(wd_mul)
+    arr = (MuonAdamTensor * max(n, 1))()
+    dt = None
+    for i in range(n):
+        p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+        for t in (p, g, m, v):
+            if not t.is_contiguous():
+                raise ValueError("Adam tensors must be contiguous")
+            if t.numel() != p.numel():
+                raise ValueError("param, grad and moments must have the same element count")
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError("Adam moments are float32")
+        d = _dtype_code(p)
+        if _dtype_code(g) != d:
+            raise TypeError("param and grad must share one dtype")
+        if dt is None:
+            dt = d
+        elif d != dt:
+            raise TypeError("all parameters of a call must share one dtype")
+        arr[i] = MuonAdamTensor(p.numel(), _ptr(p), _ptr(g), _ptr(m), _ptr(v),
+                                float(lr_mul[i]), float(wd_mul[i]))
+    return arr, n, (MUON_BF16 if dt is None else dt)
+
+
+def muon_adam_work_items(params, grads, exp_avgs, exp_avg_sqs) -> int:
+    arr, n, dt = _adam_tensors(params, grads, exp_avgs, exp_avg_sqs)
+    out = ctypes.c_int64(0)
+    _check(load_library().muon_adam_work_items(arr, n, dt, ctypes.byref(out)), "muon_adam_work_items")
+    return out.value
+
+
+class AdamPlan:
+    """Adam over a fixed list of tensors (pointers baked into the plan)."""
+
+    def __init__(self, params, grads, exp_avgs, exp_avg_sqs, lr_mul=None, wd_mul=None):
+        lib = load_library()
+        self._keep = (list(params), list(grads), list(exp_avgs), list(exp_avg_sqs))
+        arr, n, dt = _adam_tensors(params, grads, exp_avgs, exp_avg_sqs, lr_mul, wd_mul)
+        self.dtype = dt
+        h = ctypes.c_void_p(None)
+        _check(lib.muon_adam_plan_create(arr, n, dt, ctypes.byref(h)), "muon_adam_plan_create")
+        self.handle = h
+
+    def step(self, lr: float, beta1: float, beta2: float, eps: float, wd: float, step: int,
+             stream=None):
+        cfg = MuonAdamConfig(float(lr), float(beta1), float(beta2), float(eps), float(wd), int(step))
+        _check(load_library().muon_adam_plan_step(self.handle, ctypes.byref(cfg),
+                                                  _stream_handle(stream)), "muon_adam_plan_step")
+
+    def destroy(self):
+        if self.handle:
+            load_library().muon_adam_plan_destroy(self.handle)
+            self.handle = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def muon_adam_plan_create(params, grads, exp_avgs, exp_avg_sqs, lr_mul=None, wd_mul=None):
+    return AdamPlan(params, grads, exp_avgs, exp_avg_sqs, lr_mul, wd_mul)
+
+
+def muon_adam_plan_step(plan: AdamPlan, lr, beta1, beta2, eps, wd, step, stream=None):
+    plan.step(lr, beta1, beta2, eps, wd, step, stream)
+
+
+def muon_adam_plan_destroy(plan: AdamPlan):
+    plan.destroy()

@@ -15,5 +15,6 @@ from .muon_oracle import (  # noqa: F401
     muon_update,
     muon_update_set,
     apply_weight,
+    adam_update,
     falg_flops,
 )

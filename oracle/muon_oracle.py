@@ -44,6 +44,7 @@ __all__ = [
     "muon_update",
     "muon_update_set",
     "apply_weight",
+    "adam_update",
     "falg_flops",
 ]
 
@@ -208,6 +209,39 @@ def apply_weight(w, x, *, lr: float, wd: float, lr_mul: float = 1.0, wd_mul: flo
     if dtype == "fp32":
         return fp32_round(res)
     return res
+
+
+def adam_update(p, g, m, v, *, lr: float, beta1: float, beta2: float, eps: float, wd: float,
+                step: int, lr_mul: float = 1.0, wd_mul: float = 1.0, dtype: str = "bf16"):
+    """One Adam update of a parameter tensor off the Muon path, in float64.
+
+    Source: mhpq.cn, modded-nanogpt track_1_short technical guide, section
+    6.2 (training hyper-parameters): the parameter groups that are not
+    projection matrices run Adam with betas (0.9, 0.99) and their own lr_mul,
+    with wd_mul = 0 for biases and scales. The pages do not write Adam out;
+    this is the textbook update with bias correction and decoupled weight
+    decay, the multipliers scaling the rate and the decay:
+        m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+        m_hat = m / (1 - beta1^t);      v_hat = v / (1 - beta2^t)
+        p <- p (1 - lr' wd') - lr' m_hat / (sqrt(v_hat) + eps)
+    with lr' = lr*lr_mul, wd' = wd*wd_mul and t = step (1-based). The moments
+    are stored as float32 and p at its dtype (round to nearest even); those
+    stored values are returned (p, m, v).
+    """
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    t = int(step)
+    m_new = fp32_round(beta1 * m + (1.0 - beta1) * g)
+    v_new = fp32_round(beta2 * v + (1.0 - beta2) * g * g)
+    m_hat = m_new / (1.0 - beta1 ** t)
+    v_hat = v_new / (1.0 - beta2 ** t)
+    rate = float(lr) * float(lr_mul)
+    decay = float(wd) * float(wd_mul)
+    p_new = p * (1.0 - rate * decay) - rate * m_hat / (np.sqrt(v_hat) + eps)
+    p_new = bf16_round(p_new) if dtype == "bf16" else fp32_round(p_new)
+    return p_new, m_new, v_new
 
 
 def falg_flops(rows: int, cols: int, steps: int) -> int:

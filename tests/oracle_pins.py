@@ -303,6 +303,51 @@ def pin_apply_weight(impl):
     assert np.array_equal(impl.bf16_round(b), b)
 
 
+def pin_adam(impl):
+    """Adam with bias correction and decoupled decay, pinned by closed forms
+    that hold exactly for dyadic betas and inputs:
+      * from a zero state, with a constant gradient and eps = 0, the bias-
+        corrected moments are exactly g and g^2, so every step moves p by
+        -lr' sign(g) (lr' = lr lr_mul);
+      * a zero gradient leaves only the decay p (1 - lr' wd') and shrinks the
+        moments by beta1 and beta2;
+      * with beta1 = beta2 = 0 the step is lr' g / (|g| + eps);
+    plus the storage formats of the state (float32) and of p."""
+    b1, b2 = 0.5, 15.0 / 16.0      # (1 - b1) = 1/2 and sqrt(1 - b2) = 1/4 differ
+    g = np.array([0.5, -2.0, 0.25, -0.125, 4.0])
+    p0 = np.array([1.0, -0.5, 0.0, 2.0, -3.0])
+    z = np.zeros_like(g)
+    p, m, v = p0.copy(), z.copy(), z.copy()
+    for t in range(1, 5):
+        p, m, v = impl.adam_update(p, g, m, v, lr=0.0625, beta1=b1, beta2=b2, eps=0.0, wd=0.0,
+                                   step=t, lr_mul=2.0, wd_mul=3.0, dtype="fp32")
+        assert np.array_equal(p, p0 - t * 0.125 * np.sign(g)), t
+        assert np.array_equal(m, (1 - b1 ** t) * g) and np.array_equal(v, (1 - b2 ** t) * g * g)
+    # zero gradient and zero first moment: decay only, p (1 - lr' wd') with
+    # lr' wd' = (0.0625 * 2) * (1 * 4) = 1/2; the moments shrink by the betas
+    m0 = np.array([0.5, -1.0, 0.25, 2.0, 0.0])
+    v0 = np.array([1.0, 0.25, 4.0, 0.5, 0.0])
+    p1, m1, v1 = impl.adam_update(p0, z, z, v0, lr=0.0625, beta1=b1, beta2=b2, eps=1e-3, wd=1.0,
+                                  step=3, lr_mul=2.0, wd_mul=4.0, dtype="fp32")
+    assert np.array_equal(p1, 0.5 * p0) and np.array_equal(m1, z) and np.array_equal(v1, b2 * v0)
+    _, m2, _ = impl.adam_update(p0, z, m0, v0, lr=0.0625, beta1=b1, beta2=b2, eps=1e-3, wd=1.0,
+                                step=3, dtype="fp32")
+    assert np.array_equal(m2, b1 * m0)
+    # no averaging: the step is lr' g / (|g| + eps) whatever the state
+    p2, _, _ = impl.adam_update(p0, g, m0, v0, lr=0.5, beta1=0.0, beta2=0.0, eps=0.25, wd=0.0,
+                                step=7, dtype="fp32")
+    want = p0 - 0.5 * g / (np.abs(g) + 0.25)
+    assert np.allclose(p2, want, rtol=2 ** -23, atol=0)
+    # storage: moments are float32 values, p at its dtype
+    rng = np.random.default_rng(5)
+    gg, pp = rng.standard_normal(64), rng.standard_normal(64)
+    pb, mb, vb = impl.adam_update(pp, gg, np.zeros(64), np.zeros(64), lr=0.01, beta1=0.9,
+                                  beta2=0.99, eps=1e-8, wd=0.1, step=1, dtype="bf16")
+    assert np.array_equal(impl.fp32_round(mb), mb) and np.array_equal(impl.fp32_round(vb), vb)
+    assert np.array_equal(impl.bf16_round(pb), pb)
+    assert not np.array_equal(pb, pp)
+
+
 ALL_PINS = [pin_closed_form, pin_closed_form_with_momentum, pin_momentum_bf16_state,
             pin_polar_limit, pin_equal_singular_values, pin_golden_diagonal, pin_brute_force,
-            pin_invariants, pin_bf16_rounding, pin_apply_weight]
+            pin_invariants, pin_bf16_rounding, pin_apply_weight, pin_adam]

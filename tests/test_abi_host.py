@@ -12,7 +12,8 @@ import muon_newton_schulz_04_amd as mu
 from workloads import CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "muon.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -24,15 +25,20 @@ def lib():
 
 
 def header_functions():
-    src = open(HEADER).read()
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(muon_\w+)\s*\(", src, re.M)))
+    names = set()
+    for h in HEADERS:
+        src = open(h).read()
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(muon_\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) >= 12
+    assert len(names) >= 18
+    for n in ("muon_adam_plan_create", "muon_plan_step_apply", "muon_plan_set_weights"):
+        assert n in names
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in muon.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/*.h but not exported"
 
 
 def test_abi_version_and_status_strings(lib):
@@ -187,3 +193,47 @@ def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):
             split += 1
     assert cost.max() / cost.mean() < 1.1
     assert split <= 8
+
+
+# ------------------------------------------------------------------ Adam branch (host only)
+
+def adam_list(specs):
+    """muon_adam_tensor array from (numel, param, grad, m, v) placeholder
+    addresses (never dereferenced: only host validation runs)."""
+    arr = (mu.MuonAdamTensor * max(len(specs), 1))()
+    for i, (n, p, g, m, v) in enumerate(specs):
+        arr[i] = mu.MuonAdamTensor(n, p, g, m, v, 1.0, 1.0)
+    return arr, len(specs)
+
+
+B = 1 << 40
+
+
+@pytest.mark.parametrize("specs,want", [
+    ([(100000, B, B + 2 ** 20, B + 2 ** 21, B + 2 ** 22), (7, B + 2 ** 23, B + 2 ** 24,
+                                                          B + 2 ** 25, B + 2 ** 26)], 0),
+    ([(-1, B, B + 4096, B + 8192, B + 12288)], 3),                         # negative size
+    ([(2 ** 31 + 1, B, B + 2 ** 33, B + 2 ** 34, B + 2 ** 35)], 3),         # beyond 2^31
+    ([(64, 0, B + 4096, B + 8192, B + 12288)], 1),                          # NULL param
+    ([(64, B + 1, B + 4096, B + 8192, B + 12288)], 4),                      # param misaligned
+    ([(64, B, B + 4096, B + 8194, B + 12288)], 4),                          # moment not 4-aligned
+    ([(64, B, B + 4096, B + 8192, B + 8192 + 128)], 1),                     # m and v overlap
+    ([(64, B, B + 4096, B + 8192, B + 12288), (64, B + 64, B + 20000, B + 24000, B + 28000)], 1),
+    ([(0, 0, 0, 0, 0)], 0),                                                 # empty: pointers ignored
+])
+def test_adam_host_validation(lib, specs, want):
+    arr, n = adam_list(specs)
+    items = ctypes.c_int64(-1)
+    assert lib.muon_adam_work_items(arr, n, mu.MUON_BF16, ctypes.byref(items)) == want
+    if want == 0:
+        exp = sum((s[0] + 16383) // 16384 for s in specs)
+        assert items.value == exp
+
+
+def test_adam_grads_may_alias_each_other(lib):
+    """Read-only gradients may overlap each other (shared zero grads)."""
+    arr, n = adam_list([(64, B, B + 2 ** 20, B + 8192, B + 12288),
+                        (64, B + 2 ** 16, B + 2 ** 20, B + 2 ** 17, B + 2 ** 18)])
+    items = ctypes.c_int64(0)
+    assert lib.muon_adam_work_items(arr, n, mu.MUON_F32, ctypes.byref(items)) == 0
+    assert items.value == 2

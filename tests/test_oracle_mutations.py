@@ -42,6 +42,19 @@ MUTATIONS = {
     "apply_no_lr_mul": ("lr_eff = float(lr) * float(lr_mul)", "lr_eff = float(lr)"),
     "apply_decay_no_lr": ("res = w * (1.0 - lr_eff * wd_eff) - lr_eff * x",
                           "res = w * (1.0 - wd_eff) - lr_eff * x"),
+    "adam_no_m_correction": ("m_hat = m_new / (1.0 - beta1 ** t)", "m_hat = m_new"),
+    "adam_no_v_correction": ("v_hat = v_new / (1.0 - beta2 ** t)", "v_hat = v_new"),
+    "adam_betas_swapped": ("m_new = fp32_round(beta1 * m + (1.0 - beta1) * g)",
+                           "m_new = fp32_round(beta2 * m + (1.0 - beta2) * g)"),
+    "adam_eps_inside_sqrt": ("(np.sqrt(v_hat) + eps)", "np.sqrt(v_hat + eps)"),
+    "adam_v_not_squared": ("(1.0 - beta2) * g * g)", "(1.0 - beta2) * np.abs(g))"),
+    "adam_decay_without_lr": ("p * (1.0 - rate * decay) - rate * m_hat",
+                              "p * (1.0 - decay) - rate * m_hat"),
+    "adam_no_lr_mul": ("rate = float(lr) * float(lr_mul)", "rate = float(lr)"),
+    "adam_no_wd_mul": ("decay = float(wd) * float(wd_mul)", "decay = float(wd)"),
+    "adam_moments_not_rounded": ("m_new = fp32_round(beta1 * m + (1.0 - beta1) * g)",
+                                 "m_new = beta1 * m + (1.0 - beta1) * g"),
+    "adam_step_off_by_one": ("t = int(step)", "t = int(step) + 1"),
     "apply_multipliers_swapped": ("lr_eff = float(lr) * float(lr_mul)\n    wd_eff = float(wd) * float(wd_mul)",
                                   "lr_eff = float(lr) * float(wd_mul)\n    wd_eff = float(wd) * float(lr_mul)"),
     "apply_not_rounded": ("        return bf16_round(res)\n    if dtype == \"fp32\"",

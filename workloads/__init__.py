@@ -13,3 +13,9 @@ from .generators import (  # noqa: F401
     make_workload,
     to_f64,
 )
+from .adam import (  # noqa: F401
+    gpt2_124m_adam_shapes,
+    gpt2_124m_adam_multipliers,
+    make_adam_state,
+    new_grads,
+)
