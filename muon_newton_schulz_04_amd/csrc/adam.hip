@@ -91,6 +91,94 @@ __device__ __forceinline__ float adam_elem(float p, float g, float& m, float& v,
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Eight consecutive elements of one tensor in registers.
+struct Vec8 {
+  float p[kVec], g[kVec], m[kVec], v[kVec];
+};
+
+template <typename T>
+__device__ __forceinline__ void load8(const Tensor& t, int64_t e0, Vec8& x) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 pw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(t.p) + e0);
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(t.g) + e0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x.p[2 * q] = __uint_as_float(pw[q] << 16);
+      x.p[2 * q + 1] = __uint_as_float(pw[q] & 0xffff0000u);
+      x.g[2 * q] = __uint_as_float(gw[q] << 16);
+      x.g[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(static_cast<const float*>(t.p) + e0 + 4 * h);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(static_cast<const float*>(t.g) + e0 + 4 * h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x.p[4 * h + q] = pv[q];
+        x.g[4 * h + q] = gv[q];
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 mv = *reinterpret_cast<const f32x4*>(t.m + e0 + 4 * h);
+    const f32x4 vv = *reinterpret_cast<const f32x4*>(t.v + e0 + 4 * h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x.m[4 * h + q] = mv[q];
+      x.v[4 * h + q] = vv[q];
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(const Tensor& t, int64_t e0, const Vec8& x) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    *reinterpret_cast<f32x4*>(t.m + e0 + 4 * h) =
+        f32x4{x.m[4 * h], x.m[4 * h + 1], x.m[4 * h + 2], x.m[4 * h + 3]};
+    *reinterpret_cast<f32x4*>(t.v + e0 + 4 * h) =
+        f32x4{x.v[4 * h], x.v[4 * h + 1], x.v[4 * h + 2], x.v[4 * h + 3]};
+  }
+  if constexpr (sizeof(T) == 2) {
+    u32x4 pw;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pw[q] = uint32_t(f2bf(x.p[2 * q])) | (uint32_t(f2bf(x.p[2 * q + 1])) << 16);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(t.p) + e0) = pw;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(t.p) + e0 + 4 * h) =
+          f32x4{x.p[4 * h], x.p[4 * h + 1], x.p[4 * h + 2], x.p[4 * h + 3]};
+  }
+}
+
+__device__ __forceinline__ void update8(Vec8& x, const Consts& k) {
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) x.p[e] = adam_elem(x.p[e], x.g[e], x.m[e], x.v[e], k);
+}
+
+// Elements e0 .. min(e0 + 8, end) - 1, vector or scalar.
+template <typename T>
+__device__ __forceinline__ void run8(const Tensor& t, int64_t e0, int64_t end, const Consts& k) {
+  if (t.vec && e0 + kVec <= end) {
+    Vec8 x;
+    load8<T>(t, e0, x);
+    update8(x, k);
+    store8<T>(t, e0, x);
+  } else {
+    const int64_t e1 = e0 + kVec < end ? e0 + kVec : end;
+    for (int64_t e = e0; e < e1; ++e) {
+      float m = t.m[e], v = t.v[e];
+      const float p = adam_elem(PElem<T>::load(t.p, e), PElem<T>::load(t.g, e), m, v, k);
+      t.m[e] = m;
+      t.v[e] = v;
+      PElem<T>::store(t.p, e, p);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void adam_kernel(Args A) {
   const Item it = A.items[blockIdx.x];
@@ -107,68 +195,21 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(Args A) {
   k.isb2 = A.inv_sqrt_bc2;
   const int64_t base = int64_t(it.chunk) * kChunk;
   const int64_t end = base + kChunk < t.numel ? base + kChunk : t.numel;
-  for (int64_t e0 = base + int64_t(threadIdx.x) * kVec; e0 < end; e0 += int64_t(kThreads) * kVec) {
-    if (t.vec && e0 + kVec <= end) {
-      float p[kVec], g[kVec], m[kVec], v[kVec];
-      if constexpr (sizeof(T) == 2) {
-        const u32x4 pw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(t.p) + e0);
-        const u32x4 gw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(t.g) + e0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          p[2 * q] = __uint_as_float(pw[q] << 16);
-          p[2 * q + 1] = __uint_as_float(pw[q] & 0xffff0000u);
-          g[2 * q] = __uint_as_float(gw[q] << 16);
-          g[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4 pv = *reinterpret_cast<const f32x4*>(static_cast<const float*>(t.p) + e0 + 4 * h);
-          const f32x4 gv = *reinterpret_cast<const f32x4*>(static_cast<const float*>(t.g) + e0 + 4 * h);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            p[4 * h + q] = pv[q];
-            g[4 * h + q] = gv[q];
-          }
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(t.m + e0 + 4 * h);
-        const f32x4 vv = *reinterpret_cast<const f32x4*>(t.v + e0 + 4 * h);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          m[4 * h + q] = mv[q];
-          v[4 * h + q] = vv[q];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) p[e] = adam_elem(p[e], g[e], m[e], v[e], k);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *reinterpret_cast<f32x4*>(t.m + e0 + 4 * h) = f32x4{m[4 * h], m[4 * h + 1], m[4 * h + 2], m[4 * h + 3]};
-        *reinterpret_cast<f32x4*>(t.v + e0 + 4 * h) = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
-      }
-      if constexpr (sizeof(T) == 2) {
-        u32x4 pw;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pw[q] = uint32_t(f2bf(p[2 * q])) | (uint32_t(f2bf(p[2 * q + 1])) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(t.p) + e0) = pw;
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<f32x4*>(static_cast<float*>(t.p) + e0 + 4 * h) =
-              f32x4{p[4 * h], p[4 * h + 1], p[4 * h + 2], p[4 * h + 3]};
-      }
+  // two vectors per thread per pass, both loaded before either is updated
+  constexpr int64_t kPass = int64_t(kThreads) * kVec;
+  for (int64_t e0 = base + int64_t(threadIdx.x) * kVec; e0 < end; e0 += 2 * kPass) {
+    const int64_t e1 = e0 + kPass;
+    if (t.vec && e1 + kVec <= end) {
+      Vec8 x, y;
+      load8<T>(t, e0, x);
+      load8<T>(t, e1, y);
+      update8(x, k);
+      update8(y, k);
+      store8<T>(t, e0, x);
+      store8<T>(t, e1, y);
     } else {
-      const int64_t e1 = e0 + kVec < end ? e0 + kVec : end;
-      for (int64_t e = e0; e < e1; ++e) {
-        float m = t.m[e], v = t.v[e];
-        const float p = adam_elem(PElem<T>::load(t.p, e), PElem<T>::load(t.g, e), m, v, k);
-        t.m[e] = m;
-        t.v[e] = v;
-        PElem<T>::store(t.p, e, p);
-      }
+      run8<T>(t, e0, end, k);
+      if (e1 < end) run8<T>(t, e1, end, k);
     }
   }
 }
