@@ -940,6 +940,39 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
   return r;
 }
 
+// Mixed-precision FMAs (v_fma_mix*) for the fp16 update epilogue: each one
+// rounds once, so the split below is exactly hi = RN16(x), lo = RN16((x -
+// hi) 2^11) of x = fma(a', lo_old, acc) in fp32, with no separate
+// conversions or packing. VALU-only asm (no memory access).
+//   mix_l / mix_h:  a * f16(low / high half of h) + c, as fp32
+//   sub_l / sub_h:  x - f16(low / high half of h), as fp32 (exact here)
+//   pk16:           RN16(x0 s) | RN16(x1 s) << 16
+__device__ __forceinline__ float mix_l(float a, uint32_t h, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float mix_h(float a, uint32_t h, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float sub_l(float x, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float sub_h(float x, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk16(float x0, float x1, float s) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0\n\tv_fma_mixhi_f16 %0, %2, %3, 0" : "=&v"(r) : "v"(x0), "v"(x1), "v"(s));
+  return r;
+}
+
 // POLY: acc[i][J] += f A[m][n] at this lane's accumulator positions of
 // column block J, read from the row-operand half of the stage at `st`, which
 // holds A[m][k] for the 32 k that are these n (the caller picks the stage).
@@ -1302,6 +1335,36 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
           for (int g = 0; g < 4; ++g) lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
     }
     const float a2 = P.a * (1.f / 2048.f);
+    if constexpr (F16 && !LAST) {
+      // X' = B' hi + a 2^-11 lo (B' = a I + B carries a hi), split back into
+      // hi (staged straight into the LDS tile, the ring is free) and lo
+      // (stored in accumulator order), two values per packed register
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t hp[2], lp[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const uint32_t l = q ? lv[i][j][g].y : lv[i][j][g].x;
+              const float v0 = e16::mix_l(a2, l, acc[i][j][4 * g + 2 * q]);
+              const float v1 = e16::mix_h(a2, l, acc[i][j][4 * g + 2 * q + 1]);
+              hp[q] = e16::pk16(v0, v1, 1.f);
+              lp[q] = e16::pk16(e16::sub_l(v0, hp[q]), e16::sub_h(v1, hp[q]), 2048.f);
+            }
+            *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) = make_uint2(lp[0], lp[1]);
+            *reinterpret_cast<uint2*>(lds + soff(wm * 128 + 32 * i + l32, wn * 8 + 4 * j + g) + lh * 8) =
+                make_uint2(hp[0], hp[1]);
+          }
+      __syncthreads();
+      uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
+      rows_out([&](int m, int n, const uint4& v) {
+        *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
+      });
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x2 hv[2][4];
