@@ -2,21 +2,23 @@
 //
 //   momentum_kernel   buf' = mu buf + G, u = G + mu buf' | buf' | G, and one
 //                     fixed-order sum of u^2 per work item        (HBM-bound)
-//   normalize_kernel  X0 = u / (sqrt(sum u^2) + eps) written in the
-//                     rows<=cols orientation as fp32 master + operand copy,
-//                     zero-padded to 128-multiples                 (HBM-bound)
-//   gemm_kernel<GRAM>   A = X X^T           upper-triangle tiles, mirrored
-//   gemm_kernel<POLY>   B = b A + c A A     upper-triangle tiles, mirrored
-//   gemm_kernel<UPDATE> X = a X + B X       (last step writes `out`)
+//   normalize_kernel  X0 = u / (sqrt(sum u^2) + eps) in the rows<=cols
+//                     orientation, zero-padded: fp32 sets an fp32 master,
+//                     bf16 sets a 16-bit operand (hi, in 32-column panels)
+//                     and a low part (lo)                          (HBM-bound)
+//   gemm*_kernel<GRAM>   A = X X^T          upper-triangle tiles, mirrored
+//   gemm*_kernel<POLY>   B = b A + c A A    upper-triangle tiles, mirrored
+//   gemm*_kernel<UPDATE> X = a X + B X      the last step writes `out`, or
+//                                           applies X to the weights
 //
-// The three matrix-core kernels share one 128 x 128 output-tile engine:
-// 4 waves of 64 lanes, each wave owning a 64 x 64 sub-tile made of 4 x 4
-// v_mfma_f32_16x16x32_{f16,bf16} (bf16 sets; fp16 operands by default) or
-// v_mfma_f32_16x16x4_f32 (fp32 sets) accumulators. Operands are staged through LDS as [row][k] tiles of
-// 128 rows x 128 bytes (16-byte chunks XOR-swizzled against bank conflicts);
-// the next k-slab is prefetched into registers while the current one is
-// multiplied. Operands whose k index runs along memory rows (X in B X) are
-// transposed in registers on their way into LDS.
+// Two matrix-core engines:
+//  - gemm32_kernel (fp32 sets): 128 x 128 output tiles, 4 waves each owning
+//    64 x 64 as 4 x 4 v_mfma_f32_16x16x4_f32 accumulators, operands staged
+//    through LDS from registers (the next k-slab prefetched while the
+//    current one is multiplied).
+//  - gemm16_kernel (bf16 sets; fp16 operands by default): 256 x 256 output
+//    tiles, 8 waves, operands DMA'd straight into a 4-stage LDS ring (see
+//    the section below).
 //
 // Every launch takes a schedule of work items; block b runs item b. The
 // schedules keep one matrix's tiles on one XCD (block b runs on XCD b % 8).
@@ -706,12 +708,13 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
 //   C[m][n], m = row0 + 32 i + l % 32, n = col0 + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4,
 // i.e. runs of 4 consecutive output columns: vector epilogue loads/stores.
 //
-// k advances in stages of 32. Operands go from global memory straight into
-// a ring of NS LDS stages (global_load_lds_dwordx4: lane i of a 1 KB piece
-// writes base + 16 i, so the bank swizzle is applied by choosing which
-// global 16-byte chunk lane i fetches). While stage g is multiplied, stages
-// g+1 .. g+NS-2 are in flight and stage g+NS-1 is issued into the slot that
-// stage g-1 freed; one barrier per stage.
+// k advances in stages of 32. Operands (stored in 32-column panels, so a
+// stage of one operand is whole 128-byte lines) go from global memory
+// straight into a ring of NS LDS stages (global_load_lds_dwordx4: lane i of
+// a 1 KB piece writes base + 16 i, so the bank swizzle is applied by choosing
+// which global 16-byte chunk lane i fetches). While stage g is multiplied,
+// stages g+1 .. g+NS-2 are in flight and the slot that stage g-1 freed is
+// refilled, its DMA spread over the two k-steps; one barrier per stage.
 //   Row operand (k contiguous in memory): [row][k], 64-byte rows.
 //   Column operand, k contiguous (Gram, A A): [col][k], 64-byte rows.
 //   Column operand, k along memory rows (X in B X): [k][col], 512-byte rows,
