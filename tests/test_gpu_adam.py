@@ -164,3 +164,16 @@ def test_adam_validation():
     plan.step(lr=1e-3, beta1=0.9, beta2=0.99, eps=1e-8, wd=0.0, step=1)
     torch.cuda.synchronize()
     plan.destroy()
+
+
+def test_adam_empty_and_zero_sized_lists():
+    """An empty list and a list of only empty tensors plan and step as no-ops."""
+    plan = mu.AdamPlan([], [], [], [])
+    plan.step(lr=1e-3, beta1=0.9, beta2=0.99, eps=1e-8, wd=0.0, step=1)
+    plan.destroy()
+    e = [torch.empty(0, dtype=torch.bfloat16, device=DEV)]
+    m = [torch.empty(0, dtype=torch.float32, device=DEV)]
+    plan = mu.AdamPlan(e, e, m, m)
+    plan.step(lr=1e-3, beta1=0.9, beta2=0.99, eps=1e-8, wd=0.0, step=1)
+    torch.cuda.synchronize()
+    plan.destroy()

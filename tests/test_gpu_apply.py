@@ -149,3 +149,23 @@ def test_apply_validation():
     plan.step_apply(cfg, 0.1, 0.1)
     torch.cuda.synchronize()
     plan.destroy()
+
+
+def test_apply_without_momentum_state():
+    """A plan without momentum buffers (mu = 0) applies X0's orthogonalisation
+    of the raw gradient; checked against the oracle with mu = 0."""
+    shapes = [(384, 640), (640, 384)]
+    grads, _, ws = make_set(shapes, "bf16", seed=8)
+    g64 = [to_f64(g) for g in grads]
+    w64 = [to_f64(w) for w in ws]
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, None, outs)
+    plan.set_weights(ws, [1.0, 2.0], [1.0, 0.0])
+    plan.step_apply(mu.make_config(*QUINTIC, 5, 0.0, False, 1e-7), 0.3, 0.2)
+    torch.cuda.synchronize()
+    plan.destroy()
+    for i, (lm, wm) in enumerate([(1.0, 1.0), (2.0, 0.0)]):
+        want, x, _ = oracle_apply(g64[i], None, w64[i], 5, 0.3, 0.2, lm, wm, "bf16", momentum=0.0,
+                                  nesterov=False)
+        bound = BAR["bf16"] * np.linalg.norm(f32(0.3) * f32(lm) * x) + ROUND["bf16"] * np.linalg.norm(want)
+        assert np.linalg.norm(to_f64(ws[i]) - want) <= bound
