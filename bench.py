@@ -38,12 +38,12 @@ def kernel_work(shapes, steps, dtype):
     {kernel: (flops, bytes)}.
 
     Bytes count each operand read once and each result written once, in the
-    library's formats: bf16 sets keep X as two 16-bit halves (high part = the
-    matrix-core operand, low part = the residual) and A, B as 16-bit; fp32
-    sets keep everything in fp32. The Newton-Schulz kernels run `steps` times;
-    the last update writes `out` instead of X's halves."""
+    library's formats: bf16 sets (fp16 operands) keep X as a 16-bit high part
+    (the matrix-core operand) and a one-byte low part (the residual), and A, B
+    as 16-bit; fp32 sets keep everything in fp32. The Newton-Schulz kernels
+    run `steps` times; the last update writes `out` instead of X's parts."""
     es = 2 if dtype == "bf16" else 4
-    xb = 4                                  # X per element: hi + lo halves, or fp32
+    xb = 3 if dtype == "bf16" else 4        # X per element: hi + lo byte, or fp32
     xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
     w = {k: [0.0, 0.0] for k in ("momentum", "normalize", "gram", "poly", "update")}
     for r, c in shapes:

@@ -246,14 +246,15 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
  * rows<=cols orientation, zero-padded to mp x np (X) or mp x mp (A, B),
  * with mp and np the tile multiples (256 for bf16 sets, 128 for fp32
  * sets). bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
- * matrix-core operand, ping-pong between steps) and x_lo the low part in
- * the same format (X = hi + lo * 2^-11 for fp16 operands, hi + lo for bf16
- * operands); gram (A) and poly are 16-bit. The three 16-bit operands
- * (x_op0/x_op1, gram, poly) are stored in 32-column panels: element (r, c)
- * is at element index ((c / 32) * mp + r) * 32 + c % 32. With fp16
- * operands poly holds a I + B (the a X term of the high part rides in the
- * product) and x_lo is stored in the update kernel's accumulator order;
- * with bf16 operands x_lo is row-major. fp32 sets: x_op0/x_op1 are fp32 X
+ * matrix-core operand, ping-pong between steps) and x_lo the low part.
+ * fp16 operands: one signed byte q per element, X = hi + q * 2^(e - 33)
+ * with e = max(E, 1) and E the 5-bit exponent field of hi, stored in the
+ * update kernel's accumulator order (per 256 x 256 tile, 32-row blocks of
+ * 8 KB). bf16 operands: a bf16 lo, X = hi + lo, row-major. gram (A) and
+ * poly are 16-bit. The three 16-bit operands (x_op0/x_op1, gram, poly) are
+ * stored in 32-column panels: element (r, c) is at element index
+ * ((c / 32) * mp + r) * 32 + c % 32. With fp16 operands poly holds a I + B
+ * (the a X term of the high part rides in the product). fp32 sets: x_op0/x_op1 are fp32 X
  * (ping-pong), gram/poly (B) fp32, all row-major, x_lo = -1. After a step
  * of k iterations X is in x_op[k % 2]. */
 typedef struct {

@@ -80,18 +80,31 @@ template <> struct Op<OP_F32> {
 };
 template <> struct Op<OP_F16> {
   static constexpr int bytes = 2;
-  // X = hi + lo * 2^-11: hi is the operand, lo the scaled residual (about
-  // 22 significant bits together; the scaling keeps lo out of subnormals)
-  static __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
-    const _Float16 h = static_cast<_Float16>(x);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x - static_cast<float>(h)) * 2048.f));
-  }
-  static __device__ __forceinline__ float join(uint32_t hi, uint32_t lo) {
-    return __fmaf_rn(load16(lo), 1.f / 2048.f, load16(hi));
-  }
   static __device__ __forceinline__ float load16(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+  }
+  // The X master of fp16-operand sets: X = hi + lo 2^-18 with hi = RN16(X)
+  // and lo one byte, the OCP e4m3 rounding (to nearest even) of
+  // (X - hi) 2^18: 4 significant bits below hi's last one. |X - hi| <=
+  // ulp(hi) / 2 = 2^-11 for |X| < 2 keeps |lo| <= 2^7; larger residuals are
+  // clamped to the format's largest finite value, 448, first (the
+  // conversion would make them NaN).
+  static constexpr float kLoScale = 262144.f;  // 2^18
+  // the four lo bytes of residuals r0..r3 (x - hi, exact in fp32), byte q
+  // holding r_q
+  static __device__ __forceinline__ uint32_t lo4(float r0, float r1, float r2, float r3) {
+    auto c = [](float r) { return fminf(fmaxf(r * kLoScale, -448.f), 448.f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(r0), c(r1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c(r2), c(r3), w, true);
+    return static_cast<uint32_t>(w);
+  }
+  // the four lo bytes of w as floats (lo, not yet scaled by 2^-18)
+  static __device__ __forceinline__ void lo_vals(uint32_t w, float (&v)[4]) {
+    const int x = static_cast<int>(w);
+    v[0] = __builtin_amdgcn_cvt_f32_fp8(x, 0);
+    v[1] = __builtin_amdgcn_cvt_f32_fp8(x, 1);
+    v[2] = __builtin_amdgcn_cvt_f32_fp8(x, 2);
+    v[3] = __builtin_amdgcn_cvt_f32_fp8(x, 3);
   }
   static __device__ __forceinline__ uint16_t bits(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));  // RNE
@@ -245,20 +258,20 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
 // out row-major, zeros in the padding. With zero steps the scaled values go
 // straight to `out` in the caller's layout.
 
-// fp16 operand sets keep the low part of X in the update kernel's
-// accumulator order: per 256 x TN tile, per wave (2 x TN/64 waves of
-// 128 x 64), per accumulator group (i, j, g) a contiguous 64-lane x
-// 4-element block. Lane loads and stores of the update epilogue are then
-// contiguous across the wave. Element index of X(m, n) in that layout
-// (np = padded row length):
-__device__ __forceinline__ int64_t lo_index(int m, int n, int np) {
+// fp16 operand sets keep the low byte of X (Op<OP_F16>::lo4) in the update
+// kernel's accumulator order: per 256 x TN tile (TM * TN bytes), per 32-row
+// block u, per wave column wn and accumulator column block j, a 1 KB run
+// holds 16 bytes per lane: lane l32 + 32 lh has row 32 u + l32, columns
+// 64 wn + 32 j + 8 g + 4 lh + r at byte 4 g + r. One 16-byte load or store
+// per lane and accumulator block, contiguous across the wave. Byte offset
+// of X(m, n) (np = padded row length):
+__device__ __forceinline__ int64_t lo8_index(int m, int n, int np) {
   constexpr int TN = kTileN16, WN = TN / 64;
   const int tile = (m >> 8) * (np / TN) + n / TN;
   const int mm = m & 255, nn = n % TN;
-  const int wave = (mm >> 7) * WN + (nn >> 6);
   const int lane = (mm & 31) + 32 * ((nn >> 2) & 1);
-  const int grp = (((mm >> 5) & 3) * 2 + ((nn >> 5) & 1)) * 4 + ((nn >> 3) & 3);
-  return (((int64_t(tile) * 2 * WN + wave) * 32 + grp) * 64 + lane) * 4 + (nn & 3);
+  return ((((int64_t(tile) * 8 + (mm >> 5)) * WN + (nn >> 6)) * 2 + ((nn >> 5) & 1)) * 64 + lane) * 16 +
+         ((nn >> 3) & 3) * 4 + (nn & 3);
 }
 
 template <typename T, int OP>
@@ -375,9 +388,14 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
       u32x4_t whi, wlo;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t h0, l0, h1, l1;
-        Op<OP>::split(u[h][2 * q], h0, l0);
-        Op<OP>::split(u[h][2 * q + 1], h1, l1);
+        uint32_t h0, l0 = 0, h1, l1 = 0;
+        if constexpr (OP == OP_F16) {  // the low bytes go out below
+          h0 = Op<OP>::bits(u[h][2 * q]);
+          h1 = Op<OP>::bits(u[h][2 * q + 1]);
+        } else {
+          Op<OP>::split(u[h][2 * q], h0, l0);
+          Op<OP>::split(u[h][2 * q + 1], h1, l1);
+        }
         whi[q] = h0 | (h1 << 16);
         wlo[q] = l0 | (l1 << 16);
       }
@@ -393,10 +411,11 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
     }
   }
   if constexpr (OP == OP_F16) {
-    // Low part in accumulator order. A 32-row x 64-column block (this tile
-    // holds two) is one contiguous 4 KB run of that layout; thread t writes
-    // its bytes 16 t .. 16 t + 15, which hold columns 32 j + 8 g + 4 h .. +3
-    // (q = j * 4 + g = t / 32, h = lane bit 5) of rows 2 t % 32 and the next.
+    // Low bytes in accumulator order. Each 32-row half of this tile is one
+    // contiguous 2 KB run of that layout (64 columns: one wave column, both
+    // column blocks j); thread t writes the 16 bytes of lane t % 64 of block
+    // j = t / 64 % 2 of half b = t / 128: row 32 b + t % 32, columns
+    // 32 j + 8 g + 4 (t / 32 % 2) + r at byte 4 g + r.
     __syncthreads();  // the tall path above has finished reading the tile
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -405,27 +424,21 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
       for (int e = 0; e < 8; ++e) tile[v >> 3][(v & 7) * 8 + e] = u[h][e];
     }
     __syncthreads();
-    uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
-    const int t = threadIdx.x, q = t >> 5, lane0 = (2 * t) & 63;
-    const int col = 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane0 >> 5);
+    const int t = threadIdx.x, b = t >> 7, j = (t >> 6) & 1, ln = t & 63;
+    const int row = 32 * b + (ln & 31), col = 32 * j + 4 * (ln >> 5);
+    uint32_t w[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      uint32_t w[4];
+    for (int g = 0; g < 4; ++g) {
+      float r[4];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int row = 32 * b + ((lane0 + d) & 31);
-        uint32_t l[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t hh;
-          Op<OP>::split(tile[row][col + r], hh, l[r]);
-        }
-        w[2 * d] = l[0] | (l[1] << 16);
-        w[2 * d + 1] = l[2] | (l[3] << 16);
+      for (int q = 0; q < 4; ++q) {
+        const float x = tile[row][col + 8 * g + q];
+        r[q] = x - Op<OP>::load16(Op<OP>::bits(x));
       }
-      *reinterpret_cast<u32x4_t*>(lo + lo_index(i0 + 32 * b, j0, M.np) + 8 * t) =
-          u32x4_t{w[0], w[1], w[2], w[3]};
+      w[g] = Op<OP>::lo4(r[0], r[1], r[2], r[3]);
     }
+    char* lo = A.ws + M.xl_off + lo8_index(i0 + 32 * b, j0, M.np);
+    *reinterpret_cast<u32x4_t*>(lo + (j * 64 + ln) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -944,22 +957,10 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
 }
 
 // Mixed-precision FMAs (v_fma_mix*) for the fp16 update epilogue: each one
-// rounds once, so the split below is exactly hi = RN16(x), lo = RN16((x -
-// hi) 2^11) of x = fma(a', lo_old, acc) in fp32, with no separate
-// conversions or packing. VALU-only asm (no memory access).
-//   mix_l / mix_h:  a * f16(low / high half of h) + c, as fp32
+// rounds once, so hi = RN16(x) and the residual x - hi come out with no
+// separate conversions or packing. VALU-only asm (no memory access).
 //   sub_l / sub_h:  x - f16(low / high half of h), as fp32 (exact here)
 //   pk16:           RN16(x0 s) | RN16(x1 s) << 16
-__device__ __forceinline__ float mix_l(float a, uint32_t h, float c) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float mix_h(float a, uint32_t h, float c) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
-  return r;
-}
 __device__ __forceinline__ float sub_l(float x, uint32_t h) {
   float r;
   asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
@@ -1313,101 +1314,98 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
       }
     });
   } else {
-    // UPDATE. The low part of X is read (and, unless this is the last step,
-    // written back) in accumulator order for fp16 operands; for bf16
-    // operands it is row-major and read at the accumulator positions.
-    const int64_t ldx = M.np;
-    uint16_t* lo_t = reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
-                     (((int64_t(TI) * (M.np / TN) + TJ) * NWAVE + wave) * 32) * 256 + lane * 4;
-    const uint16_t* hi_cur = reinterpret_cast<const uint16_t*>(P.ws + M.xo_cur);
-    auto lo_ptr = [&](int i, int j, int g) -> uint16_t* {
-      if constexpr (F16) return lo_t + ((i * 2 + j) * 4 + g) * 256;
-      else
-        return reinterpret_cast<uint16_t*>(P.ws + M.xl_off) +
-               int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j + 8 * g + 4 * lh;
-    };
-    // fp16 operands: all loads first (one latency for the tile); bf16
-    // operands (two parts to read) load one row group at a time.
-    u32x2 lv[4][2][4];
+    // UPDATE. fp16 operands: the low bytes are read (and, unless this is
+    // the last step, written back) in accumulator order, one 16-byte access
+    // per lane and accumulator block, all loads first (one latency for the
+    // tile). bf16 operands: the low part is row-major and read at the
+    // accumulator positions with the high part, one row group at a time.
     if constexpr (F16) {
+      char* lo_t = P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) + lane * 16;
+      auto lo_ptr = [&](int i, int j) { return lo_t + (((wm * 4 + i) * WN + wn) * 2 + j) * 1024; };
+      u32x4 lq[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
-    }
-    const float a2 = P.a * (1.f / 2048.f);
-    if constexpr (F16 && !LAST) {
-      // X' = B' hi + a 2^-11 lo (B' = a I + B carries a hi), split back into
-      // hi (staged straight into the LDS tile, the ring is free) and lo
-      // (stored in accumulator order), two values per packed register
+        for (int j = 0; j < 2; ++j) lq[i][j] = *reinterpret_cast<const u32x4*>(lo_ptr(i, j));
+      // X' = B' hi + a 2^-18 lo  (B' = a I + B carries a hi)
+      const float as = P.a * (1.f / Op<OP>::kLoScale);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          uint32_t qw[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            uint32_t hp[2], lp[2];
+            float lv[4];
+            Op<OP>::lo_vals(lq[i][j][g], lv);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const uint32_t l = q ? lv[i][j][g].y : lv[i][j][g].x;
-              const float v0 = e16::mix_l(a2, l, acc[i][j][4 * g + 2 * q]);
-              const float v1 = e16::mix_h(a2, l, acc[i][j][4 * g + 2 * q + 1]);
-              hp[q] = e16::pk16(v0, v1, 1.f);
-              lp[q] = e16::pk16(e16::sub_l(v0, hp[q]), e16::sub_h(v1, hp[q]), 2048.f);
+            for (int r = 0; r < 4; ++r) acc[i][j][4 * g + r] = __fmaf_rn(as, lv[r], acc[i][j][4 * g + r]);
+            if constexpr (!LAST) {
+              // split back into hi (staged straight into the LDS tile, the
+              // ring is free) and the low bytes; x - hi is exact (sub_l/h)
+              uint32_t hp[2];
+              float rs[4];
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const float v0 = acc[i][j][4 * g + 2 * q], v1 = acc[i][j][4 * g + 2 * q + 1];
+                hp[q] = e16::pk16(v0, v1, 1.f);
+                rs[2 * q] = e16::sub_l(v0, hp[q]);
+                rs[2 * q + 1] = e16::sub_h(v1, hp[q]);
+              }
+              qw[g] = Op<OP>::lo4(rs[0], rs[1], rs[2], rs[3]);
+              *reinterpret_cast<uint2*>(lds + soff(wm * 128 + 32 * i + l32, wn * 8 + 4 * j + g) + lh * 8) =
+                  make_uint2(hp[0], hp[1]);
             }
-            *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) = make_uint2(lp[0], lp[1]);
-            *reinterpret_cast<uint2*>(lds + soff(wm * 128 + 32 * i + l32, wn * 8 + 4 * j + g) + lh * 8) =
-                make_uint2(hp[0], hp[1]);
           }
-      __syncthreads();
-      uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
-      rows_out([&](int m, int n, const uint4& v) {
-        *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
-      });
-      return;
-    }
+          if constexpr (!LAST) *reinterpret_cast<u32x4*>(lo_ptr(i, j)) = u32x4{qw[0], qw[1], qw[2], qw[3]};
+        }
+      if constexpr (!LAST) {
+        __syncthreads();
+        uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
+        rows_out([&](int m, int n, const uint4& v) {
+          *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
+        });
+        return;
+      }
+    } else {
+      const int64_t ldx = M.np;
+      const uint16_t* hi_cur = reinterpret_cast<const uint16_t*>(P.ws + M.xo_cur);
+      auto lo_ptr = [&](int i, int j, int g) -> uint16_t* {
+        return reinterpret_cast<uint16_t*>(P.ws + M.xl_off) + int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j +
+               8 * g + 4 * lh;
+      };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 hv[2][4];
-      if constexpr (!F16) {
+      for (int i = 0; i < 4; ++i) {
+        u32x2 lv[2][4], hv[2][4];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            lv[i][j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
+            lv[j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
             hv[j][g] = *reinterpret_cast<const u32x2*>(
                 hi_cur + pidx(mb + 32 * i + l32, nb + 32 * j + 8 * g + 4 * lh, M.mp));
           }
-      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t lw[4] = {lv[i][j][g].x & 0xffffu, lv[i][j][g].x >> 16,
-                                  lv[i][j][g].y & 0xffffu, lv[i][j][g].y >> 16};
-          if constexpr (F16) {
-            // X' = B' hi + a 2^-11 lo  (B' = a I + B carries a hi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j][4 * g + r] = __fmaf_rn(a2, Op<OP>::load16(lw[r]), acc[i][j][4 * g + r]);
-          } else {
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t lw[4] = {lv[j][g].x & 0xffffu, lv[j][g].x >> 16, lv[j][g].y & 0xffffu,
+                                    lv[j][g].y >> 16};
             // X' = B hi + a (hi + lo)
             const uint32_t hw[4] = {hv[j][g].x & 0xffffu, hv[j][g].x >> 16, hv[j][g].y & 0xffffu,
                                     hv[j][g].y >> 16};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               acc[i][j][4 * g + r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), acc[i][j][4 * g + r]);
-          }
-          if constexpr (!LAST) {
-            uint32_t nh[4], nl[4];
+            if constexpr (!LAST) {
+              uint32_t nh[4], nl[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Op<OP>::split(acc[i][j][4 * g + r], nh[r], nl[r]);
-            *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) =
-                make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
+              for (int r = 0; r < 4; ++r) Op<OP>::split(acc[i][j][4 * g + r], nh[r], nl[r]);
+              *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) =
+                  make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
+            }
           }
-        }
+      }
     }
     if constexpr (!LAST) {
       // the next high part (the operand of the next step), rows of the tile

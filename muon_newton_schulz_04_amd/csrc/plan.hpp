@@ -34,8 +34,9 @@ struct MatInfo {
   int32_t mp, np;    // m, n padded to the engine's tile multiples
   int32_t tall;      // rows > cols: the iteration runs on the transpose
   int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
-  int64_t xl_off;    // bf16 sets: low part of X (X = hi + lo * 2^-11 for fp16
-                     // operands, hi + lo for bf16 operands), -1 otherwise
+  int64_t xl_off;    // bf16 sets: low part of X (one signed byte per element
+                     // for fp16 operands, a bf16 lo for bf16 operands; sized
+                     // for the latter), -1 otherwise
   int64_t xo_off[2]; // bf16 sets: ping-pong high parts (the matrix-core
                      // operand); fp32 sets: ping-pong fp32 X
   int64_t a_off;     // A = X X^T
