@@ -179,6 +179,63 @@ def test_gram_is_bitwise_symmetric_and_padding_zero():
     plan.destroy()
 
 
+def lo_byte_index(mp, np_):
+    """Byte offset of X(m, n) in the fp16 path's low-byte layout: per 256 x 256
+    tile (row-major over tiles), per 32-row block u, per 64-column wave
+    column wn and 32-column block j, 64 lanes x 16 bytes; lane l32 + 32 lh
+    holds row 32 u + l32, columns 64 wn + 32 j + 8 g + 4 lh + r at byte
+    4 g + r."""
+    m = np.arange(mp)[:, None]
+    n = np.arange(np_)[None, :]
+    tile = (m // 256) * (np_ // 256) + n // 256
+    mm, nn = m % 256, n % 256
+    lane = mm % 32 + 32 * ((nn // 4) % 2)
+    return (((((tile * 8 + mm // 32) * 4 + nn // 64) * 2 + (nn // 32) % 2) * 64 + lane) * 16
+            + ((nn // 8) % 4) * 4 + nn % 4)
+
+
+@pytest.mark.parametrize("prec", [0, 1], ids=["fp16ops", "bf16ops"])
+def test_x0_master_parts(prec):
+    """After a one-step call the workspace still holds X0 (the last update
+    reads it and writes `out`): its high part (panels) plus its low part
+    must give the oracle's X0 = u / (||u|| + eps) to the format's precision.
+    fp16 operands: X = hi + e4m3 byte * 2^-18, |error| <= ulp16(x) / 32 <=
+    2^-15 |x|, the e4m3 rounding (4 significant bits) of a residual of at
+    most half an ulp. bf16 operands:
+    X = hi + lo, two bf16 roundings (8 significant bits each): |x - hi| <=
+    2^-8 |x|, so |error| <= 2^-16 |x|."""
+    shapes = [(200, 333), (333, 200), (256, 512), (40, 700)]
+    grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=9, shapes=shapes)]
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, None, outs)
+    ws = plan.step(mu.make_config(*QUINTIC, 1, precision=prec))
+    torch.cuda.synchronize()
+    for i, g in enumerate(grads):
+        info = plan.buffer_info(i)
+        m, n, mp, np_ = info["m"], info["n"], info["mp"], info["np"]
+        x0 = oracle.frobenius_normalize(to_f64(g), 1e-7)
+        if g.shape[0] > g.shape[1]:
+            x0 = x0.T
+        want = np.zeros((mp, np_))
+        want[:m, :n] = x0
+        off = info["x_op0"]
+        if prec == 0:
+            hi = unpanel(ws[off: off + mp * np_ * 2].view(torch.float16), mp, np_).double().cpu().numpy()
+            lob = ws[info["x_lo"]: info["x_lo"] + mp * np_].cpu().numpy()[lo_byte_index(mp, np_)]
+            lo = torch.from_numpy(np.ascontiguousarray(lob)).view(torch.float8_e4m3fn).double().numpy()
+            got = hi + lo * 2.0 ** -18
+            bound = 1.1 * 2.0 ** -15 * np.abs(want) + 2.0 ** -26
+        else:
+            hi = unpanel(ws[off: off + mp * np_ * 2].view(torch.bfloat16), mp, np_).double().cpu().numpy()
+            lo = ws[info["x_lo"]: info["x_lo"] + mp * np_ * 2].view(torch.bfloat16).view(mp, np_)
+            got = hi + lo.double().cpu().numpy()
+            bound = 1.1 * 2.0 ** -16 * np.abs(want) + 2.0 ** -60
+        err = np.abs(got - want)
+        assert np.all(err <= bound), (i, float(np.max(err / (bound))))
+        assert not np.any(got[m:, :]) and not np.any(got[:, n:])   # padding stays zero
+    plan.destroy()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_deterministic_odd_and_scale_invariant(dtype):
     shapes = [(256, 640), (640, 256)]
