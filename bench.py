@@ -204,6 +204,31 @@ def main():
     kt = plan.kernel_times()
     plan.set_timing(False)
 
+    # one rank's share of an 8-GPU data-parallel step: the matrices rank 0
+    # owns (ownership by algorithmic flops), through the same library; the
+    # reduce-scatter and all-gather around it need more GPUs than this run has
+    from workloads import matrix_flops, owner_split
+    world_d = 8
+    share = owner_split(wl.shapes, world_d)[0]
+    splan = mu.MuonPlan([grads[i] for i in share], [bufs[i] for i in share] if bufs else None,
+                        [outs[i] for i in share])
+    sws = torch.empty(splan.workspace_bytes, dtype=torch.uint8, device=dev)
+    s_steps = max(10, args.steps // 2)
+    for _ in range(3):
+        splan.step(cfg, sws, stream)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(s_steps):
+        splan.step(cfg, sws, stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    s_ms = s0.elapsed_time(s1) / s_steps
+    s_falg = wl.steps * sum(matrix_flops(*wl.shapes[i]) for i in share)
+    s_bytes = sum(grads[i].numel() * grads[i].element_size() for i in share)
+    splan.destroy()
+    del sws
+
     # the next row beside the path: the same step with the weight application
     # fused into the last update (W read and written instead of out written)
     gen = torch.Generator(device="cpu").manual_seed(1234)
@@ -302,7 +327,14 @@ def main():
         "wall_s_timed": wall,
         "kernels": per_kernel,
         "roofline": roof,
-        "next": {"weight_apply": {
+        "next": {"rank_share": {
+            "world": world_d, "rank": 0, "matrices": len(share),
+            "shapes": sorted({tuple(wl.shapes[i]) for i in share}),
+            "ms_per_step": s_ms, "steps": s_steps, "TFLOP/s": s_falg / (s_ms * 1e-3) / 1e12,
+            "grad_bytes_owned": s_bytes,
+            "note": "muon_step on one rank's matrices of an 8-way sharded step; the "
+                    "reduce-scatter / all-gather around it are not run (one GPU)"},
+            "weight_apply": {
             "ms_per_step": ms_apply, "steps": 3 * n_apply,
             "plain_ms_per_step_same_blocks": ms_plain_b,
             "extra_us_vs_plain_step": (ms_apply - ms_plain_b) * 1e3,

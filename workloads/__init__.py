@@ -13,6 +13,7 @@ from .generators import (  # noqa: F401
     make_workload,
     to_f64,
 )
+from .sharding import matrix_flops, owner_split  # noqa: F401
 from .adam import (  # noqa: F401
     gpt2_124m_adam_shapes,
     gpt2_124m_adam_multipliers,
