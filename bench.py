@@ -4,7 +4,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--no-cpu-baseline] [--cpu-budget SECONDS] [--calibrate-copy]
 
 A step is one muon_plan_step over all matrices of the workload (momentum,
-normalisation and k Newton-Schulz steps), inputs resident in HBM. `value` is
+normalisation and k Newton-Schulz steps), inputs resident in HBM, one plan
+over fixed gradient buffers as in training (the momentum buffers evolve from
+step to step). `step_ms` gives the spread of single steps from a separate
+pass with events around each step. `value` is
 algorithmic TFLOP/s of the whole step; `roofline` describes the kernel with
 the largest share of the step's time, timed with HIP events recorded around
 each launch in a second pass of the same length (in that pass the launches
@@ -174,6 +177,8 @@ def main():
     wl = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # one plan over fixed gradient buffers, as in training (backward rewrites
+    # the same .grad tensors every step); the momentum buffers evolve
     grads = [g.to(dev) for g in make_gradients(wl, step=0, device="cpu")]
     bufs = [torch.zeros_like(g) for g in grads] if wl.momentum else None
     outs = [torch.empty_like(g) for g in grads]
@@ -182,18 +187,29 @@ def main():
     cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         plan.step(cfg, ws, stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         plan.step(cfg, ws, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+
+    # spread of single steps: a pass of the same length with events around
+    # every step (outside the timed region above)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i, (a0, a1) in enumerate(ev):
+        a0.record(stream)
+        plan.step(cfg, ws, stream)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([a0.elapsed_time(a1) for a0, a1 in ev])
 
     # second pass of the same length with per-launch HIP events
     plan.set_timing(True)
@@ -324,6 +340,9 @@ def main():
                    "nesterov": wl.nesterov, "falg_gflop_per_step": falg / 1e9},
         "pct_bf16_dense_peak": 100.0 * value / PEAK["bf16"],
         "matrices_per_s": wl.n_matrices / (ms * 1e-3),
+        "step_ms": {"n": int(step_ms.size), "mean": float(step_ms.mean()),
+                    "sd": float(step_ms.std(ddof=1)) if step_ms.size > 1 else 0.0,
+                    "min": float(step_ms.min())},
         "wall_s_timed": wall,
         "kernels": per_kernel,
         "roofline": roof,
