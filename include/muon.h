@@ -222,7 +222,13 @@ typedef enum {
  * row, tile col, 0} of the tiles on or above the diagonal; update: {matrix,
  * tile row, tile col, 0}; matrix-core tiles are 256 x 256 for bf16 sets and
  * 128 x 128 for fp32 sets), in launch order with empty slots as
- * {-1,-1,-1,-1}.
+ * {-1,-1,-1,-1}. Small bf16 sets whose longest Gram tiles would set the
+ * Gram launch's time split those tiles' k range into S parts: such a tile
+ * has S gram items with c = pbase << 16 | s << 8 | S (s = 0 .. S-1), each
+ * writing an fp32 partial tile to the workspace, and kind == MUON_K_COUNT
+ * queries the second Gram pass that sums them, four items {matrix, tile
+ * row, tile col, pbase << 16 | q << 8 | S} per split tile, one per 128 x 128
+ * quarter q (empty when nothing splits).
  * Writes min(cap, count) items to `items` (may be NULL when cap == 0) and
  * the total to *count. No device calls. */
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,

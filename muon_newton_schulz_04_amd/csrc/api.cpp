@@ -27,8 +27,8 @@ struct muon_plan_s {
   int device = -1;
   void* dmem = nullptr;                       // MatInfo table + schedules
   const MatInfo* d_mats = nullptr;
-  const WorkItem* d_items[MUON_K_COUNT] = {};
-  const WorkItem* d_whole[MUON_K_COUNT] = {};  // one-group schedules (timing)
+  const WorkItem* d_items[muon::kKinds] = {};
+  const WorkItem* d_whole[muon::kKinds] = {};  // one-group schedules (timing)
   // groups > 1: one stream per group (default priority) and the events that
   // fork them from, and join them back to, the caller's stream
   hipStream_t gstream[muon::kMaxGroups] = {};
@@ -52,8 +52,8 @@ muon_status upload(muon_plan_s* p) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_E_DEVICE;
   p->device = dev;
   size_t bytes = sizeof(MatInfo) * std::max<size_t>(1, p->host.info.size());
-  size_t offs[MUON_K_COUNT], woffs[MUON_K_COUNT];
-  for (int k = 0; k < MUON_K_COUNT; ++k) {
+  size_t offs[muon::kKinds], woffs[muon::kKinds];
+  for (int k = 0; k < muon::kKinds; ++k) {
     bytes = (bytes + 255) / 256 * 256;
     offs[k] = bytes;
     bytes += sizeof(WorkItem) * std::max<size_t>(1, p->host.sched[k].items.size());
@@ -64,7 +64,7 @@ muon_status upload(muon_plan_s* p) {
   std::vector<char> h(bytes, 0);
   if (!p->host.info.empty())
     std::memcpy(h.data(), p->host.info.data(), sizeof(MatInfo) * p->host.info.size());
-  for (int k = 0; k < MUON_K_COUNT; ++k) {
+  for (int k = 0; k < muon::kKinds; ++k) {
     const auto& it = p->host.sched[k].items;
     if (!it.empty()) std::memcpy(h.data() + offs[k], it.data(), sizeof(WorkItem) * it.size());
     const auto& wt = p->host.whole[k].items;
@@ -94,7 +94,7 @@ muon_status upload(muon_plan_s* p) {
   }
   char* base = static_cast<char*>(p->dmem);
   p->d_mats = reinterpret_cast<const MatInfo*>(base);
-  for (int k = 0; k < MUON_K_COUNT; ++k) {
+  for (int k = 0; k < muon::kKinds; ++k) {
     p->d_items[k] = reinterpret_cast<const WorkItem*>(base + offs[k]);
     p->d_whole[k] = reinterpret_cast<const WorkItem*>(base + woffs[k]);
   }
@@ -158,31 +158,38 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.nesterov = cfg->nesterov;
   a.use_mom = use_mom ? 1 : 0;
   a.direct = cfg->steps == 0 ? 1 : 0;
+  a.split_off = H.split_off;
   if (ap) {
     a.apply = 1;
     a.lr = ap->lr;
     a.wd = ap->wd;
   }
 
+  // Schedule `kind` (a muon_kernel_kind, or the sums of split Gram tiles,
+  // which run as a second pass of the Gram kernel) -> kernel and flag.
+  auto kernel_of = [](int kind) { return kind == muon::kGramReduce ? int(MUON_K_GRAM) : kind; };
   // One launch of kernel `kind` for group g on stream `q`.
   auto launch = [&](int kind, int g, hipStream_t q) -> muon_status {
     const int32_t b = H.gbeg[g][kind], e = H.gbeg[g + 1][kind];
     if (e == b) return MUON_OK;
     a.items = p->d_items[kind] + b;
-    return muon::launch_kernel(kind, H.dtype, cfg->precision, a, e - b, q) == hipSuccess
-               ? MUON_OK
-               : MUON_E_LAUNCH;
+    a.reduce = kind == muon::kGramReduce ? 1 : 0;
+    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, cfg->precision, a, e - b, q);
+    a.reduce = 0;
+    return r == hipSuccess ? MUON_OK : MUON_E_LAUNCH;
   };
   // Per-kernel timing: kernel `kind` over the whole set in one launch on
   // the caller's stream (the one-group schedule), bracketed by HIP events.
   auto timed = [&](int kind) -> muon_status {
     const int grid = static_cast<int>(H.whole[kind].items.size());
     if (grid == 0) return MUON_OK;
-    TimedLaunch t{kind, get_event(p), get_event(p)};
+    TimedLaunch t{kernel_of(kind), get_event(p), get_event(p)};
     if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
     a.items = p->d_whole[kind];
-    if (muon::launch_kernel(kind, H.dtype, cfg->precision, a, grid, s) != hipSuccess)
-      return MUON_E_LAUNCH;
+    a.reduce = kind == muon::kGramReduce ? 1 : 0;
+    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, cfg->precision, a, grid, s);
+    a.reduce = 0;
+    if (r != hipSuccess) return MUON_E_LAUNCH;
     if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
     p->pending.push_back(t);
     return MUON_OK;
@@ -196,7 +203,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     for (int t = 0; t < cfg->steps; ++t) {
       a.cur = t & 1;
       a.last = t == cfg->steps - 1 ? 1 : 0;
-      for (int kind : {MUON_K_GRAM, MUON_K_POLY, MUON_K_UPDATE})
+      for (int kind : {int(MUON_K_GRAM), muon::kGramReduce, int(MUON_K_POLY), int(MUON_K_UPDATE)})
         if ((r = launch(kind, g, q)) != MUON_OK) return r;
     }
     return MUON_OK;
@@ -209,7 +216,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     for (int t = 0; t < cfg->steps; ++t) {
       a.cur = t & 1;
       a.last = t == cfg->steps - 1 ? 1 : 0;
-      for (int kind : {MUON_K_GRAM, MUON_K_POLY, MUON_K_UPDATE})
+      for (int kind : {int(MUON_K_GRAM), muon::kGramReduce, int(MUON_K_POLY), int(MUON_K_UPDATE)})
         if ((r = timed(kind)) != MUON_OK) return r;
     }
     return MUON_OK;
@@ -392,7 +399,7 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
 
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype, int32_t kind,
                                 int32_t* items, int64_t cap, int64_t* count) {
-  if (count == nullptr || kind < 0 || kind >= MUON_K_COUNT || cap < 0 ||
+  if (count == nullptr || kind < 0 || kind > MUON_K_COUNT || cap < 0 ||
       (cap > 0 && items == nullptr))
     return MUON_E_INVALID;
   HostPlan P;

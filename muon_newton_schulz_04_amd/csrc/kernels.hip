@@ -1019,7 +1019,9 @@ __device__ __forceinline__ void fold_bias(f32x16_t (&acc)[4][2], const char* st,
 // bf16 sets. Item {mat, TI, TJ} of 256 x 256 tiles. GRAM/POLY: tiles on or
 // above the diagonal (TJ >= TI); each stored element (m <= n) is mirrored to
 // (n, m). UPDATE: X = a X + B X on all tiles.
-template <typename T, int OP, int KIND, bool LAST>
+// SK (Gram only): the variant that also runs split tiles and the reduce
+// pass, launched for plans that split Gram tiles.
+template <typename T, int OP, int KIND, bool LAST, bool SK = false>
 __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
@@ -1052,11 +1054,18 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   int64_t lda, ldb, K;
   // Every operand has mp rows, so one panel stride serves both.
   lda = ldb = int64_t(M.mp) * 64;
+  // Split Gram tiles: part sp of S covers k in [sp K / S, (sp + 1) K / S)
+  // and stores an fp32 partial tile; the reduce pass sums the S partials.
+  const int S = SK ? max(it.c & 255, 1) : 1;
+  const int sp = SK ? (it.c >> 8) & 255 : 0;
+  const int pbase = SK ? (it.c >> 16) : 0;
+  const bool reducing = SK && P.reduce;
+  const bool partial = SK && !reducing && S > 1;
   if (KIND == GRAM) {
     const char* X = P.ws + M.xo_cur;
-    opA = X + int64_t(TI) * TM * 64;
-    opB = X + int64_t(TJ) * TN * 64;
-    K = M.np;
+    K = M.np / S;
+    opA = X + int64_t(TI) * TM * 64 + (sp * K / 32) * lda;
+    opB = X + int64_t(TJ) * TN * 64 + (sp * K / 32) * ldb;
   } else if (KIND == POLY) {
     const char* Am = P.ws + M.a_off;
     opA = Am + int64_t(TI) * TM * 64;
@@ -1086,8 +1095,9 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   //   the slot of g-1 | mma(g, 1) | read (g+1, 0)
   // Every pass issues one stage, so the wait count is the same in every pass;
   // past the end the DMA repeats the last stage (valid addresses, unused).
-  const int nst = static_cast<int>(K / KS);
   const bool fold = KIND == POLY && P.c != 0.f;
+  if (!reducing) {
+  const int nst = static_cast<int>(K / KS);
   constexpr bool SPLIT = SPLIT_DMA && NS >= 4 && DMA_PER_STAGE % 2 == 0 && 4 % (DMA_PER_STAGE / 2) == 0;
   constexpr int H = DMA_PER_STAGE / 2;  // pieces per k-step (split issue)
   if constexpr (SPLIT) {
@@ -1168,6 +1178,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     cur = nxt;
   }
   MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
+  }
 
   // ---------------------------------------------------------------- epilogue
   // acc[i][j][4 g + r] = C[m][n], m = mb + 32 i + l32, n = nb + 32 j + 8 g + 4 lh + r
@@ -1183,6 +1194,29 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   const int mb = m0 + wm * 128, nb = n0 + wn * 64;
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // every wave is done reading the operand stages
+
+  // Split Gram tiles: a part stores its fp32 accumulators in accumulator
+  // order (per wave and block (i, j): 64 lanes x 64 bytes); the reduce pass
+  // sums the parts in order straight into the staged tile (below) and goes
+  // on as an ordinary tile.
+  auto part_ptr = [&](int q, int i, int j) {
+    return reinterpret_cast<const f32x4_t*>(P.ws + P.split_off + int64_t(pbase + q) * (TM * TN * 4) +
+                                            ((((wave * 4 + i) * 2 + j) * 64) + lane) * 64);
+  };
+  if constexpr (SK) {
+    if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            f32x4_t* d = const_cast<f32x4_t*>(part_ptr(sp, i, j));
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              d[v] = f32x4_t{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+          }
+      return;
+    }
+  }
 
   // Staged address of (row r, chunk c). The XOR gives 16 consecutive rows
   // distinct chunk positions (accumulator-order writes) and keeps the four
@@ -1300,12 +1334,56 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
             *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], F16);
           }
       }
+    } else if (SK && reducing) {
+      // one 128 x 128 quarter (qr, qc) of the tile: its 64 KB of each part's
+      // accumulator-order partial (waves qr*4 + 2qc and the next) summed in
+      // part order by all threads, 16 bytes (4 floats of one lane and block)
+      // at a time, into the staged tile
+      const int qr = sp >> 1, qc = sp & 1;
+      const char* qbase = P.ws + P.split_off + int64_t(pbase) * (TM * TN * 4) + (qr * 4 + 2 * qc) * 32768;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4_t sum[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sum[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < S; q0 += 4) {
+          f32x4_t x[4][4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q0 + q < S)
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                x[q][u] = *reinterpret_cast<const f32x4_t*>(qbase + int64_t(q0 + q) * (TM * TN * 4) +
+                                                            ((h * 4 + u) * NTHR + threadIdx.x) * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q0 + q < S)
+#pragma unroll
+              for (int u = 0; u < 4; ++u) sum[u] += x[q][u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int o = ((h * 4 + u) * NTHR + threadIdx.x) * 16;
+          const int wl = o >> 15, blk = (o >> 12) & 7, ln = (o >> 6) & 63, v = (o >> 4) & 3;
+          const int r = qr * 128 + 32 * (blk >> 1) + (ln & 31);
+          const int c = (2 * qc + wl) * 8 + 4 * (blk & 1) + v;
+          *reinterpret_cast<uint2*>(lds + soff(r, c) + (ln >> 5) * 8) =
+              e16::pack4(sum[u][0], sum[u][1], sum[u][2], sum[u][3], F16);
+        }
+      }
     } else {
       stage16(F16);
     }
     __syncthreads();
+    // (the reduce pass of a split tile stores its quarter only)
+    auto in_quarter = [&](int m, int n) {
+      if constexpr (!SK) return true;
+      if (!reducing) return true;
+      return ((m - m0) >> 7) == (sp >> 1) && ((n - n0) >> 7) == (sp & 1);
+    };
     // C[m][n..n+7] where m <= n
     rows_out([&](int m, int n, const uint4& v) {
+      if (!in_quarter(m, n)) return;
       uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(m, n, mp);
       if (strict || m <= n) {
         *reinterpret_cast<uint4*>(d) = v;
@@ -1317,6 +1395,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     });
     // mirror: C[n][m..m+7] = C[m..m+7][n] where m < n
     cols_out([&](int n, int m, const uint4& v) {
+      if (!in_quarter(m, n)) return;
       uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(n, m, mp);
       if (strict || m + 7 < n) {
         *reinterpret_cast<uint4*>(d) = v;
@@ -1498,6 +1577,7 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
     case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;
     case MUON_K_GRAM:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, GRAM>), g, b, 0, s, a);
+      else if (a.split_off >= 0) hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM, false, true>), g, b, 0, s, a);
       else hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM, false>), g, b, 0, s, a);
       break;
     case MUON_K_POLY:

@@ -21,6 +21,8 @@ struct StepArgs {
   int32_t direct;   // zero steps: the normalise kernel writes `out`
   int32_t apply;    // write W <- W (1 - lr' wd') - lr' X instead of `out` (lr' = lr lr_mul, wd' = wd wd_mul)
   float lr, wd;
+  int32_t reduce;   // Gram: sum split partial tiles and store A (second pass)
+  int64_t split_off;  // workspace offset of the split Gram partials (-1: none)
 };
 
 // precision: muon_precision (operand format of bf16 sets).

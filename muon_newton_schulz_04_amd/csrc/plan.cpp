@@ -177,12 +177,14 @@ Schedule assign_xcd(std::vector<Chunk> chunks) {
   return s;
 }
 
-// Splits each matrix's item list into chunks of at most `max_cost`.
+// Splits each matrix's item list into chunks of at most `max_cost` (the
+// parts of one split Gram tile stay in one chunk, so they share an XCD).
 void add_matrix_chunks(std::vector<Chunk>& chunks, int32_t mat, const std::vector<WorkItem>& items,
                        const std::vector<double>& costs, double max_cost) {
   Chunk cur{mat, {}, 0.0};
   for (size_t i = 0; i < items.size(); ++i) {
-    if (!cur.items.empty() && cur.cost + costs[i] > max_cost) {
+    const bool tile_start = ((items[i].c >> 8) & 255) == 0;
+    if (!cur.items.empty() && cur.cost + costs[i] > max_cost && tile_start) {
       chunks.push_back(std::move(cur));
       cur = Chunk{mat, {}, 0.0};
     }
@@ -190,6 +192,33 @@ void add_matrix_chunks(std::vector<Chunk>& chunks, int32_t mat, const std::vecto
     cur.cost += costs[i];
   }
   if (!cur.items.empty()) chunks.push_back(std::move(cur));
+}
+
+// Places each reduce item of a split Gram tile on the XCD that ran the
+// tile's parts in `gram` (block b runs on XCD b % 8), so that the reduce
+// pass reads the partial tiles from that XCD's L2.
+Schedule place_reduce(const Schedule& gram, const std::vector<WorkItem>& reduce) {
+  auto key = [](const WorkItem& w) { return (int64_t(w.mat) << 32) | (int64_t(w.a) << 16) | w.b; };
+  std::vector<std::pair<int64_t, int>> xcd_of;
+  for (size_t b = 0; b < gram.items.size(); ++b) {
+    const WorkItem& w = gram.items[b];
+    if (w.mat >= 0 && (w.c & 255) >= 2 && ((w.c >> 8) & 255) == 0)
+      xcd_of.push_back({key(w), static_cast<int>(b % kNumXcd)});
+  }
+  std::sort(xcd_of.begin(), xcd_of.end());
+  std::vector<std::vector<WorkItem>> lists(kNumXcd);
+  size_t longest = 0;
+  for (const WorkItem& r : reduce) {
+    auto it = std::lower_bound(xcd_of.begin(), xcd_of.end(), std::make_pair(key(r), -1));
+    const int x = (it != xcd_of.end() && it->first == key(r)) ? it->second : 0;
+    lists[x].push_back(r);
+    longest = std::max(longest, lists[x].size());
+  }
+  Schedule s;
+  s.items.assign(longest * kNumXcd, WorkItem{-1, -1, -1, -1});
+  for (int x = 0; x < kNumXcd; ++x)
+    for (size_t p = 0; p < lists[x].size(); ++p) s.items[p * kNumXcd + x] = lists[x][p];
+  return s;
 }
 
 }  // namespace
@@ -264,10 +293,8 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
   if (!any) P.ws_bytes = 0;
 
   // Work items and their costs, per kernel.
-  std::vector<std::vector<std::vector<WorkItem>>> per(MUON_K_COUNT,
-                                                      std::vector<std::vector<WorkItem>>(n));
-  std::vector<std::vector<std::vector<double>>> cost(MUON_K_COUNT,
-                                                     std::vector<std::vector<double>>(n));
+  std::vector<std::vector<std::vector<WorkItem>>> per(kKinds, std::vector<std::vector<WorkItem>>(n));
+  std::vector<std::vector<std::vector<double>>> cost(kKinds, std::vector<std::vector<double>>(n));
   for (int32_t i = 0; i < n; ++i) {
     const MatInfo& I = P.info[i];
     if (I.m == 0) continue;
@@ -304,6 +331,69 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
         cost[MUON_K_UPDATE][i].push_back(area * I.mp);
       }
   }
+  // Split Gram tiles (bf16 sets). A Gram launch takes about max(longest
+  // tile, total work / CUs). When the longest tiles (the k loops of the
+  // widest matrices) are at least twice the work per CU, each tile of k
+  // loop longer than `target` stages is cut into S parts of at most
+  // `target` stages (S dividing stages / 8, so each part keeps whole groups
+  // of 8 stages); the parts write fp32 partial tiles, and a second pass sums
+  // them in part order, one 128 x 128 quarter of a tile per workgroup, and
+  // stores A (and its mirror) like an ordinary tile.
+  if (bf16) {
+    double work = 0;
+    int32_t longest = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t st = P.info[i].np / 32;
+      work += double(st) * per[MUON_K_GRAM][i].size();
+      if (!per[MUON_K_GRAM][i].empty()) longest = std::max(longest, st);
+    }
+    const int32_t target = std::max<int32_t>(kSplitMinStages, static_cast<int32_t>(std::ceil(work / kNumCu)));
+    int32_t parts = 0;
+    std::vector<int32_t> split(n, 1);
+    if (longest >= 2 * target) {
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t st = P.info[i].np / 32, g8 = st / 8;
+        if (per[MUON_K_GRAM][i].empty() || st < 2 * target) continue;
+        int32_t S = g8;
+        for (int32_t d = 2; d <= g8; ++d)
+          if (g8 % d == 0 && st / d <= target) {
+            S = d;
+            break;
+          }
+        if (S < 2 || S > 255) continue;
+        const int64_t need = int64_t(S) * per[MUON_K_GRAM][i].size();
+        if (parts + need > kSplitMaxParts) continue;
+        split[i] = S;
+        parts += static_cast<int32_t>(need);
+      }
+    }
+    if (parts > 0) {
+      int32_t pbase = 0;
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t S = split[i];
+        if (S < 2) continue;
+        std::vector<WorkItem> items;
+        std::vector<double> costs;
+        for (size_t t = 0; t < per[MUON_K_GRAM][i].size(); ++t) {
+          const WorkItem w = per[MUON_K_GRAM][i][t];
+          for (int32_t sp = 0; sp < S; ++sp) {
+            items.push_back({w.mat, w.a, w.b, (pbase << 16) | (sp << 8) | S});
+            costs.push_back(cost[MUON_K_GRAM][i][t] / S);
+          }
+          for (int32_t qd = 0; qd < 4; ++qd) {  // the reduce pass takes quarters of 128 x 128
+            per[kGramReduce][i].push_back({w.mat, w.a, w.b, (pbase << 16) | (qd << 8) | S});
+            cost[kGramReduce][i].push_back(1.0);
+          }
+          pbase += S;
+        }
+        per[MUON_K_GRAM][i] = std::move(items);
+        cost[MUON_K_GRAM][i] = std::move(costs);
+      }
+      P.split_parts = parts;
+      P.split_off = take(static_cast<size_t>(parts) * kTileM16 * kTileN16 * 4);
+      P.ws_bytes = off;
+    }
+  }
   // Groups: matrices by update cost, longest first, onto the lighter group.
   int64_t upd_tiles = 0;
   for (int32_t i = 0; i < n; ++i) upd_tiles += static_cast<int64_t>(per[MUON_K_UPDATE][i].size());
@@ -316,8 +406,8 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     std::iota(order.begin(), order.end(), 0);
     auto work = [&](int32_t i) {
       double w = 0;
-      for (int k = 0; k < MUON_K_COUNT; ++k)
-        for (double c : cost[k][i]) w += k >= MUON_K_GRAM ? c : 0.0;
+      for (int k = MUON_K_GRAM; k < MUON_K_COUNT; ++k)
+        for (double c : cost[k][i]) w += c;
       return w;
     };
     std::vector<double> wi(n);
@@ -356,6 +446,27 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     }
     P.gbeg[P.ngroups][k] = static_cast<int32_t>(P.sched[k].items.size());
     P.whole[k] = P.ngroups == 1 ? P.sched[k] : schedule_of(k, -1, 1.0);
+  }
+  // reduce items of split Gram tiles, on the XCDs of their parts
+  {
+    auto reduce_of = [&](int g) {
+      std::vector<WorkItem> r;
+      for (int32_t i = 0; i < n; ++i)
+        if (g < 0 || group[i] == g) r.insert(r.end(), per[kGramReduce][i].begin(), per[kGramReduce][i].end());
+      return r;
+    };
+    const int k = kGramReduce;
+    P.sched[k].items.clear();
+    for (int g = 0; g < P.ngroups; ++g) {
+      P.gbeg[g][k] = static_cast<int32_t>(P.sched[k].items.size());
+      Schedule gram_g;
+      gram_g.items.assign(P.sched[MUON_K_GRAM].items.begin() + P.gbeg[g][MUON_K_GRAM],
+                          P.sched[MUON_K_GRAM].items.begin() + P.gbeg[g + 1][MUON_K_GRAM]);
+      const Schedule s = place_reduce(gram_g, reduce_of(g));
+      P.sched[k].items.insert(P.sched[k].items.end(), s.items.begin(), s.items.end());
+    }
+    P.gbeg[P.ngroups][k] = static_cast<int32_t>(P.sched[k].items.size());
+    P.whole[k] = P.ngroups == 1 ? P.sched[k] : place_reduce(P.whole[MUON_K_GRAM], reduce_of(-1));
   }
   *out = std::move(P);
   return MUON_OK;

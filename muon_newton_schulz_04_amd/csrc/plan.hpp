@@ -21,7 +21,16 @@ constexpr int kTileN16 = MUON_TILE_N;
 constexpr int kNormTile = 64;          // tile of the normalise / layout kernel
 constexpr int kMomentumElems = 16384;  // target elements per momentum work item
 constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X
+constexpr int kNumCu = 256;            // compute units of an MI355X
 constexpr size_t kWsAlign = 256;
+// Internal schedule after the public kernel kinds: the sums of split Gram
+// tiles (bf16 sets), launched as a second Gram pass.
+constexpr int kGramReduce = MUON_K_COUNT;
+constexpr int kKinds = MUON_K_COUNT + 1;
+// Split Gram tiles: k ranges of at least 8 stages of 32; each partial is a
+// 256 x TN fp32 tile in the workspace.
+constexpr int32_t kSplitMaxParts = 32767;
+constexpr int32_t kSplitMinStages = 24;
 
 // Per-matrix record read by the kernels (device table; plain data).
 struct MatInfo {
@@ -52,6 +61,10 @@ struct MatInfo {
   int32_t pad_;
 };
 
+// Gram items of bf16 sets: c = 0, or for a tile whose k range is split into
+// S parts, c = pbase << 16 | s << 8 | S (part s of S, stored in partial
+// slot pbase + s); reduce items: c = pbase << 16 | q << 8 | S for quarter q
+// (rows 128 (q >> 1), columns 128 (q & 1) of the tile).
 struct WorkItem {
   int32_t mat, a, b, c;
 };
@@ -75,13 +88,17 @@ struct HostPlan {
   std::vector<MatInfo> info;
   // Schedules of all groups, concatenated: group g's items of kernel k are
   // sched[k].items[gbeg[g][k] .. gbeg[g + 1][k]) (each a multiple of 8).
-  Schedule sched[MUON_K_COUNT];
+  Schedule sched[kKinds];
   int32_t ngroups = 1;
-  int32_t gbeg[kMaxGroups + 1][MUON_K_COUNT] = {};
+  int32_t gbeg[kMaxGroups + 1][kKinds] = {};
   // The same work as one group (per-kernel timing runs each kernel over the
   // whole set in one launch).
-  Schedule whole[MUON_K_COUNT];
+  Schedule whole[kKinds];
   int32_t total_partials = 0;
+  // Split Gram tiles (small bf16 sets whose longest Gram tiles would set
+  // the launch time): partial tiles in the workspace at split_off.
+  int32_t split_parts = 0;
+  int64_t split_off = -1;
   size_t ws_bytes = 0;
 };
 

@@ -124,7 +124,19 @@ def expected_ws(shapes, dtype):
                  [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
         for s in sizes:
             off = ru(off + s, 256)
+    # split Gram tiles: one 256 x 256 fp32 partial tile per part, at the end
+    if dtype == mu.MUON_BF16:
+        red = split_reduce_items(shapes)
+        nparts = int(red[:, 3].astype(np.int64).__and__(255).sum()) // 4 if len(red) else 0
+        if nparts:
+            off = ru(off + nparts * 256 * 256 * 4, 256)
     return off
+
+
+def split_reduce_items(shapes):
+    """The reduce items of split Gram tiles (schedule kind MUON_K_COUNT)."""
+    s = mu.muon_schedule_query(shapes, mu.MUON_BF16, 5)
+    return s[s[:, 0] >= 0] if len(s) else s
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
@@ -132,6 +144,18 @@ def test_workspace_bytes_formula(lib, name):
     cfg = CONFIGS[name]
     dt = mu.MUON_F32 if cfg.dtype == "fp32" else mu.MUON_BF16
     assert mu.muon_workspace_bytes(list(cfg.shapes), dt) == expected_ws(cfg.shapes, dt)
+
+
+def test_gram_split_only_where_the_longest_tiles_dominate(lib):
+    """Split Gram tiles: the one-block set (two 768 x 3072 matrices among
+    four 768^2) splits its 96-stage tiles into 24-stage parts; the full
+    GPT-2-124M set (work per CU above half the longest tile) does not split."""
+    small = list(CONFIGS["gpt2_small_block"].shapes)
+    red = split_reduce_items(small)
+    assert len(red) == 4 * 12 and set(red[:, 3] & 255) == {4}
+    assert set(max(small[i]) for i in red[:, 0]) == {3072}
+    assert len(split_reduce_items(list(CONFIGS["gpt2_124m_matrix_set"].shapes))) == 0
+    assert len(mu.muon_schedule_query(small, mu.MUON_F32, 5)) == 0   # fp32 sets never split
 
 
 SHAPE_SETS = {
@@ -167,13 +191,44 @@ def test_schedules_cover_every_tile_exactly_once(lib, setname, dtype):
         # tiles that reach the upper triangle, and every upper element in exactly one
         want_tri = [(a, b) for a in range(mp // tm) for b in range(mp // tn)
                     if b * tn + tn - 1 >= a * tm]
+        # gram: a tile is one item (c = 0) or S parts (c = pbase << 16 | sp << 8 | S,
+        # sp = 0 .. S-1, S dividing the tile's stages / 8) plus one reduce item
+        gi = gram[gram[:, 0] == i]
+        tiles = {}
+        for _, a, b, c in gi:
+            tiles.setdefault((a, b), []).append(int(c))
+        assert sorted(tiles) == want_tri
+        red_i = split_reduce_items(shapes) if dtype == mu.MUON_BF16 else np.zeros((0, 4), int)
+        red = {}
+        for m_, a, b, c in red_i:
+            if m_ == i:
+                red.setdefault((int(a), int(b)), []).append(int(c))
+        for t, cs in red.items():      # four quarters per split tile, same pbase and S
+            assert sorted((c >> 8) & 255 for c in cs) == [0, 1, 2, 3]
+            assert len({c & ~0xff00 for c in cs}) == 1
+        red = {t: cs[0] & ~0xff00 for t, cs in red.items()}
+        for t, cs in tiles.items():
+            if cs == [0]:
+                assert t not in red
+                continue
+            S = cs[0] & 255
+            assert S >= 2 and (np_ // 32 // 8) % S == 0 and len(cs) == S
+            assert sorted((c >> 8) & 255 for c in cs) == list(range(S))
+            assert len({c >> 16 for c in cs}) == 1 and red[t] == ((cs[0] >> 16) << 16 | S)
+        assert set(red) <= set(tiles)
+    if dtype == mu.MUON_BF16:
+        spans = sorted({(c >> 16, (c >> 16) + (c & 255)) for *_, c in split_reduce_items(shapes)})
+        assert all(e0 <= b1 for (_, e0), (b1, _) in zip(spans, spans[1:]))   # disjoint partial slots
         for s in (gram, poly):
             si = s[s[:, 0] == i]
-            assert sorted(map(tuple, si[:, 1:3])) == want_tri
             cover = np.zeros((mp, mp), int)
-            for _, a, b, _c in si:
+            for _, a, b, c in si:
+                if s is gram and (c & 255) >= 2 and (c >> 8) & 255:
+                    continue                      # count each split tile once
                 cover[a * tm:(a + 1) * tm, b * tn:(b + 1) * tn] += 1
             assert np.all(np.triu(cover) == np.triu(np.ones((mp, mp), int)))
+        pi = poly[poly[:, 0] == i]
+        assert sorted(map(tuple, pi[:, 1:3])) == want_tri
         ui = upd[upd[:, 0] == i]
         assert sorted(map(tuple, ui[:, 1:3])) == [(a, b) for a in range(mp // tm) for b in range(np_ // tn)]
 
