@@ -7,6 +7,9 @@
 //                     bf16 sets a 16-bit operand (hi, in 32-column panels)
 //                     and a low part (lo)                          (HBM-bound)
 //   gemm*_kernel<GRAM>   A = X X^T          upper-triangle tiles, mirrored
+//                                           (small bf16 sets: long k loops
+//                                           split into parts, summed in a
+//                                           second pass)
 //   gemm*_kernel<POLY>   B = b A + c A A    upper-triangle tiles, mirrored
 //   gemm*_kernel<UPDATE> X = a X + B X      the last step writes `out`, or
 //                                           applies X to the weights
@@ -18,7 +21,7 @@
 //    current one is multiplied).
 //  - gemm16_kernel (bf16 sets; fp16 operands by default): 256 x 256 output
 //    tiles, 8 waves, operands DMA'd straight into a 4-stage LDS ring (see
-//    the section below).
+//    the section below); X kept as an fp16 high part plus an e4m3 low byte.
 //
 // Every launch takes a schedule of work items; block b runs item b. The
 // schedules keep one matrix's tiles on one XCD (block b runs on XCD b % 8).
