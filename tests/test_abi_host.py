@@ -168,7 +168,23 @@ SHAPE_SETS = {
 @pytest.mark.parametrize("dtype", [mu.MUON_BF16, mu.MUON_F32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("setname", list(SHAPE_SETS))
 def test_schedules_cover_every_tile_exactly_once(lib, setname, dtype):
-    shapes = SHAPE_SETS[setname]
+    check_schedules(SHAPE_SETS[setname], dtype)
+
+
+def test_schedules_of_random_sets(lib):
+    """The same invariants on seeded random sets (1 to 12 matrices, sides 1
+    to 9000, some of them split their Gram tiles)."""
+    rng = np.random.default_rng(2024)
+    for _ in range(25):
+        k = int(rng.integers(1, 13))
+        shapes = [(int(rng.integers(1, 3000)), int(rng.integers(1, 9000))) for _ in range(k)]
+        shapes = [(r, c) if rng.random() < 0.5 else (c, r) for r, c in shapes]
+        for dtype in (mu.MUON_BF16, mu.MUON_F32):
+            check_schedules(shapes, dtype)
+            assert mu.muon_workspace_bytes(shapes, dtype) == expected_ws(shapes, dtype)
+
+
+def check_schedules(shapes, dtype):
     tm = tn = 256 if dtype == mu.MUON_BF16 else 128
     scheds = [mu.muon_schedule_query(shapes, dtype, k) for k in range(5)]
     for k, s in enumerate(scheds):
