@@ -208,6 +208,25 @@ def test_split_gram_tiles():
         assert rel(t.T, a) < 1e-2
 
 
+@pytest.mark.parametrize("seed", [7, 8, 9])
+def test_random_small_sets(seed):
+    """Seeded random sets of 2 to 4 bf16 matrices (any orientation, ragged
+    sides up to 1200 x 4000; most of them split Gram tiles) against the
+    oracle, with momentum."""
+    rng = np.random.default_rng(seed)
+    shapes = [(int(rng.integers(1, 1200)), int(rng.integers(1, 4000))) for _ in range(int(rng.integers(2, 5)))]
+    shapes = [(r, c) if rng.random() < 0.5 else (c, r) for r, c in shapes]
+    grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=seed, shapes=shapes)]
+    bufs = [torch.zeros_like(g) for g in grads]
+    say(f"random set seed={seed} shapes={shapes}")
+    got, nb = gpu_call(grads, bufs, QUINTIC, 5, momentum=0.95, nesterov=True)
+    want, wb = oracle_call([to_f64(g) for g in grads], [np.zeros(g.shape) for g in grads], QUINTIC, 5,
+                           momentum=0.95, nesterov=True)
+    for shp, o, w in zip(shapes, got, want):
+        assert rel(o, w) < TOL["bf16"], shp
+    check_buffers(nb, wb, "bf16")
+
+
 def lo_byte_index(mp, np_):
     """Byte offset of X(m, n) in the fp16 path's low-byte layout: per 256 x 256
     tile (row-major over tiles), per 32-row block u, per 64-column wave
