@@ -184,13 +184,17 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     const int grid = static_cast<int>(H.whole[kind].items.size());
     if (grid == 0) return MUON_OK;
     TimedLaunch t{kernel_of(kind), get_event(p), get_event(p)};
-    if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return MUON_E_LAUNCH;
+    auto give_back = [&]() {
+      if (t.start) p->free_events.push_back(t.start);
+      if (t.stop) p->free_events.push_back(t.stop);
+      return MUON_E_LAUNCH;
+    };
+    if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return give_back();
     a.items = p->d_whole[kind];
     a.reduce = kind == muon::kGramReduce ? 1 : 0;
     const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, cfg->precision, a, grid, s);
     a.reduce = 0;
-    if (r != hipSuccess) return MUON_E_LAUNCH;
-    if (hipEventRecord(t.stop, s) != hipSuccess) return MUON_E_LAUNCH;
+    if (r != hipSuccess || hipEventRecord(t.stop, s) != hipSuccess) return give_back();
     p->pending.push_back(t);
     return MUON_OK;
   };
@@ -282,7 +286,7 @@ muon_status cached_step(const muon_matrix* mats, int32_t n, muon_dtype dt, const
     return MUON_E_WORKSPACE;
   }
   if ((st = upload(p)) != MUON_OK) {
-    delete p;
+    release(p);  // also frees the streams and events of a partial upload
     return st;
   }
   g_cache.push_front({key, p});
@@ -331,9 +335,12 @@ muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtyp
   muon_plan_s* p = new (std::nothrow) muon_plan_s();
   if (!p) return MUON_E_ALLOC;
   muon_status st = muon::build_plan(mats, n, dtype, &p->host);
-  if (st == MUON_OK) st = upload(p);
   if (st != MUON_OK) {
     delete p;
+    return st;
+  }
+  if ((st = upload(p)) != MUON_OK) {
+    release(p);  // also frees the streams and events of a partial upload
     return st;
   }
   *plan = p;

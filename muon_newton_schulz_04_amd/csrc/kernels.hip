@@ -790,6 +790,11 @@ __device__ __forceinline__ int off_k(int k, int c) { return k * KROW + ((c ^ ((k
 // with a wait for all DMA in flight (it cannot tell the ring slots apart,
 // and it cannot see the alias scopes of the transposing LDS reads). The
 // ring's own waits (s_waitcnt vmcnt + s_barrier) order the accesses.
+// M0 is a reserved register, so clang warns that it does not save it around
+// the asm; the generated code of this file holds no live value in M0 (its
+// only writes are these), so the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -799,6 +804,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       : "s"(lds_base), "v"(src)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // DMA of one stage in pieces of 1 KB: 16 of the row operand, TN/16 of the
 // column operand. Operands are in 32-column panels (pidx) and lda / ldb are
