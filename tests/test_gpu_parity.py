@@ -349,6 +349,46 @@ def test_zero_matrix_empty_matrix_and_aliasing():
     assert rel(to_f64(outs[2]), want[0]) < 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("pad", [8, 3], ids=["ld16B", "ld_unaligned"])
+def test_strided_rows(dtype, pad):
+    """Matrices that are column slices of wider buffers (row stride ld = cols
+    + pad): pad 8 keeps 16-byte rows for bf16, pad 3 does not (scalar
+    paths). Wide and tall, ragged against the tiles. The columns beyond
+    `cols` of grad, momentum and out must stay untouched."""
+    wl = CONFIGS["gpt2_small_block"]
+    shapes = [(200, 333), (333, 200), (64, 520)]
+    grads = [g.to(TDT[dtype]) for g in make_gradients(wl, step=6, shapes=shapes)]
+    bufs0 = [(0.3 * g.float()).to(g.dtype) for g in grads]
+    say(f"strided rows {dtype} pad {pad}")
+    g_dev, b_dev, o_dev, parents = [], [], [], []
+    for g, b in zip(grads, bufs0):
+        r, c = g.shape
+        pg = torch.full((r, c + pad), 5.0, dtype=g.dtype, device=DEV)
+        pb = torch.full((r, c + pad), 6.0, dtype=g.dtype, device=DEV)
+        po = torch.full((r, c + pad), 7.0, dtype=g.dtype, device=DEV)
+        pg[:, :c] = g.to(DEV)
+        pb[:, :c] = b.to(DEV)
+        parents.append((pg, pb, po))
+        g_dev.append(pg[:, :c])
+        b_dev.append(pb[:, :c])
+        o_dev.append(po[:, :c])
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True, 1e-7)
+    mu.muon_step(g_dev, b_dev, o_dev, cfg)
+    torch.cuda.synchronize()
+    want, wb = oracle_call([to_f64(g) for g in grads], [to_f64(b) for b in bufs0], QUINTIC, 5,
+                           momentum=0.95, nesterov=True, buf_dtype=dtype)
+    for i, (pg, pb, po) in enumerate(parents):
+        c = shapes[i][1]
+        e = rel(to_f64(o_dev[i]), want[i])
+        say(f"  matrix {shapes[i]} rel err {e:.3e}")
+        assert e < TOL[dtype], (i, e)
+        check_buffers([to_f64(b_dev[i])], [wb[i]], dtype)
+        assert torch.equal(pg[:, c:].float().cpu(), torch.full((shapes[i][0], pad), 5.0))
+        assert torch.equal(pb[:, c:].float().cpu(), torch.full((shapes[i][0], pad), 6.0))
+        assert torch.equal(po[:, c:].float().cpu(), torch.full((shapes[i][0], pad), 7.0))
+
+
 # ------------------------------------------------------ full configurations
 
 def run_config(name, sample_per_group=2, step_seeds=(0,), device_gen="cpu", precision=0):
