@@ -451,3 +451,65 @@ def test_config_gpt2_350m_matrix_set():
 @pytest.mark.slow
 def test_config_wide_powerlaw():
     run_config("wide_2048x8192_powerlaw", device_gen=DEV)
+
+
+# ------------------------------------------------------------ maximum sizes
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_max_dims(dtype):
+    """One side at the largest dimension the ABI accepts (65536), wide and
+    tall: a Gram matrix of 64 x 64 over k = 65536 (long k loops, split Gram
+    tiles for bf16 sets)."""
+    wl = CONFIGS["gpt2_small_block"]
+    shapes = [(64, 65536), (65536, 64)]
+    grads = [g.to(TDT[dtype]) for g in make_gradients(wl, step=9, shapes=shapes)]
+    say(f"max dims {dtype}")
+    outs, _ = gpu_call([g.to(DEV) for g in grads], None, QUINTIC, 5, ortho=True)
+    for i, g in enumerate(grads):
+        want = oracle.orthogonalize(to_f64(g), *(f32(x) for x in QUINTIC), 5, eps=f32(1e-7))
+        e = rel(outs[i], want)
+        say(f"  matrix {shapes[i]} rel err {e:.3e}")
+        assert e < TOL[dtype], (i, e)
+
+
+def orthonormal_rows(m, n, seed):
+    """m x n (n = 4 m) with orthonormal rows, on the GPU: row i holds +-1/2
+    at columns i, i + m, i + 2m, i + 3m (disjoint supports, exact in bf16).
+    Returns the matrix and its nonzero mask."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    signs = (torch.randint(0, 2, (4, m), generator=gen) * 2 - 1).to(torch.bfloat16).to(DEV)
+    q = torch.zeros(m, n, dtype=torch.bfloat16, device=DEV)
+    rows = torch.arange(m, device=DEV)
+    for t in range(4):
+        q[rows, rows + t * m] = 0.5 * signs[t]
+    return q
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("tall", [False, True], ids=["wide", "tall"])
+def test_max_elements_orthonormal_rows(tall):
+    """A matrix of 2^30 elements (16384 x 65536, the largest the ABI
+    accepts; byte offsets beyond 2^31). Its rows are orthonormal, so every
+    singular value of X0 is sigma0 = 1 / (sqrt(m) + eps) and the exact output
+    is p^5(sigma0) Q, p^5 from the oracle's iteration on the 1 x 1 matrix
+    [[sigma0]] (the iteration acts on singular values only). The zero pattern
+    must come out exactly (every product of a misplaced index would land on
+    a zero), and every nonzero within 2e-2 of the value."""
+    m, n = 16384, 65536
+    q = orthonormal_rows(m, n, seed=11)
+    g = q.t().contiguous() if tall else q
+    del q
+    say(f"max elements {'tall' if tall else 'wide'} {tuple(g.shape)}")
+    out = torch.empty_like(g)
+    cfg = mu.make_config(*QUINTIC, 5, 0.0, False, 1e-7)
+    mu.muon_orthogonalize([g], [out], cfg)
+    torch.cuda.synchronize()
+    sigma0 = 1.0 / (np.sqrt(m) + f32(1e-7))
+    p5 = float(oracle.newton_schulz(np.array([[sigma0]]), *(f32(x) for x in QUINTIC), 5)[0, 0])
+    mask = g != 0
+    assert int(torch.count_nonzero(out[~mask])) == 0
+    ratio = (out[mask].float() / g[mask].float()).double()       # = p5 for every entry
+    lo, hi = float(ratio.min()), float(ratio.max())
+    say(f"  p5 {p5:.6f}: output / input in [{lo:.6f}, {hi:.6f}]")
+    assert abs(lo - p5) < 2e-2 * p5 and abs(hi - p5) < 2e-2 * p5
+    assert int(mask.sum()) == 4 * m
