@@ -513,3 +513,51 @@ def test_max_elements_orthonormal_rows(tall):
     say(f"  p5 {p5:.6f}: output / input in [{lo:.6f}, {hi:.6f}]")
     assert abs(lo - p5) < 2e-2 * p5 and abs(hi - p5) < 2e-2 * p5
     assert int(mask.sum()) == 4 * m
+
+
+# ------------------------------------------------------------ HIP graphs
+
+def test_graph_capture_replays_match_eager():
+    """A whole step (the GPT-2-124M set: two groups of matrices forked onto
+    their own streams and joined back) captured once as a HIP graph: three
+    replays, with eager work and synchronisations in between, give bitwise
+    the outputs and momentum buffers of three eager steps from the same
+    state."""
+    wl = CONFIGS["gpt2_124m_matrix_set"]
+    grads = [g.to(DEV) for g in make_gradients(wl, step=0)]
+    bufs = [torch.zeros_like(g) for g in grads]
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, bufs, outs)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+    cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
+    say("graph capture: eager reference")
+    ref = []
+    for _ in range(3):
+        plan.step(cfg, ws)
+        torch.cuda.synchronize()
+        ref.append(([o.clone() for o in outs], [b.clone() for b in bufs]))
+    for b in bufs:
+        b.zero_()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        plan.step(cfg, ws)
+    torch.cuda.synchronize()
+    for b in bufs:                      # capture runs nothing; start again from zero
+        b.zero_()
+    for o in outs:
+        o.fill_(3.0)
+    torch.cuda.synchronize()
+    for k in range(3):
+        say(f"graph replay {k}")
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (grads[0].float() * 2).sum().item()   # eager work between replays
+        for o, r in zip(outs, ref[k][0]):
+            assert torch.equal(o, r)
+        for b, r in zip(bufs, ref[k][1]):
+            assert torch.equal(b, r)
+    del graph
+    plan.destroy()
