@@ -165,7 +165,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} "
-              "is not supported (the update shards by matrix; see the design notes).",
+              "is not supported (a several-GPU step would give each rank whole matrices to "
+              "update; only one rank's share is timed, under next.rank_share).",
               file=sys.stderr)
         sys.exit(2)
 
