@@ -4,8 +4,9 @@ Bar (per matrix, relative Frobenius error): 2e-2 for bf16 sets, 1e-4 for
 fp32 sets; momentum buffers bitwise equal to the oracle's. bf16 sets run
 with fp16 matrix-core operands (default) and with bf16 operands; the latter
 is held to 2e-2 except on matrices with min(rows, cols) <= 8, where a single
-bf16-rounded B entry near sigma = 1 is amplified by |B|/|a + B| ~ 4 per step
-(derived bound 5e-2, see the design notes).
+bf16-rounded B entry near sigma = 1 is amplified by |B|/|a + B| ~ 4 per step:
+there the bound is 5e-2 (a relative rounding of 2^-9 grown over the last two
+or three steps, with few singular values to average it out).
 The oracle receives the same seeded inputs and the float32 values of the
 scalars the C ABI takes (a, b, c, mu, eps are floats there).
 """
