@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--no-cpu-baseline] [--cpu-budget SECONDS] [--calibrate-copy]
+                [--vendor-ceiling]
 
 A step is one muon_plan_step over all matrices of the workload (momentum,
 normalisation and k Newton-Schulz steps), inputs resident in HBM, one plan
@@ -9,12 +10,13 @@ over fixed gradient buffers as in training (the momentum buffers evolve from
 step to step). `step_ms` gives the spread of single steps from a separate
 pass with events around each step. `value` is
 algorithmic TFLOP/s of the whole step; `roofline` describes the kernel with
-the largest share of the step's time, timed with HIP events recorded around
+the largest share of the step's time against its matrix-core roof (HBM under
+`roofline.other`), timed with HIP events recorded around
 each launch in a second pass of the same length (in that pass the launches
 run one at a time on the step's stream, so each interval holds one launch;
 the timed pass runs large sets as two concurrent groups); the
 CPU baseline times the float64 oracle on a bounded sample of the same
-matrices. `roofline.traffic` is the dominant kernel's HBM bytes per step
+matrices. `roofline.traffic` is the dominant kernel's HBM bytes per launch
 from the committed rocprofv3 counter summary (null if that summary was taken
 on a different kernel source). Prints one JSON line.
 """
@@ -66,22 +68,75 @@ def kernel_work(shapes, steps, dtype):
 
 
 def roofline_of(flops, nbytes, secs, dtype):
-    """Both roofs for one kernel's work in `secs`; the binding one (the larger
-    lower bound on the time) is the headline, the other is kept under
-    `other`."""
+    """Roofline entry of a matrix-core kernel's work in `secs`: the headline
+    is the matrix-core roof (algorithmic flops over the dense MFMA peak of
+    the operand type: fp16 and bf16 share 2.5 PFLOP/s on MI355X); the HBM
+    figure (algorithmic bytes over 8 TB/s) is kept under `other`, with both
+    lower bounds on the time."""
     mf = {"bound": "mfma", "achieved": flops / secs / 1e12, "peak": PEAK[dtype],
           "unit": "TFLOP/s"}
     hb = {"bound": "hbm", "achieved": nbytes / secs / 1e9, "peak": HBM_PEAK_GBS,
           "unit": "GB/s"}
     for r in (mf, hb):
         r["frac"] = r["achieved"] / r["peak"]
-    t_mfma = flops / (PEAK[dtype] * 1e12)
-    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    head, other = (hb, mf) if t_hbm >= t_mfma else (mf, hb)
-    if flops > 0:
-        head["other"] = other
-    head["bound_us"] = {"hbm": t_hbm * 1e6, "mfma": t_mfma * 1e6}
-    return head
+    mf["other"] = hb
+    mf["bound_us"] = {"hbm": nbytes / (HBM_PEAK_GBS * 1e9) * 1e6,
+                      "mfma": flops / (PEAK[dtype] * 1e12) * 1e6}
+    return mf
+
+
+def vendor_ceiling(wl, reps: int = 50):
+    """Empirical ceiling from the vendor GEMM (hipBLASLt through torch,
+    bf16 operands, fp32 accumulation): dense TFLOP/s of single GEMMs at the
+    step's shapes and at 8192^3, and a plain torch version of the whole
+    Newton-Schulz part of the step (batched products over each shape group,
+    every operand contiguous), timed with events on the current stream."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    gemms = {}
+    for (m, k, n) in [(768, 768, 768), (768, 3072, 768), (768, 768, 3072), (1024, 1024, 1024),
+                      (1024, 4096, 1024), (1024, 1024, 4096), (2048, 8192, 2048),
+                      (2048, 2048, 8192), (8192, 8192, 8192)]:
+        x = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        y = torch.randn(k, n, device=dev, dtype=torch.bfloat16)
+        t = timed(lambda: torch.matmul(x, y))
+        gemms[f"{m}x{k}x{n}"] = {"us": t * 1e6, "TFLOP/s": 2.0 * m * k * n / t / 1e12}
+        del x, y
+    # the step's Newton-Schulz part in plain torch (X in rows <= cols form)
+    groups = {}
+    for r, c in wl.shapes:
+        groups[(min(r, c), max(r, c))] = groups.get((min(r, c), max(r, c)), 0) + 1
+    xs = [torch.randn(cnt, m, n, device=dev, dtype=torch.bfloat16) / (m * n) ** 0.5
+          for (m, n), cnt in groups.items()]
+    a, b, c = wl.coeffs
+
+    def ns():
+        for x in xs:
+            y = x
+            for _ in range(wl.steps):
+                A = torch.bmm(y, y.transpose(1, 2).contiguous())
+                B = b * A + c * torch.bmm(A, A)
+                y = a * y + torch.bmm(B, y)
+    t = timed(ns)
+    return {"gemm": gemms,
+            "torch_ns_step": {"ms": t * 1e3, "TFLOP/s_alg": wl.falg_flops() / t / 1e12,
+                              "note": "Newton-Schulz part only (no momentum or normalisation), "
+                                      "bf16 torch.bmm per shape group, k steps"}}
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -149,6 +204,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m_matrix_set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--vendor-ceiling", action="store_true",
+                    help="only time the vendor GEMM (hipBLASLt via torch) at the workload's "
+                         "shapes and a plain torch Newton-Schulz step, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 512 MiB three times (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -161,6 +219,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 3}))
+        return
+    if args.vendor_ceiling:
+        from workloads import CONFIGS
+        print(json.dumps({"vendor_ceiling": vendor_ceiling(CONFIGS[args.workload]),
+                          "workload": args.workload}), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -341,7 +404,12 @@ def main():
     dom = max(kt, key=lambda k: kt[k][0])
     d_step = kt[dom][0] / args.steps * 1e-3
     roof = roofline_of(*work[dom], d_step, wl.dtype)
-    roof["traffic"] = measured_traffic(wl.name, dom)
+    t_step = measured_traffic(wl.name, dom)
+    n_launch = kt[dom][1] / args.steps
+    # HBM bytes per launch (the counter runs' per-step figure over the step's
+    # launches of this kernel), null when taken on another kernel source
+    roof["traffic"] = None if t_step is None else t_step / n_launch
+    roof["traffic_per_step"] = t_step
     roof["kernel"] = dom
     roof["us_per_step"] = d_step * 1e6
     roof["launches_per_step"] = kt[dom][1] / args.steps

@@ -14,20 +14,28 @@
  *   k times:  A = X X^T;  B = b A + c A A;  X = a X + B X
  *   out  = X (transposed back), stored at the set's dtype (RNE)
  *
- * Arithmetic: momentum, norms and the X master copy are fp32. The matrix
- * products run on the matrix cores with fp32 accumulation; their operands
- * (X, A, B) are fp16 for bf16 sets by default (MUON_PRECISION_DEFAULT:
- * 11-bit significands at the same MFMA rate as bf16, and every iterate is
- * bounded by the normalisation) or bf16 (MUON_PRECISION_BF16_OPERANDS);
- * fp32 sets use fp32 operands throughout.
+ * Arithmetic: the stored buffer buf' is the exact mu * buf + G rounded once
+ * to the buffer's dtype (round to nearest, ties to even); u and the norm are
+ * fp32. The matrix products run on the matrix cores with fp32
+ * accumulation. bf16 sets: the operands X, A and B are fp16 (11-bit
+ * significands at bf16's MFMA rate; every iterate is bounded by the
+ * normalisation, so fp16's range suffices), and between steps X is kept as
+ * its fp16 rounding hi plus one OCP e4m3 byte holding (X - hi) * 2^18
+ * (about 15 significant bits together; the byte saturates at +-448, which
+ * only an entry |X| >= 4 can reach). fp32 sets use fp32 operands and an
+ * fp32 X throughout.
  *
  * Conventions shared by every entry point:
  *  - Pointers in muon_matrix, `workspace` and `stream` are device-side
  *    objects owned by the caller (`stream` is a hipStream_t; NULL = the
  *    default stream). The library never frees or retains them beyond a call,
  *    except that a plan remembers the matrix pointers it was created with.
- *  - All arguments are validated before any work is enqueued. On an error
- *    nothing is launched and nothing is written; the status says why.
+ *  - All arguments are validated before any work is enqueued. On a
+ *    validation error nothing is launched and nothing is written; the
+ *    status says why. On MUON_E_LAUNCH (a kernel launch was refused part
+ *    way) the outputs, momentum buffers and workspace hold undefined
+ *    values, and every kernel that was enqueued is still ordered before
+ *    later work on `stream`.
  *  - Work is enqueued asynchronously on `stream`; the caller synchronises.
  *    No C++ exception crosses this interface.
  *  - Results are deterministic: equal inputs give bitwise-equal outputs.
@@ -43,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum {
@@ -85,18 +93,22 @@ typedef struct {
   void* out;
 } muon_matrix;
 
-/* Operand format of the matrix products (see the top of this file). */
-typedef enum { MUON_PRECISION_DEFAULT = 0, MUON_PRECISION_BF16_OPERANDS = 1 } muon_precision;
+/* Operand format of the matrix products (see the top of this file). Only
+ * the default exists; the field is kept for other formats. */
+typedef enum { MUON_PRECISION_DEFAULT = 0 } muon_precision;
 
 /* Per-call scalars. (a, b, c) are the odd polynomial's coefficients
  * p(x) = a x + b x^3 + c x^5 (e.g. the quintic (3.4445, -4.7750, 2.0315) or
  * the cubic (1.5, -0.5, 0)); steps in [0, MUON_MAX_STEPS] (0 returns X0);
  * momentum mu in [0, 1) (0: no momentum state, u = G); nesterov 0 or 1;
- * eps >= 0 is added to ||u||_F (1e-7 is the usual value); precision is a
- * muon_precision value (ignored for fp32 sets). All must be finite. With
- * fp16 operands the iterates must stay below 65504 in magnitude, which
- * holds for polynomials that keep [0, 1] inside [-2, 2] over the steps
- * (all Newton-Schulz coefficient sets in use do). */
+ * eps >= 0 is added to ||u||_F (1e-7 is the usual value); precision must
+ * be MUON_PRECISION_DEFAULT. All must be finite (else MUON_E_INVALID).
+ * bf16 sets also reject (MUON_E_INVALID) coefficients whose iteration takes
+ * a point of [0, 1] (where X0's singular values lie) outside [-2, 2]
+ * within `steps` steps, checked on 4097 evenly spaced points, or with
+ * |a| + 4|b| + 16|c| > 4096: the fp16 operands and the low byte of X need
+ * the iterates' entries below 4 and B = b A + c A A well inside fp16's
+ * range. Every Newton-Schulz coefficient set in use passes. */
 typedef struct {
   float a, b, c;
   int32_t steps;
@@ -122,31 +134,47 @@ muon_status muon_workspace_bytes(const muon_matrix* mats, int32_t n, muon_dtype 
                                  size_t* bytes);
 
 /* Builds a plan for `mats` (copied; pointers included) and uploads its
- * tables to the current device. Allocates a few KB to a few MB of device
- * memory owned by the plan; *plan receives NULL on error. */
+ * tables to the current device. A plan serves the update of one set of
+ * hidden weight matrices, each with a single momentum buffer, the only
+ * state Muon keeps (blog.hotdry.top, "How to train a GPT model in 3
+ * minutes", section 2, customised Muon optimizer). Allocates a few KB to a
+ * few MB of device memory owned by the plan; *plan receives NULL on
+ * error. */
 muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtype,
                              muon_plan** plan);
 
-/* Enqueues one Muon update of every matrix of the plan on `stream`.
+/* Enqueues one Muon update of every matrix of the plan on `stream`: the
+ * momentum step, the normalisation and `steps` Newton-Schulz steps in place
+ * of the SVD of spectral descent (blog.hotdry.top, "How to train a GPT
+ * model in 3 minutes", section 2, customised Muon optimizer; yongjin360.com,
+ * Modded-NanoGPT green-AI article, technical evolution: Newton-Schulz
+ * orthogonalisation). Results are bitwise those of muon_step.
  * `workspace` must hold at least muon_workspace_bytes bytes, 256-byte
  * aligned, and must not be used by anything else until the work ends.
  * Calls on the same workspace must be ordered (same stream). */
 muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Frees a plan after waiting for the device (NULL is a no-op). */
+/* Frees a plan after waiting for the device (NULL is a no-op). Plans own
+ * only their descriptor tables and, for sets split into concurrent groups,
+ * two streams and their events. */
 void muon_plan_destroy(muon_plan* plan);
 
-/* One Muon update of `mats` without an explicit plan: looks up (or builds
- * and caches, keyed by the full descriptor array including pointers) a plan
- * and calls muon_plan_step. A cache miss allocates and synchronises once;
+/* One Muon update of `mats` (the whole optimizer step of the Muon path for
+ * one training step: blog.hotdry.top, "How to train a GPT model in 3
+ * minutes", section 2, customised Muon optimizer) without an explicit plan:
+ * looks up (or builds and caches, keyed by the full descriptor array
+ * including pointers) a plan and calls muon_plan_step. A cache miss allocates and synchronises once;
  * training loops with stable buffers hit the cache on every later call. */
 muon_status muon_step(const muon_matrix* mats, int32_t n, muon_dtype dtype,
                       const muon_config* cfg, void* workspace, size_t workspace_bytes,
                       void* stream);
 
 /* Orthogonalisation only: u = grad (momentum pointers ignored, cfg->momentum
- * and cfg->nesterov ignored), then normalisation and the iteration. */
+ * and cfg->nesterov ignored), then normalisation and the iteration: the
+ * Newton-Schulz stand-in for the SVD (yongjin360.com, Modded-NanoGPT
+ * green-AI article, technical evolution). With the cubic (1.5, -0.5, 0) and
+ * enough steps it tends to the polar factor U V^T of grad. */
 muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dtype,
                                const muon_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream);
@@ -251,18 +279,17 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
  * workspace base; -1 where a buffer does not exist). All buffers use the
  * rows<=cols orientation, zero-padded to mp x np (X) or mp x mp (A, B),
  * with mp and np the tile multiples (256 for bf16 sets, 128 for fp32
- * sets). bf16 sets: x_op0/x_op1 hold the high part of X (the 16-bit
- * matrix-core operand, ping-pong between steps) and x_lo the low part.
- * fp16 operands: one signed byte q per element, X = hi + q * 2^(e - 33)
- * with e = max(E, 1) and E the 5-bit exponent field of hi, stored in the
+ * sets). bf16 sets: x_op0/x_op1 hold the fp16 high part hi of X (the
+ * matrix-core operand, ping-pong between steps) and x_lo the low part, one
+ * OCP e4m3 byte per element with X = hi + byte * 2^-18, stored in the
  * update kernel's accumulator order (per 256 x 256 tile, 32-row blocks of
- * 8 KB). bf16 operands: a bf16 lo, X = hi + lo, row-major. gram (A) and
- * poly are 16-bit. The three 16-bit operands (x_op0/x_op1, gram, poly) are
- * stored in 32-column panels: element (r, c) is at element index
- * ((c / 32) * mp + r) * 32 + c % 32. With fp16 operands poly holds a I + B
- * (the a X term of the high part rides in the product). fp32 sets: x_op0/x_op1 are fp32 X
- * (ping-pong), gram/poly (B) fp32, all row-major, x_lo = -1. After a step
- * of k iterations X is in x_op[k % 2]. */
+ * 8 KB; within a block, per 64-column wave column and 32-column half, 64
+ * lanes x 16 bytes). gram (A) and poly are fp16. The three 16-bit operands
+ * (x_op0/x_op1, gram, poly) are stored in 32-column panels: element (r, c)
+ * is at element index ((c / 32) * mp + r) * 32 + c % 32. poly holds
+ * a I + B (the a X term of the high part rides in the product). fp32 sets:
+ * x_op0/x_op1 are fp32 X (ping-pong), gram/poly (B) fp32, all row-major,
+ * x_lo = -1. After a step of k iterations X is in x_op[k % 2]. */
 typedef struct {
   int64_t m, n, mp, np;
   int64_t x_lo, x_op0, x_op1, gram, poly;

@@ -22,7 +22,7 @@ __all__ = [
     "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
     "MuonAdamTensor", "MuonAdamConfig", "AdamPlan", "muon_adam_plan_create",
     "muon_adam_plan_step", "muon_adam_plan_destroy", "muon_adam_work_items",
-    "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT", "MUON_PRECISION_BF16_OPERANDS",
+    "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmuon_mi355x.so")
@@ -194,7 +194,7 @@ def _shape_matrices(shapes: Sequence, dtype: int):
     return arr, n
 
 
-MUON_PRECISION_DEFAULT, MUON_PRECISION_BF16_OPERANDS = 0, 1
+MUON_PRECISION_DEFAULT = 0
 
 
 def make_config(a: float, b: float, c: float, steps: int, momentum: float = 0.0,

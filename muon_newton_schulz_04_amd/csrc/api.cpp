@@ -132,9 +132,9 @@ hipEvent_t get_event(muon_plan_s* p) {
 muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t ws_bytes,
                       void* stream, bool orthogonalize_only, const muon_apply* ap = nullptr) {
   if (p == nullptr) return MUON_E_INVALID;
-  muon_status st = muon::validate_config(cfg);
-  if (st != MUON_OK) return st;
   const HostPlan& H = p->host;
+  muon_status st = muon::validate_config(cfg, H.dtype);
+  if (st != MUON_OK) return st;
   if (H.ws_bytes == 0) return MUON_OK;  // nothing to do (all matrices empty)
   if (ws == nullptr || ws_bytes < H.ws_bytes || reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return MUON_E_WORKSPACE;
@@ -174,7 +174,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     if (e == b) return MUON_OK;
     a.items = p->d_items[kind] + b;
     a.reduce = kind == muon::kGramReduce ? 1 : 0;
-    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, cfg->precision, a, e - b, q);
+    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, a, e - b, q);
     a.reduce = 0;
     return r == hipSuccess ? MUON_OK : MUON_E_LAUNCH;
   };
@@ -192,7 +192,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return give_back();
     a.items = p->d_whole[kind];
     a.reduce = kind == muon::kGramReduce ? 1 : 0;
-    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, cfg->precision, a, grid, s);
+    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, a, grid, s);
     a.reduce = 0;
     if (r != hipSuccess || hipEventRecord(t.stop, s) != hipSuccess) return give_back();
     p->pending.push_back(t);
@@ -227,16 +227,29 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   }
   if (H.ngroups == 1) return sequence(0, s);
   // several groups, no timing: each group runs its whole sequence on its
-  // own stream, forked once and joined once
+  // own stream, forked once and joined once. Every group that was forked is
+  // joined back to the caller's stream, also when a launch fails part way,
+  // so no work of this call outlives the stream order the caller sees (if a
+  // join itself cannot be enqueued, the host waits for that group).
   if (hipEventRecord(p->fork_ev, s) != hipSuccess) return MUON_E_LAUNCH;
-  for (int g = 0; g < H.ngroups; ++g) {
-    if (hipStreamWaitEvent(p->gstream[g], p->fork_ev, 0) != hipSuccess) return MUON_E_LAUNCH;
-    if ((st = sequence(g, p->gstream[g])) != MUON_OK) return st;
-    if (hipEventRecord(p->join_ev[g], p->gstream[g]) != hipSuccess) return MUON_E_LAUNCH;
+  muon_status res = MUON_OK;
+  int forked = 0;
+  for (int g = 0; g < H.ngroups && res == MUON_OK; ++g) {
+    if (hipStreamWaitEvent(p->gstream[g], p->fork_ev, 0) != hipSuccess) {
+      res = MUON_E_LAUNCH;
+      break;
+    }
+    forked = g + 1;
+    res = sequence(g, p->gstream[g]);
   }
-  for (int g = 0; g < H.ngroups; ++g)
-    if (hipStreamWaitEvent(s, p->join_ev[g], 0) != hipSuccess) return MUON_E_LAUNCH;
-  return MUON_OK;
+  for (int g = 0; g < forked; ++g) {
+    if (hipEventRecord(p->join_ev[g], p->gstream[g]) != hipSuccess ||
+        hipStreamWaitEvent(s, p->join_ev[g], 0) != hipSuccess) {
+      (void)hipStreamSynchronize(p->gstream[g]);
+      if (res == MUON_OK) res = MUON_E_LAUNCH;
+    }
+  }
+  return res;
 }
 
 // ---- plan cache for muon_step / muon_orthogonalize
@@ -260,7 +273,7 @@ std::string make_key(const muon_matrix* mats, int32_t n, muon_dtype dt) {
 
 muon_status cached_step(const muon_matrix* mats, int32_t n, muon_dtype dt, const muon_config* cfg,
                         void* ws, size_t ws_bytes, void* stream, bool ortho) {
-  muon_status st = muon::validate_config(cfg);
+  muon_status st = muon::validate_config(cfg, dt);
   if (st != MUON_OK) return st;
   st = muon::validate_matrices(mats, n, dt, !ortho && cfg->momentum != 0.f);
   if (st != MUON_OK) return st;

@@ -34,7 +34,6 @@
 
 namespace muon {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -55,7 +54,6 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
     static_cast<float*>(p)[i] = v;
   }
-  static __device__ __forceinline__ float round(float v) { return v; }
 };
 template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float load(const void* p, int64_t i) {
@@ -64,11 +62,10 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
     static_cast<uint16_t*>(p)[i] = f2bf(v);
   }
-  static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
 };
 
 // Operand formats of the matrix products (X, A, B in the workspace).
-enum OpFmt { OP_F32 = 0, OP_F16 = 1, OP_BF16 = 2 };
+enum OpFmt { OP_F32 = 0, OP_F16 = 1 };
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 template <int OP> struct Op;
@@ -119,26 +116,6 @@ template <> struct Op<OP_F16> {
     static_cast<uint16_t*>(p)[i] = bits(v);
   }
 };
-template <> struct Op<OP_BF16> {
-  static constexpr int bytes = 2;
-  // X = hi + lo (about 17 significant bits together)
-  static __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
-    hi = f2bf(x);
-    lo = f2bf(x - bf2f(static_cast<uint16_t>(hi)));
-  }
-  static __device__ __forceinline__ float join(uint32_t hi, uint32_t lo) {
-    return bf2f(static_cast<uint16_t>(hi)) + bf2f(static_cast<uint16_t>(lo));
-  }
-  static __device__ __forceinline__ float load16(uint32_t h) { return bf2f(static_cast<uint16_t>(h)); }
-  static __device__ __forceinline__ uint16_t bits(float v) { return f2bf(v); }
-  static __device__ __forceinline__ float load(const void* p, int64_t i) {
-    return bf2f(static_cast<const uint16_t*>(p)[i]);
-  }
-  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
-    static_cast<uint16_t*>(p)[i] = f2bf(v);
-  }
-};
-
 // Fixed-order block sum over 256 threads (deterministic).
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -185,6 +162,41 @@ struct WApply {
   }
 };
 
+// buf' = mu buf + g rounded once to the buffer's type, returned as a float
+// (the caller stores it; the store is exact). For fp32 state the fused
+// multiply-add is that rounding. For bf16 state s = fma(mu, b, g) is the
+// float32 nearest to the exact value, and rounding s to bf16 (ties to even)
+// gives the bf16 nearest to the exact value unless s lies exactly halfway
+// between two bf16 values while the exact value does not (double rounding).
+// Then the sign of the residual (mu b + g) - s decides, evaluated exactly
+// in float64: mu b is exact there (at most 32 significant bits), the sum
+// with g splits into its rounded value S and exact error E (Knuth's
+// TwoSum), and S - s is exact (the two are within a factor of two:
+// Sterbenz's lemma), so (S - s) + E has the residual's sign. s then moves
+// one float32 ulp toward the exact value, off the halfway point, before the
+// bf16 rounding. The float64 path runs only on halfway points.
+__device__ __forceinline__ float momentum_bf16(float mu, float b, float g) {
+  const float s = __fmaf_rn(mu, b, g);
+  const uint32_t bits = __float_as_uint(s);
+  if ((bits & 0xffffu) == 0x8000u) {
+    const double P = __dmul_rn(double(mu), double(b));
+    const double S = __dadd_rn(P, double(g));
+    const double bb = __dsub_rn(S, P);
+    const double E = __dadd_rn(__dsub_rn(P, __dsub_rn(S, bb)), __dsub_rn(double(g), bb));
+    const double d = __dadd_rn(__dsub_rn(S, double(s)), E);
+    if (d != 0.0 && d == d) {
+      const bool away = (d > 0.0) == (s > 0.0);  // toward the exact value
+      return bf2f(f2bf(__uint_as_float(away ? bits + 1u : bits - 1u)));
+    }
+  }
+  return bf2f(f2bf(s));
+}
+template <typename T>
+__device__ __forceinline__ float momentum_new(float mu, float b, float g) {
+  if constexpr (sizeof(T) == 2) return momentum_bf16(mu, b, g);
+  else return __fmaf_rn(mu, b, g);
+}
+
 // u from the gradient and the already-updated buffer (same expression in
 // both elementwise kernels so u is bitwise identical).
 __device__ __forceinline__ float form_u(float g, float nb, const StepArgs& A) {
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const float gf = Elem<T>::load(ge, e);
-          const float nb = Elem<T>::round(__fmaf_rn(A.mu, Elem<T>::load(be, e), gf));
+          const float nb = momentum_new<T>(A.mu, Elem<T>::load(be, e), gf);
           Elem<T>::store(oe, e, nb);
           const float u = form_u(gf, nb, A);
           acc = __fmaf_rn(u, u, acc);
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
       const float gf = Elem<T>::load(g, off);
       float u = gf;
       if (A.use_mom) {
-        const float nb = Elem<T>::round(__fmaf_rn(A.mu, Elem<T>::load(mb, off), gf));
+        const float nb = momentum_new<T>(A.mu, Elem<T>::load(mb, off), gf);
         Elem<T>::store(mb, off, nb);
         u = form_u(gf, nb, A);
       }
@@ -388,25 +400,11 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
     const int64_t off = int64_t(i0 + (v >> 3)) * M.np + j0 + (v & 7) * 8;
     if constexpr (OP != OP_F32) {
       const int64_t poff = pidx(i0 + (v >> 3), j0 + (v & 7) * 8, M.mp);
-      u32x4_t whi, wlo;
+      u32x4_t whi;  // the high parts; the low bytes go out below
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t h0, l0 = 0, h1, l1 = 0;
-        if constexpr (OP == OP_F16) {  // the low bytes go out below
-          h0 = Op<OP>::bits(u[h][2 * q]);
-          h1 = Op<OP>::bits(u[h][2 * q + 1]);
-        } else {
-          Op<OP>::split(u[h][2 * q], h0, l0);
-          Op<OP>::split(u[h][2 * q + 1], h1, l1);
-        }
-        whi[q] = h0 | (h1 << 16);
-        wlo[q] = l0 | (l1 << 16);
-      }
+      for (int q = 0; q < 4; ++q)
+        whi[q] = uint32_t(Op<OP>::bits(u[h][2 * q])) | (uint32_t(Op<OP>::bits(u[h][2 * q + 1])) << 16);
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]) + poff) = whi;
-      if constexpr (OP != OP_F16) {
-        uint16_t* lo = reinterpret_cast<uint16_t*>(A.ws + M.xl_off);
-        *reinterpret_cast<u32x4_t*>(lo + off) = wlo;
-      }
     } else {
       float* x0 = reinterpret_cast<float*>(A.ws + M.xo_off[0]) + off;
       reinterpret_cast<f32x4_t*>(x0)[0] = f32x4_t{u[h][0], u[h][1], u[h][2], u[h][3]};
@@ -523,8 +521,7 @@ __device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
   }
 }
 
-// One k-slab (128 bytes of k per row) of MFMAs for this wave's 64 x 64.
-template <int OP>
+// One k-slab (128 bytes of k per row) of fp32 MFMAs for this wave's 64 x 64.
 __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, const char* sB,
                                          int wm, int wn) {
   const int lane = threadIdx.x & 63;
@@ -539,34 +536,16 @@ __device__ __forceinline__ void mma_slab(f32x4_t (&acc)[4][4], const char* sA, c
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       bfr[j] = *reinterpret_cast<const uint4*>(sB + lds_off(wn * 64 + j * 16 + lr, ch));
-    if constexpr (OP == OP_BF16) {
+    // four k=4 MFMAs per 16-byte chunk; lane group g supplies k = 4(ch)+e
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]),
-              acc[i][j], 0, 0, 0);
-    } else if constexpr (OP == OP_F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bfr[j]),
-              acc[i][j], 0, 0, 0);
-    } else {
-      // four k=4 MFMAs per 16-byte chunk; lane group g supplies k = 4(ch)+e
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                __uint_as_float(comp(af[i], e)), __uint_as_float(comp(bfr[j], e)), acc[i][j], 0,
-                0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              __uint_as_float(comp(af[i], e)), __uint_as_float(comp(bfr[j], e)), acc[i][j], 0,
+              0, 0);
   }
 }
 
@@ -633,7 +612,7 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
       if (KIND == UPDATE) load_cols<ES>(rb, opB, ldb_b, k0 + KS);
       else load_rows(rb, opB, ldb_b, (k0 + KS) * ES);
     }
-    mma_slab<OP>(acc, sA, sB, wm, wn);
+    mma_slab(acc, sA, sB, wm, wn);
   }
 
   // ------------------------------------------------------------ epilogue
@@ -741,25 +720,19 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
 namespace e16 {
 
 constexpr int TM = 256;                // output tile rows
-constexpr int TN = kTileN16;           // output tile columns (128 or 256)
+constexpr int TN = kTileN16;           // output tile columns
 constexpr int WN = TN / 64;            // waves per tile row (2 rows of waves)
 constexpr int NWAVE = 2 * WN;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int KS = 32;                 // k per stage
-// Ring depth: 256 x 256 tiles run one workgroup per CU with four 32 KB
-// stages; 256 x 128 tiles run two per CU with three 24 KB stages each.
-#ifndef MUON_RING_STAGES
-#define MUON_RING_STAGES (kTileN16 == 256 ? 4 : 3)
-#endif
-constexpr int NS = MUON_RING_STAGES;
-constexpr int WG_PER_CU = TN == 256 ? 1 : 2;
+// Ring depth: one workgroup per CU with four 32 KB stages.
+constexpr int NS = 4;
 constexpr int HALF_A = TM * KS * 2;    // row operand of one stage: 16 KB
 constexpr int HALF_B = TN * KS * 2;    // column operand of one stage
 constexpr int STAGE = HALF_A + HALF_B;
 constexpr int LDS_BYTES = NS * STAGE;
 constexpr int KROW = TN * 2;           // bytes of one k-row of the [k][col] layout
-static_assert(TN == 128 || TN == 256, "tile width");
-static_assert(NS >= 3 && NS <= 8, "a stage in use, one in flight, one being refilled; K >= 8 stages");
+static_assert(TN == 256 && NS == 4, "the ring and its DMA split assume 256 x 256 tiles, 4 stages");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -818,16 +791,9 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 // never waits behind a DMA issue; measured against every wave issuing, on
 // one device back to back: the update launch 2 % faster, Gram and poly the
 // same.
-#ifndef MUON_DMA_WAVES
-#define MUON_DMA_WAVES (NWAVE / 2)
-#endif
-constexpr int DMA_WAVES = MUON_DMA_WAVES;
+constexpr int DMA_WAVES = NWAVE / 2;
 static_assert(NWAVE % DMA_WAVES == 0 && (16 + TN / 16) % DMA_WAVES == 0 && 16 % DMA_WAVES == 0, "DMA waves");
 constexpr int DMA_PER_STAGE = (16 + TN / 16) / DMA_WAVES;  // pieces per DMA wave per stage
-#ifndef MUON_SPLIT_DMA
-#define MUON_SPLIT_DMA 1
-#endif
-constexpr bool SPLIT_DMA = MUON_SPLIT_DMA;
 template <bool KN>
 __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0, int q) {
@@ -857,12 +823,9 @@ __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda
 
 template <int OP>
 __device__ __forceinline__ f32x16_t mfma(const u32x4& colop, const u32x4& rowop, f32x16_t c) {
-  if constexpr (OP == OP_F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, colop),
-                                                  __builtin_bit_cast(f16x8_t, rowop), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, colop),
-                                                   __builtin_bit_cast(bf16x8_t, rowop), c, 0, 0, 0);
+  static_assert(OP == OP_F16, "the 16-bit engine takes fp16 operands");
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, colop),
+                                                __builtin_bit_cast(f16x8_t, rowop), c, 0, 0, 0);
 }
 
 // Operand fragments of one k-step (16 k) of this wave's 128 x 64 block.
@@ -907,17 +870,6 @@ __device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int w
   for (int i = 0; i < 4; ++i) frag_load_a(f, st, ks, wm, i);
 }
 
-// Scheduling hint for a region holding one k-step of MFMAs (8) and the LDS
-// reads of the next k-step (8): alternate them, so the reads are spread over
-// the multiplies instead of bunching before or after them.
-__device__ __forceinline__ void interleave_mma_reads() {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-}
-
 // One k-step with DMA spread over it: the 8 MFMAs of fragment set fm, the
 // LDS reads of fragment set fl (k-step ks of the stage at `st`) and NCH DMA
 // pieces, dma(c) at the start of chunk c. Each chunk takes 4 / NCH row
@@ -953,14 +905,6 @@ __device__ __forceinline__ void kstep_dma(f32x16_t (&acc)[4][2], const Frag& fm,
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int OP>
-__device__ __forceinline__ void frag_mma(f32x16_t (&acc)[4][2], const Frag& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = mfma<OP>(f.b[j], f.a[i], acc[i][j]);
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool f16) {
@@ -1031,7 +975,7 @@ __device__ __forceinline__ void fold_bias(f32x16_t (&acc)[4][2], const char* st,
 // SK (Gram only): the variant that also runs split tiles and the reduce
 // pass, launched for plans that split Gram tiles.
 template <typename T, int OP, int KIND, bool LAST, bool SK = false>
-__global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepArgs P) {
+__global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
@@ -1107,24 +1051,17 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   const bool fold = KIND == POLY && P.c != 0.f;
   if (!reducing) {
   const int nst = static_cast<int>(K / KS);
-  constexpr bool SPLIT = SPLIT_DMA && NS >= 4 && DMA_PER_STAGE % 2 == 0 && 4 % (DMA_PER_STAGE / 2) == 0;
-  constexpr int H = DMA_PER_STAGE / 2;  // pieces per k-step (split issue)
-  if constexpr (SPLIT) {
-    // stages 0 .. NS-3 and the first half of stage NS-2 (its second half
-    // goes out with the first k-step of stage 0)
+  constexpr int H = DMA_PER_STAGE / 2;  // pieces per k-step (the DMA of a stage is split over two)
+  static_assert(DMA_PER_STAGE % 2 == 0 && 4 % H == 0, "DMA split");
+  // stages 0 .. NS-3 and the first half of stage NS-2 (its second half
+  // goes out with the first k-step of stage 0)
 #pragma unroll
-    for (int p = 0; p < NS - 2; ++p)
-      if (dma_wave) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+  for (int p = 0; p < NS - 2; ++p)
+    if (dma_wave) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
 #pragma unroll
-    for (int q = 0; q < H; ++q)
-      if (dma_wave) dma_piece<KN>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
-    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
-  } else {
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (dma_wave) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
-    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 2));  // stage 0 landed (this wave's pieces)
-  }
+  for (int q = 0; q < H; ++q)
+    if (dma_wave) dma_piece<KN>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
+  MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
   asm volatile("s_barrier" ::: "memory");
   // POLY with c != 0 folds the b A term into the accumulators on the way:
   // acc = A A + (b / c) A, and the epilogue scales by c. Column n of this
@@ -1138,7 +1075,7 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   for (int g = 0; g < nst; ++g) {
     const int nxt = cur == NS - 1 ? 0 : cur + 1;  // slot of stage g+1
     const int old = cur == 0 ? NS - 1 : cur - 1;  // slot of stage g-1 (unused for g = 0)
-    if constexpr (SPLIT) {
+    {
       // second half of stage g+NS-2 (its slot was freed at the previous
       // barrier; the first half went out then)
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
@@ -1146,12 +1083,6 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
       kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, [&](int c) {
         if (dma_wave) dma_piece<KN>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
       });
-    } else {
-      __builtin_amdgcn_sched_barrier(0);
-      frag_mma<OP>(acc, f0);
-      frag_load<KN>(f1, lds + cur * STAGE, 1, wm, wn);
-      interleave_mma_reads();
-      __builtin_amdgcn_sched_barrier(0);
     }
     // This wave's pieces of stage g+1 have landed (stages up to g+NS-2 may
     // still be in flight). A bare s_barrier: the workgroup fence of
@@ -1159,22 +1090,15 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
     // compiler from moving LDS accesses across it.
     MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3));
     asm volatile("s_barrier" ::: "memory");
-    // every wave has finished reading stage g-1: refill its slot (with the
-    // split issue, the first half of stage g+NS-1 now and the second half
-    // with the next k-step)
+    // every wave has finished reading stage g-1: refill its slot, the first
+    // half of stage g+NS-1 now and the second half with the next k-step
     // (after the last stage the fragment reads come from a stale slot; the
     // values are unused)
-    if constexpr (SPLIT) {
+    {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, [&](int c) {
         if (dma_wave) dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
       });
-    } else {
-      if (dma_wave) dma_stage<KN>(lds + old * STAGE, opA, lda, opB, ldb, int64_t(min(g + NS - 1, nst - 1)) * KS);
-      __builtin_amdgcn_sched_barrier(0);
-      frag_mma<OP>(acc, f1);
-      frag_load<KN>(f0, lds + nxt * STAGE, 0, wm, wn);
-      interleave_mma_reads();
     }
     if constexpr (KIND == POLY) {
       // (stage g stays in its slot until every wave has passed the next
@@ -1196,7 +1120,6 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
   // there: rows with 16-byte reads (whole 128-byte lines per store), columns
   // (mirror, transposed output) with transposing reads, 8 rows per lane.
   const int l32 = lane & 31, lh = lane >> 5;
-  constexpr bool F16 = OP == OP_F16;
   constexpr int ROWB = TN * 2;   // bytes per staged row
   constexpr int CPR = TN / 8;    // 16-byte chunks per staged row
   const int m0 = TI * TM, n0 = TJ * TN;  // tile origin
@@ -1296,13 +1219,11 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 float v = P.c * acc[i][j][4 * g + r];
-                if constexpr (OP == OP_F16) {
-                  const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh + r;
-                  if (m == n && m < M.m) v += P.a;  // padding stays zero
-                }
+                const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh + r;
+                if (m == n && m < M.m) v += P.a;  // padding stays zero
                 acc[i][j][4 * g + r] = v;
               }
-        stage16(F16);
+        stage16(true);
       } else {
       // c = 0: the A tile goes into the staging layout by DMA (whole rows,
       // coalesced); each lane then reads its accumulator positions, combines
@@ -1337,10 +1258,9 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               v[r] = __fmaf_rn(P.c, acc[i][j][4 * g + r], P.b * a4[r]);
-              if constexpr (OP == OP_F16)
-                if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
+              if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
             }
-            *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], F16);
+            *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], true);
           }
       }
     } else if (SK && reducing) {
@@ -1377,11 +1297,11 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
           const int r = qr * 128 + 32 * (blk >> 1) + (ln & 31);
           const int c = (2 * qc + wl) * 8 + 4 * (blk & 1) + v;
           *reinterpret_cast<uint2*>(lds + soff(r, c) + (ln >> 5) * 8) =
-              e16::pack4(sum[u][0], sum[u][1], sum[u][2], sum[u][3], F16);
+              e16::pack4(sum[u][0], sum[u][1], sum[u][2], sum[u][3], true);
         }
       }
     } else {
-      stage16(F16);
+      stage16(true);
     }
     __syncthreads();
     // (the reduce pass of a split tile stores its quarter only)
@@ -1415,12 +1335,10 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
       }
     });
   } else {
-    // UPDATE. fp16 operands: the low bytes are read (and, unless this is
-    // the last step, written back) in accumulator order, one 16-byte access
-    // per lane and accumulator block, all loads first (one latency for the
-    // tile). bf16 operands: the low part is row-major and read at the
-    // accumulator positions with the high part, one row group at a time.
-    if constexpr (F16) {
+    // UPDATE. The low bytes are read (and, unless this is the last step,
+    // written back) in accumulator order, one 16-byte access per lane and
+    // accumulator block, all loads first (one latency for the tile).
+    {
       char* lo_t = P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) + lane * 16;
       auto lo_ptr = [&](int i, int j) { return lo_t + (((wm * 4 + i) * WN + wn) * 2 + j) * 1024; };
       u32x4 lq[4][2];
@@ -1468,55 +1386,9 @@ __global__ __launch_bounds__(e16::NTHR, e16::WG_PER_CU) void gemm16_kernel(StepA
         });
         return;
       }
-    } else {
-      const int64_t ldx = M.np;
-      const uint16_t* hi_cur = reinterpret_cast<const uint16_t*>(P.ws + M.xo_cur);
-      auto lo_ptr = [&](int i, int j, int g) -> uint16_t* {
-        return reinterpret_cast<uint16_t*>(P.ws + M.xl_off) + int64_t(mb + 32 * i + l32) * ldx + nb + 32 * j +
-               8 * g + 4 * lh;
-      };
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 lv[2][4], hv[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            lv[j][g] = *reinterpret_cast<const u32x2*>(lo_ptr(i, j, g));
-            hv[j][g] = *reinterpret_cast<const u32x2*>(
-                hi_cur + pidx(mb + 32 * i + l32, nb + 32 * j + 8 * g + 4 * lh, M.mp));
-          }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t lw[4] = {lv[j][g].x & 0xffffu, lv[j][g].x >> 16, lv[j][g].y & 0xffffu,
-                                    lv[j][g].y >> 16};
-            // X' = B hi + a (hi + lo)
-            const uint32_t hw[4] = {hv[j][g].x & 0xffffu, hv[j][g].x >> 16, hv[j][g].y & 0xffffu,
-                                    hv[j][g].y >> 16};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j][4 * g + r] = __fmaf_rn(P.a, Op<OP>::join(hw[r], lw[r]), acc[i][j][4 * g + r]);
-            if constexpr (!LAST) {
-              uint32_t nh[4], nl[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) Op<OP>::split(acc[i][j][4 * g + r], nh[r], nl[r]);
-              *reinterpret_cast<uint2*>(lo_ptr(i, j, g)) =
-                  make_uint2(nl[0] | (nl[1] << 16), nl[2] | (nl[3] << 16));
-            }
-          }
-      }
     }
-    if constexpr (!LAST) {
-      // the next high part (the operand of the next step), rows of the tile
-      stage16(F16);  // rounds each value to the operand format, as split does
-      __syncthreads();
-      uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
-      rows_out([&](int m, int n, const uint4& v) {
-        *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
-      });
-    } else if (P.apply) {
+    // the last step: X is the result
+    if (P.apply) {
       // weight application: W' = W keep - step X in the caller's layout
       // (transposed for tall matrices); X is staged as fp16, three more
       // significant bits than the set's bf16
@@ -1603,10 +1475,8 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_kernel(int kind, muon_dtype dt, int precision, const StepArgs& a, int grid,
-                         hipStream_t s) {
+hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s) {
   if (dt == MUON_F32) return launch_t<float, OP_F32>(kind, a, grid, s);
-  if (precision == MUON_PRECISION_BF16_OPERANDS) return launch_t<uint16_t, OP_BF16>(kind, a, grid, s);
   return launch_t<uint16_t, OP_F16>(kind, a, grid, s);
 }
 

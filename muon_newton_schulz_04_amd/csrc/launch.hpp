@@ -25,8 +25,6 @@ struct StepArgs {
   int64_t split_off;  // workspace offset of the split Gram partials (-1: none)
 };
 
-// precision: muon_precision (operand format of bf16 sets).
-hipError_t launch_kernel(int kind, muon_dtype dt, int precision, const StepArgs& a, int grid,
-                         hipStream_t s);
+hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s);
 
 }  // namespace muon

@@ -14,10 +14,7 @@ namespace muon {
 // Tile sizes shared by the planner and the kernels.
 constexpr int kGemmTile = 128;         // output tile of the matrix-core kernels (fp32 sets)
 constexpr int kTileM16 = 256;          // 16-bit-operand engine (bf16 sets): 256 x 256 tiles
-#ifndef MUON_TILE_N
-#define MUON_TILE_N 256
-#endif
-constexpr int kTileN16 = MUON_TILE_N;
+constexpr int kTileN16 = 256;
 constexpr int kNormTile = 64;          // tile of the normalise / layout kernel
 constexpr int kMomentumElems = 16384;  // target elements per momentum work item
 constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X
@@ -43,9 +40,9 @@ struct MatInfo {
   int32_t mp, np;    // m, n padded to the engine's tile multiples
   int32_t tall;      // rows > cols: the iteration runs on the transpose
   int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
-  int64_t xl_off;    // bf16 sets: low part of X (one signed byte per element
-                     // for fp16 operands, a bf16 lo for bf16 operands; sized
-                     // for the latter), -1 otherwise
+  int64_t xl_off;    // bf16 sets: low part of X, one OCP e4m3 byte per
+                     // element holding (X - hi) 2^18 (saturating at +-448,
+                     // reached only when |X| >= 4), -1 otherwise
   int64_t xo_off[2]; // bf16 sets: ping-pong high parts (the matrix-core
                      // operand); fp32 sets: ping-pong fp32 X
   int64_t a_off;     // A = X X^T
@@ -76,10 +73,7 @@ struct Schedule {
 // Large sets are split into groups of matrices that run concurrently on
 // streams of their own, so one group's kernels fill the CUs that the other
 // group's tail (the last, partial wave of tiles) and launch gaps leave idle.
-#ifndef MUON_MAX_GROUPS
-#define MUON_MAX_GROUPS 2
-#endif
-constexpr int kMaxGroups = MUON_MAX_GROUPS;
+constexpr int kMaxGroups = 2;
 constexpr int kGroupMinTiles = 512;  // matrix-core tiles per update launch to split
 
 struct HostPlan {
@@ -105,8 +99,8 @@ struct HostPlan {
 // Validates the matrix set (shapes, dtype, alignment, overlaps).
 muon_status validate_matrices(const muon_matrix* mats, int32_t n, muon_dtype dtype,
                               bool need_momentum);
-// Validates per-call scalars.
-muon_status validate_config(const muon_config* cfg);
+// Validates per-call scalars for a set of `dtype`.
+muon_status validate_config(const muon_config* cfg, muon_dtype dtype);
 // Validates the weights of a plan's matrices (one record per matrix; empty
 // matrices' records are ignored) against the set's buffers.
 muon_status validate_weights(const HostPlan& plan, const muon_weight* w, int32_t n);

@@ -7,13 +7,14 @@ never does; see ``oracle/muon_oracle.py`` for the arithmetic and its sources.
 from .muon_oracle import (  # noqa: F401
     bf16_round,
     fp32_round,
+    two_sum,
+    round_exact_sum,
     momentum_update,
     frobenius_normalize,
     newton_schulz,
     ns_polynomial_step,
     orthogonalize,
     muon_update,
-    muon_update_set,
     apply_weight,
     adam_update,
     falg_flops,

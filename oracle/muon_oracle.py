@@ -36,13 +36,14 @@ import numpy as np
 __all__ = [
     "bf16_round",
     "fp32_round",
+    "two_sum",
+    "round_exact_sum",
     "momentum_update",
     "frobenius_normalize",
     "ns_polynomial_step",
     "newton_schulz",
     "orthogonalize",
     "muon_update",
-    "muon_update_set",
     "apply_weight",
     "adam_update",
     "falg_flops",
@@ -89,6 +90,37 @@ def fp32_round(x) -> np.ndarray:
 _ROUND = {"bf16": bf16_round, "fp32": fp32_round, "f64": lambda x: np.asarray(x, np.float64)}
 
 
+def two_sum(a, b):
+    """Error-free sum of two float64 arrays (Knuth's TwoSum): returns (s, e)
+    with s = fl(a + b) and s + e == a + b exactly (round to nearest, no
+    overflow)."""
+    s = a + b
+    bb = s - a
+    e = (a - (s - bb)) + (b - bb)
+    return s, e
+
+
+def round_exact_sum(hi, lo, fmt: str) -> np.ndarray:
+    """Round the exact real value hi + lo (an unevaluated float64 sum with
+    hi = fl(hi + lo)) to the storage format ``fmt`` ("bf16" or "fp32"),
+    round to nearest, ties to even.
+
+    Every value and every halfway point of bf16 and fp32 is a float64, and
+    rounding to float64 is monotone, so hi lies on the same side of each
+    halfway point as hi + lo unless hi *is* a halfway point. Only then does
+    lo decide: a positive lo moves the value above the halfway point, a
+    negative one below it; lo == 0 is a true tie (ties to even).
+    """
+    rnd = _ROUND[fmt]
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.asarray(lo, dtype=np.float64)
+    r = rnd(hi)
+    up = rnd(np.nextafter(hi, np.inf))
+    down = rnd(np.nextafter(hi, -np.inf))
+    tie = (up != down) & np.isfinite(hi) & (lo != 0)
+    return np.where(tie, np.where(lo > 0, up, down), r)
+
+
 # ---------------------------------------------------------------------------
 # The update, step by step.
 # ---------------------------------------------------------------------------
@@ -96,24 +128,27 @@ _ROUND = {"bf16": bf16_round, "fp32": fp32_round, "f64": lambda x: np.asarray(x,
 def momentum_update(g, buf, mu: float, nesterov: bool, buf_dtype: str = "bf16"):
     """Momentum step of the Muon update. Returns (u, new_buf).
 
-    buf' = mu * buf + g, rounded to the buffer's storage dtype (via the
-    float32 fused multiply-add value for bf16/fp32 buffers); the vector that
-    is orthogonalised is u = g + mu * buf' (Nesterov) or u = buf'.
+    buf' = mu * buf + g, the exact real value rounded once to the buffer's
+    storage dtype (round to nearest, ties to even); the vector that is
+    orthogonalised is u = g + mu * buf' (Nesterov) or u = buf'.
     With mu == 0 (no momentum state) u = g and buf is ignored.
     [MUON]: Muon keeps a single momentum buffer per hidden matrix.
+
+    For bf16 and fp32 state with a float32 mu the product mu * buf has at
+    most 48 significant bits, so it is exact in float64; the sum with g is
+    carried exactly as a float64 pair (two_sum) and rounded once.
     """
     g = np.asarray(g, dtype=np.float64)
     if mu == 0.0 or buf is None:
         return g.copy(), None
     buf = np.asarray(buf, dtype=np.float64)
-    acc = mu * buf + g              # exact for bf16/fp32 state and float32 mu
     if buf_dtype in ("bf16", "fp32"):
-        # The stored buffer is a quantisation of mu*buf + g. The decision is
-        # taken in the precision the update is computed in: one float32
-        # fused multiply-add (a single rounding of the exact value), then
-        # rounding to the buffer's storage type.
-        acc = fp32_round(acc)
-    new_buf = _ROUND[buf_dtype](acc)
+        if float(np.float32(mu)) != float(mu):
+            raise ValueError("mu must be a float32 value for bf16/fp32 state")
+        hi, lo = two_sum(mu * buf, g)
+        new_buf = round_exact_sum(hi, lo, buf_dtype)
+    else:
+        new_buf = mu * buf + g
     u = g + mu * new_buf if nesterov else new_buf.copy()
     return u, new_buf
 
@@ -171,16 +206,6 @@ def muon_update(g, buf, *, a: float, b: float, c: float, steps: int, mu: float,
     """
     u, new_buf = momentum_update(g, buf, mu, nesterov, buf_dtype)
     return newton_schulz(frobenius_normalize(u, eps), a, b, c, steps), new_buf
-
-
-def muon_update_set(grads, bufs, **cfg):
-    """``muon_update`` applied to each matrix of a set independently."""
-    outs, new_bufs = [], []
-    for i, g in enumerate(grads):
-        o, nb = muon_update(g, None if bufs is None else bufs[i], **cfg)
-        outs.append(o)
-        new_bufs.append(nb)
-    return outs, new_bufs
 
 
 def apply_weight(w, x, *, lr: float, wd: float, lr_mul: float = 1.0, wd_mul: float = 1.0,

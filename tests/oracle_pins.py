@@ -10,7 +10,8 @@ AssertionError when the implementation disagrees with an independent fact:
     exact rational arithmetic;
   * a naive pure-Python loop implementation on tiny inputs;
   * invariants (scale, sign, transpose, orthogonal equivariance, rank, zero);
-  * momentum closed forms; bf16 rounding against torch's float32 -> bfloat16
+  * momentum closed forms; the buffer's single rounding against exact
+    rational arithmetic; bf16 rounding against torch's float32 -> bfloat16
     cast and hand-made ties.
 ``test_oracle.py`` runs every pin on the oracle; ``test_oracle_mutations.py``
 plants mistakes in copies of the oracle and checks a pin catches each one.
@@ -88,34 +89,86 @@ def pin_closed_form_with_momentum(impl):
         assert rel_fro(out3, closed_form(mu * g1 + g2, 1.5, -0.5, 0.0, 4)) < 1e-11
 
 
+def exact_round(v: Fraction, sig_bits: int) -> float:
+    """Round the rational v to the nearest value with `sig_bits` significant
+    bits and float32's exponent range (bf16: 8, fp32: 24), ties to even,
+    by exact rational arithmetic: normal exponents from -126, a fixed
+    spacing of 2**(-126 - sig_bits + 1) below 2**-126, +-inf from 2**128."""
+    if v == 0:
+        return 0.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2**e <= a < 2**(e+2)
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - sig_bits + 1)
+    q = a / ulp
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * ulp
+    out = math.inf if r >= Fraction(2) ** 128 else float(r)
+    return -out if v < 0 else out
+
+
 def pin_momentum_bf16_state(impl):
-    """The stored buffer is the bf16 rounding of mu*buf + g, and the Nesterov
+    """The stored buffer is the exact mu*buf + g rounded once to the buffer's
+    dtype (checked against exact rational arithmetic), and the Nesterov
     vector uses that rounded buffer."""
     rng = np.random.default_rng(3)
-    mu = 0.95
+    mu = float(np.float32(0.95))         # the library's mu is a float32
     g1 = torch.tensor(rng.standard_normal((8, 12)), dtype=torch.bfloat16).double().numpy()
     g2 = torch.tensor(rng.standard_normal((8, 12)), dtype=torch.bfloat16).double().numpy()
     u1, b1 = impl.momentum_update(g1, np.zeros_like(g1), mu, True, "bf16")
     assert np.array_equal(b1, g1) and np.array_equal(u1, g1 + mu * g1)   # u = (1+mu) g
     u2, b2 = impl.momentum_update(g2, b1, mu, True, "bf16")
-    # float32 FMA value (torch: exact float64 value cast once to float32),
-    # then float32 -> bfloat16 (torch's round-to-nearest-even cast)
-    want_b2 = torch.tensor(mu * g1 + g2, dtype=torch.float64).float().to(torch.bfloat16)
-    want_b2 = want_b2.double().numpy()
+    want_b2 = np.array([exact_round(Fraction(mu) * Fraction(x) + Fraction(y), 8)
+                        for x, y in zip(b1.ravel().tolist(), g2.ravel().tolist())]).reshape(b1.shape)
     assert np.array_equal(b2, want_b2)
     assert np.array_equal(u2, g2 + mu * want_b2)
     assert not np.array_equal(b2, mu * g1 + g2)   # rounding actually happened
-    # a case where rounding the exact value directly would differ: mu32*b + g
-    # lies just below the bf16 tie 2.0234375, its float32 rounding sits on the
-    # tie, and ties go to the even neighbour 2.03125 (not 2.015625)
-    mu32 = float(np.float32(0.9))
+    # many random bf16 (buf, g) pairs with a float32 mu, exponents up to 2**+-40
+    # apart, for bf16 and fp32 state: a single rounding of the exact value
+    mu32 = mu
+    n = 6000
+    bb = torch.tensor(rng.standard_normal(n) * 2.0 ** rng.integers(-40, 40, n),
+                      dtype=torch.bfloat16).double().numpy()
+    gg = torch.tensor(rng.standard_normal(n) * 2.0 ** rng.integers(-40, 40, n),
+                      dtype=torch.bfloat16).double().numpy()
+    bb[: n // 2] = torch.tensor(rng.standard_normal(n // 2), dtype=torch.bfloat16).double().numpy()
+    gg[: n // 2] = torch.tensor(rng.standard_normal(n // 2), dtype=torch.bfloat16).double().numpy()
+    for fmt, bits in (("bf16", 8), ("fp32", 24)):
+        _, nb = impl.momentum_update(gg, bb, mu32, False, fmt)
+        want = [exact_round(Fraction(mu32) * Fraction(x) + Fraction(y), bits)
+                for x, y in zip(bb.tolist(), gg.tolist())]
+        assert np.array_equal(nb, np.array(want)), fmt
+    # a case where rounding through float32 would differ: mu32*b + g lies
+    # just below the bf16 halfway point 2.0234375 and its float32 rounding
+    # lands on it (ties to even would then give 2.03125); the exact value
+    # rounds down to 2.015625
+    mu9 = float(np.float32(0.9))
     b, g = np.array([0.078125]), np.array([1.953125])     # both bfloat16 values
-    exact = mu32 * b + g
+    exact = mu9 * b + g
     assert exact[0] < 2.0234375 and np.float32(exact[0]) == np.float32(2.0234375)
-    _, nb = impl.momentum_update(g, b, mu32, False, "bf16")
-    assert nb[0] == 2.03125
+    _, nb = impl.momentum_update(g, b, mu9, False, "bf16")
+    assert nb[0] == 2.015625
+    # a case where the float64 sum itself is inexact: mu*b = 1 + 2**-8 is the
+    # bf16 halfway point between 1 and 1 + 2**-7, and g = 2**-80 puts the
+    # exact value above it (the float64 sum drops g and would tie to 1)
+    _, nb = impl.momentum_update(np.array([2.0 ** -80, -(2.0 ** -80)]),
+                                 np.array([2.0 + 2 ** -7, 2.0 + 2 ** -7]), 0.5, False, "bf16")
+    assert nb[0] == 1.0 + 2 ** -7 and nb[1] == 1.0
     u0, b0 = impl.momentum_update(g2, None, 0.0, True, "bf16")
     assert b0 is None and np.array_equal(u0, g2)
+    try:                                  # a float64 mu would make mu*buf inexact
+        impl.momentum_update(g2, b1, 0.95, True, "bf16")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a mu that is not a float32 value must be refused")
 
 
 def pin_polar_limit(impl):

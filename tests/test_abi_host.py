@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert mu.muon_abi_version() == 1
+    assert mu.muon_abi_version() == 2
     for code in range(9):
         s = mu.muon_status_str(code)
         assert s and s != "unknown status"
@@ -97,7 +97,8 @@ def test_config_validation_before_any_device_call(lib):
     mats = arr_of([(4, 8, 8, B, B + 4096, B + 8192)])
     bad = [mu.make_config(1, 0, 0, 65), mu.make_config(1, 0, 0, -1),
            mu.make_config(float("nan"), 0, 0, 1), mu.make_config(1, 0, 0, 1, momentum=1.0),
-           mu.make_config(1, 0, 0, 1, momentum=-0.1), mu.make_config(1, 0, 0, 1, eps=-1.0)]
+           mu.make_config(1, 0, 0, 1, momentum=-0.1), mu.make_config(1, 0, 0, 1, eps=-1.0),
+           mu.make_config(1, 0, 0, 1, precision=1)]          # only the default operand format
     for cfg in bad:
         assert lib.muon_step(mats, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 1
     cfg = mu.make_config(1, 0, 0, 1, momentum=0.9)
@@ -105,6 +106,31 @@ def test_config_validation_before_any_device_call(lib):
     assert lib.muon_step(nomom, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 1
     assert lib.muon_step(mats, 1, mu.MUON_BF16, None, None, 0, None) == 1
     assert lib.muon_plan_step(None, ctypes.byref(cfg), None, 0, None) == 1
+
+
+def test_coefficient_range_check_for_bf16_sets(lib):
+    """bf16 sets refuse coefficients that take a point of [0, 1] outside
+    [-2, 2] within the configured steps (fp16 operands, the low byte of X),
+    or whose B = b A + c A A could leave fp16's range; fp32 sets take any
+    finite coefficients. Every coefficient set the workloads use passes."""
+    mats = arr_of([(4, 8, 8, B, B + 4096, B + 8192)])
+    ok = [mu.make_config(3.4445, -4.7750, 2.0315, 5), mu.make_config(1.5, -0.5, 0.0, 10),
+          mu.make_config(3.4445, -4.7750, 2.0315, 64), mu.make_config(1.0, 0.0, 0.0, 64),
+          mu.make_config(0.0, 1.0, 0.0, 1), mu.make_config(0.0, 0.0, 1.0, 1),
+          mu.make_config(2.0, 0.0, 0.0, 1), mu.make_config(-1.0, 0.0, 0.0, 3)]
+    bad = [mu.make_config(2.0, 0.0, 0.0, 2),          # 4 x after two steps
+           mu.make_config(3.0, 0.0, 0.0, 1),          # 3 x
+           mu.make_config(3.4445, 0.0, 0.0, 1),       # the quintic's linear term alone
+           mu.make_config(0.0, 0.0, 300.0, 0),        # 16 |c| > 4096, even with zero steps
+           mu.make_config(1.0, 2000.0, -2000.0, 1)]   # 4|b| + 16|c| too large
+    # mats has a NULL-free set but no workspace: a config that passes
+    # validation then fails on the workspace (5), one that does not fails
+    # with MUON_E_INVALID (1), before any device call
+    for cfg in ok:
+        assert lib.muon_step(mats, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 5
+    for cfg in bad:
+        assert lib.muon_step(mats, 1, mu.MUON_BF16, ctypes.byref(cfg), None, 0, None) == 1
+        assert lib.muon_step(mats, 1, mu.MUON_F32, ctypes.byref(cfg), None, 0, None) == 5
 
 
 def expected_ws(shapes, dtype):
@@ -119,7 +145,7 @@ def expected_ws(shapes, dtype):
         m, n = min(r, c), max(r, c)
         t = 256 if dtype == mu.MUON_BF16 else 128
         mp, np_ = ru(m, t), ru(n, t)
-        sizes = ([mp * np_ * 2, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
+        sizes = ([mp * np_, mp * np_ * 2, mp * np_ * 2, mp * mp * 2, mp * mp * 2]
                  if dtype == mu.MUON_BF16 else
                  [mp * np_ * 4, mp * np_ * 4, mp * mp * 4, mp * mp * 4])
         for s in sizes:

@@ -29,9 +29,14 @@ MUTATIONS = {
     "coeffs_swapped": ("x = ns_polynomial_step(x, a, b, c)", "x = ns_polynomial_step(x, a, c, b)"),
     "nesterov_old_buffer": ("u = g + mu * new_buf if nesterov", "u = g + mu * buf if nesterov"),
     "nesterov_ignored": ("u = g + mu * new_buf if nesterov else new_buf.copy()", "u = new_buf.copy()"),
-    "buffer_not_rounded": ("new_buf = _ROUND[buf_dtype](acc)", "new_buf = acc"),
-    "buffer_rounded_from_f64": ("        acc = fp32_round(acc)\n", "        pass\n"),
-    "ema_momentum": ("acc = mu * buf + g ", "acc = mu * buf + (1 - mu) * g "),
+    "buffer_not_rounded": ("new_buf = round_exact_sum(hi, lo, buf_dtype)", "new_buf = hi + lo"),
+    "buffer_rounded_via_fp32": ("new_buf = round_exact_sum(hi, lo, buf_dtype)",
+                                "new_buf = _ROUND[buf_dtype](fp32_round(hi))"),
+    "buffer_rounded_from_f64_sum": ("new_buf = round_exact_sum(hi, lo, buf_dtype)",
+                                    "new_buf = _ROUND[buf_dtype](hi)"),
+    "tie_direction_flipped": ("np.where(lo > 0, up, down)", "np.where(lo < 0, up, down)"),
+    "two_sum_error_dropped": ("e = (a - (s - bb)) + (b - bb)", "e = 0.0 * s"),
+    "ema_momentum": ("hi, lo = two_sum(mu * buf, g)", "hi, lo = two_sum(mu * buf, (1 - mu) * g)"),
     "bf16_7_bits": ("np.rint(np.ldexp(f[normal], 8)), e[normal] - 8)",
                     "np.rint(np.ldexp(f[normal], 7)), e[normal] - 7)"),
     "bf16_truncate": ("np.rint(np.ldexp(f[normal], 8))", "np.trunc(np.ldexp(f[normal], 8))"),
