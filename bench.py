@@ -87,8 +87,9 @@ def roofline_of(flops, nbytes, secs, dtype):
 
 def vendor_ceiling(wl, reps: int = 50):
     """Empirical ceiling from the vendor GEMM (hipBLASLt through torch,
-    bf16 operands, fp32 accumulation): dense TFLOP/s of single GEMMs at the
-    step's shapes and at 8192^3, and a plain torch version of the whole
+    bf16 operands, fp32 accumulation): dense TFLOP/s of batched GEMMs at the
+    step's shapes (one launch per shape group) and of one 8192^3 GEMM, and a
+    plain torch version of the whole
     Newton-Schulz part of the step (batched products over each shape group,
     every operand contiguous), timed with events on the current stream."""
     import torch
@@ -108,14 +109,16 @@ def vendor_ceiling(wl, reps: int = 50):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3
 
+    # batched over a shape group, so that one launch fills the GPU (single
+    # small GEMMs measure the host's launch rate, not the matrix cores)
     gemms = {}
-    for (m, k, n) in [(768, 768, 768), (768, 3072, 768), (768, 768, 3072), (1024, 1024, 1024),
-                      (1024, 4096, 1024), (1024, 1024, 4096), (2048, 8192, 2048),
-                      (2048, 2048, 8192), (8192, 8192, 8192)]:
-        x = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
-        y = torch.randn(k, n, device=dev, dtype=torch.bfloat16)
-        t = timed(lambda: torch.matmul(x, y))
-        gemms[f"{m}x{k}x{n}"] = {"us": t * 1e6, "TFLOP/s": 2.0 * m * k * n / t / 1e12}
+    for (bt, m, k, n) in [(48, 768, 768, 768), (24, 768, 3072, 768), (24, 768, 768, 3072),
+                          (96, 1024, 1024, 1024), (24, 1024, 4096, 1024), (24, 1024, 1024, 4096),
+                          (32, 2048, 8192, 2048), (32, 2048, 2048, 8192), (1, 8192, 8192, 8192)]:
+        x = torch.randn(bt, m, k, device=dev, dtype=torch.bfloat16)
+        y = torch.randn(bt, k, n, device=dev, dtype=torch.bfloat16)
+        t = timed(lambda: torch.bmm(x, y))
+        gemms[f"{bt}x({m}x{k}x{n})"] = {"us": t * 1e6, "TFLOP/s": 2.0 * bt * m * k * n / t / 1e12}
         del x, y
     # the step's Newton-Schulz part in plain torch (X in rows <= cols form)
     groups = {}
