@@ -394,7 +394,7 @@ def report(name, rows):
     os.makedirs(out, exist_ok=True)
     groups = {}
     for r in rows:
-        groups.setdefault((r["shape"], r["step"]), []).append(r)
+        groups.setdefault((tuple(r["shape"]), r["step"]), []).append(r)
     lines = [f"### {name}", "",
              "| step | shape | matrices | max rel Frobenius | median | worst 256x256 tile | "
              "max abs err / max abs |", "|---|---|---|---|---|---|---|"]
