@@ -63,7 +63,8 @@ typedef enum {
   MUON_E_WORKSPACE = 5, /* workspace NULL or smaller than muon_workspace_bytes */
   MUON_E_DEVICE = 6,    /* no usable gfx950 device / HIP runtime error */
   MUON_E_LAUNCH = 7,    /* a kernel launch failed */
-  MUON_E_ALLOC = 8      /* host or device allocation for a plan failed */
+  MUON_E_ALLOC = 8,     /* host or device allocation for a plan failed */
+  MUON_E_SCRATCH = 9    /* the set needs more workspace than MUON_SCRATCH_BYTES */
 } muon_status;
 
 /* Element type of grad, momentum and out (one type per call). */
@@ -154,6 +155,24 @@ muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtyp
  * Calls on the same workspace must be ordered (same stream). */
 muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory during their loop (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): muon_plan_step with the workspace taken from a fixed device
+ * array of MUON_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends (its address is looked up when the first plan is created on
+ * that GPU). The call allocates nothing and creates no stream or event; it
+ * enqueues exactly the kernels muon_plan_step enqueues, with bitwise the
+ * same results, and ignores per-kernel timing. MUON_E_SCRATCH (nothing
+ * enqueued) if the plan's set needs more than MUON_SCRATCH_BYTES of
+ * workspace (a GPT-2 block set needs about 50 MB, the 124M set about
+ * 600 MB). Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream are safe. No state carries
+ * over between calls: every byte a step reads from the array it has written
+ * first. */
+#define MUON_SCRATCH_BYTES (128u << 20)
+muon_status muon_plan_step_noalloc(muon_plan* plan, const muon_config* cfg, void* stream);
 
 /* Frees a plan after waiting for the device (NULL is a no-op). Plans own
  * only their descriptor tables and, for sets split into concurrent groups,

@@ -20,6 +20,7 @@ __all__ = [
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
     "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
+    "muon_plan_step_noalloc", "MUON_SCRATCH_BYTES",
     "MuonAdamTensor", "MuonAdamConfig", "AdamPlan", "muon_adam_plan_create",
     "muon_adam_plan_step", "muon_adam_plan_destroy", "muon_adam_work_items",
     "MUON_F32", "MUON_BF16", "MUON_PRECISION_DEFAULT",
@@ -29,7 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libm
 MUON_F32, MUON_BF16 = 0, 1
 KERNEL_NAMES = ["momentum", "normalize", "gram", "poly", "update"]
 STATUS = ["MUON_OK", "MUON_E_INVALID", "MUON_E_DTYPE", "MUON_E_SHAPE", "MUON_E_ALIGN",
-          "MUON_E_WORKSPACE", "MUON_E_DEVICE", "MUON_E_LAUNCH", "MUON_E_ALLOC"]
+          "MUON_E_WORKSPACE", "MUON_E_DEVICE", "MUON_E_LAUNCH", "MUON_E_ALLOC", "MUON_E_SCRATCH"]
+MUON_SCRATCH_BYTES = 128 << 20
 
 
 class MuonError(RuntimeError):
@@ -96,6 +98,7 @@ def load_library(path: str = LIB_PATH):
         "muon_workspace_bytes": (i32, [P(MuonMatrix), i32, i32, P(sz)]),
         "muon_plan_create": (i32, [P(MuonMatrix), i32, i32, P(vp)]),
         "muon_plan_step": (i32, [vp, P(MuonConfig), vp, sz, vp]),
+        "muon_plan_step_noalloc": (i32, [vp, P(MuonConfig), vp]),
         "muon_plan_destroy": (None, [vp]),
         "muon_step": (i32, [P(MuonMatrix), i32, i32, P(MuonConfig), vp, sz, vp]),
         "muon_orthogonalize": (i32, [P(MuonMatrix), i32, i32, P(MuonConfig), vp, sz, vp]),
@@ -273,6 +276,13 @@ class MuonPlan:
                "muon_plan_step")
         return ws
 
+    def step_noalloc(self, cfg: MuonConfig, stream=None):
+        """muon_plan_step_noalloc: the same step with the library's fixed
+        device scratch array as workspace (no allocation)."""
+        _check(load_library().muon_plan_step_noalloc(self.handle, ctypes.byref(cfg),
+                                                     _stream_handle(stream)),
+               "muon_plan_step_noalloc")
+
     def set_weights(self, weights, lr_mul=None, wd_mul=None):
         """Attaches one weight tensor per matrix (same shape and dtype as its
         grad, row-major); lr_mul / wd_mul: per-matrix multipliers (default 1)."""
@@ -352,6 +362,10 @@ def muon_plan_set_weights(plan: MuonPlan, weights, lr_mul=None, wd_mul=None):
 def muon_plan_step_apply(plan: MuonPlan, cfg: MuonConfig, lr: float, wd: float, workspace=None,
                          stream=None):
     return plan.step_apply(cfg, lr, wd, workspace, stream)
+
+
+def muon_plan_step_noalloc(plan: MuonPlan, cfg: MuonConfig, stream=None):
+    return plan.step_noalloc(cfg, stream)
 
 
 def muon_plan_set_timing(plan: MuonPlan, on: bool):

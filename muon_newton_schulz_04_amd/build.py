@@ -35,7 +35,8 @@ def rocm_include() -> str:
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(os.path.dirname(PKG), 'include')}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = [("kernels.hip", True), ("adam.hip", True), ("api.cpp", False), ("plan.cpp", False)]
+SOURCES = [("kernels.hip", True), ("adam.hip", True), ("noalloc.hip", True), ("api.cpp", False),
+           ("plan.cpp", False)]
 
 
 def run(cmd):

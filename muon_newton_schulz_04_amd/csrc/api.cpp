@@ -40,6 +40,7 @@ struct muon_plan_s {
   double acc_ms[MUON_K_COUNT] = {};
   int64_t acc_n[MUON_K_COUNT] = {};
   bool has_weights = false;                   // muon_plan_set_weights succeeded
+  void* scratch = nullptr;                    // this device's fixed scratch array
 };
 
 namespace {
@@ -51,6 +52,12 @@ muon_status upload(muon_plan_s* p) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MUON_E_DEVICE;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_E_DEVICE;
   p->device = dev;
+  // set-up time: the device address of this GPU's scratch array (once per
+  // device) for muon_plan_step_noalloc
+  if (muon::scratch_address(&p->scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    p->scratch = nullptr;
+  }
   size_t bytes = sizeof(MatInfo) * std::max<size_t>(1, p->host.info.size());
   size_t offs[muon::kKinds], woffs[muon::kKinds];
   for (int k = 0; k < muon::kKinds; ++k) {
@@ -130,7 +137,8 @@ hipEvent_t get_event(muon_plan_s* p) {
 }
 
 muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t ws_bytes,
-                      void* stream, bool orthogonalize_only, const muon_apply* ap = nullptr) {
+                      void* stream, bool orthogonalize_only, const muon_apply* ap = nullptr,
+                      bool allow_timing = true) {
   if (p == nullptr) return MUON_E_INVALID;
   const HostPlan& H = p->host;
   muon_status st = muon::validate_config(cfg, H.dtype);
@@ -213,7 +221,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     return MUON_OK;
   };
 
-  if (p->timing) {
+  if (p->timing && allow_timing) {
     muon_status r;
     if ((r = timed(MUON_K_MOMENTUM)) != MUON_OK) return r;
     if ((r = timed(MUON_K_NORMALIZE)) != MUON_OK) return r;
@@ -327,6 +335,7 @@ const char* muon_status_str(int32_t s) {
     case MUON_E_DEVICE: return "no usable gfx950 device or HIP runtime error";
     case MUON_E_LAUNCH: return "kernel launch failed";
     case MUON_E_ALLOC: return "allocation failed";
+    case MUON_E_SCRATCH: return "set needs more workspace than the fixed scratch array holds";
     default: return "unknown status";
   }
 }
@@ -363,6 +372,13 @@ muon_status muon_plan_create(const muon_matrix* mats, int32_t n, muon_dtype dtyp
 muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* workspace,
                            size_t workspace_bytes, void* stream) {
   return step_impl(plan, cfg, workspace, workspace_bytes, stream, false);
+}
+
+muon_status muon_plan_step_noalloc(muon_plan* plan, const muon_config* cfg, void* stream) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  if (plan->host.ws_bytes > muon::kScratchBytes) return MUON_E_SCRATCH;
+  if (plan->host.ws_bytes > 0 && plan->scratch == nullptr) return MUON_E_DEVICE;
+  return step_impl(plan, cfg, plan->scratch, muon::kScratchBytes, stream, false, nullptr, false);
 }
 
 muon_status muon_plan_set_weights(muon_plan* plan, const muon_weight* w, int32_t n) {

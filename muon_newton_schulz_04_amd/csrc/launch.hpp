@@ -27,4 +27,8 @@ struct StepArgs {
 
 hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s);
 
+// Device address of the current device's fixed scratch array (kScratchBytes,
+// 256-byte aligned), looked up on the first call per device and kept.
+hipError_t scratch_address(void** out);
+
 }  // namespace muon

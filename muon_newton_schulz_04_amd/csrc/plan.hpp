@@ -20,6 +20,8 @@ constexpr int kMomentumElems = 16384;  // target elements per momentum work item
 constexpr int kNumXcd = 8;             // accelerator complex dies of an MI355X
 constexpr int kNumCu = 256;            // compute units of an MI355X
 constexpr size_t kWsAlign = 256;
+// Size of the fixed device scratch array of muon_plan_step_noalloc.
+constexpr size_t kScratchBytes = size_t(MUON_SCRATCH_BYTES);
 // Internal schedule after the public kernel kinds: the sums of split Gram
 // tiles (bf16 sets), launched as a second Gram pass.
 constexpr int kGramReduce = MUON_K_COUNT;

@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert mu.muon_abi_version() == 2
-    for code in range(9):
+    for code in range(10):
         s = mu.muon_status_str(code)
         assert s and s != "unknown status"
     assert mu.muon_status_str(99) == "unknown status"
