@@ -176,7 +176,7 @@ muon_status muon_plan_step_noalloc(muon_plan* plan, const muon_config* cfg, void
 
 /* Frees a plan after waiting for the device (NULL is a no-op). Plans own
  * only their descriptor tables and, for sets split into concurrent groups,
- * two streams and their events. */
+ * one stream and event per group (at most three). */
 void muon_plan_destroy(muon_plan* plan);
 
 /* One Muon update of `mats` (the whole optimizer step of the Muon path for

@@ -941,17 +941,18 @@ __device__ __forceinline__ uint32_t pk16(float x0, float x1, float s) {
 }
 
 // POLY: acc[i][J] += f A[m][n] at this lane's accumulator positions of
-// column block J, read from the row-operand half of the stage at `st`, which
-// holds A[m][k] for the 32 k that are these n (the caller picks the stage).
-template <int OP, int J>
-__device__ __forceinline__ void fold_bias(f32x16_t (&acc)[4][2], const char* st, int wm, float f) {
+// column block J (row blocks i < NR, rows rbase + 32 i ..), read from the
+// row-operand half of the stage at `st`, which holds A[m][k] for the 32 k
+// that are these n (the caller picks the stage).
+template <int OP, int J, int NR>
+__device__ __forceinline__ void fold_rows(f32x16_t (&acc)[4][2], const char* st, int rbase, float f) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NR; ++i) {
     u32x2 v[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      v[g] = *reinterpret_cast<const u32x2*>(st + off_r(wm * 128 + 32 * i + l32, g) + lh * 8);
+      v[g] = *reinterpret_cast<const u32x2*>(st + off_r(rbase + 32 * i + l32, g) + lh * 8);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t w[4] = {v[g].x & 0xffffu, v[g].x >> 16, v[g].y & 0xffffu, v[g].y >> 16};
@@ -962,8 +963,153 @@ __device__ __forceinline__ void fold_bias(f32x16_t (&acc)[4][2], const char* st,
   }
 }
 
+// Diagonal tiles (TI == TJ) of the symmetric products (Gram, poly). Of the
+// 8 x 8 grid of 32 x 32 blocks only the 36 on or above the diagonal are
+// needed, and the row and column operands are the same 256 rows, so a stage
+// carries the row operand only (16 KB, four 1 KB pieces per DMA wave) and
+// column fragments are read from it too. The 36 blocks are shared so that
+// each SIMD runs 9 (its two waves w and w + 4), against 16 on other tiles:
+//   waves 0..3   (strip)       block rows 0..3 of block column 4 + w (the
+//                              upper-right quadrant, 4 blocks each);
+//   waves 4, 6   (triangle A)  block columns 0 and 3 of the upper-left (4)
+//                              or lower-right (6) quadrant: 1 and 4 blocks;
+//   waves 5, 7   (triangle B)  its block columns 1 and 2: 2 and 3 blocks.
+// acc[i][j] holds block row i (rows rbase + 32 i ..) of block column j
+// (columns cb[j] ..), for i < nr[j].
+template <int ROLE> struct DiagRole;
+template <> struct DiagRole<0> { static constexpr int NJ = 1, NR0 = 4, NR1 = 0; };
+template <> struct DiagRole<1> { static constexpr int NJ = 2, NR0 = 1, NR1 = 4; };
+template <> struct DiagRole<2> { static constexpr int NJ = 2, NR0 = 2, NR1 = 3; };
+
+struct DiagGeo {
+  int rbase, cb0, cb1;  // first row, first column of block columns 0 and 1
+};
+__device__ __forceinline__ int diag_role(int wave) { return wave < 4 ? 0 : ((wave & 1) ? 2 : 1); }
+__device__ __forceinline__ DiagGeo diag_geo(int wave) {
+  if (wave < 4) return DiagGeo{0, 128 + 32 * wave, 128 + 32 * wave};
+  const int q = 128 * ((wave >> 1) & 1);  // waves 4, 5: upper-left; 6, 7: lower-right
+  return (wave & 1) ? DiagGeo{q, q + 32, q + 64} : DiagGeo{q, q, q + 96};
+}
+
+// A fragment of 32 rows (row0 ..) of k-step ks from the row-operand half.
+__device__ __forceinline__ u32x4 frag_rows(const char* st, int ks, int row0) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const u32x4*>(st + off_r(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+}
+
+// Half C (0/1) of a diagonal-tile k-step: its share of the role's MFMAs on
+// fragment set fm and of the LDS reads of fragment set fl (k-step ks of the
+// stage at `st`), interleaved.
+template <int OP, int ROLE, int C>
+__device__ __forceinline__ void kchunk_diag(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
+                                            const char* st, int ks, const DiagGeo& geo) {
+  using R = DiagRole<ROLE>;
+  constexpr int NM = R::NR0 + R::NR1;
+  constexpr int NA = R::NR0 > R::NR1 ? R::NR0 : R::NR1;
+  constexpr int NRD = R::NJ + NA;
+  constexpr int mb = C * NM / 2, me = (C + 1) * NM / 2;
+  constexpr int rb = C * NRD / 2, re = (C + 1) * NRD / 2;
+#pragma unroll
+  for (int t = mb; t < me; ++t) {
+    const int j = t < R::NR0 ? 0 : 1, i = t < R::NR0 ? t : t - R::NR0;
+    acc[i][j] = mfma<OP>(fm.b[j], fm.a[i], acc[i][j]);
+  }
+#pragma unroll
+  for (int t = rb; t < re; ++t) {
+    if (t < R::NJ) fl.b[t] = frag_rows(st, ks, t == 0 ? geo.cb0 : geo.cb1);
+    else fl.a[t - R::NJ] = frag_rows(st, ks, geo.rbase + 32 * (t - R::NJ));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < me - mb) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (k < re - rb) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+}
+template <int OP, int ROLE, typename D>
+__device__ __forceinline__ void kstep_diag(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
+                                           const char* st, int ks, const DiagGeo& geo, D&& dma) {
+  __builtin_amdgcn_sched_barrier(0);
+  dma(0);
+  kchunk_diag<OP, ROLE, 0>(acc, fm, fl, st, ks, geo);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(1);
+  kchunk_diag<OP, ROLE, 1>(acc, fm, fl, st, ks, geo);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
 #define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// The k loop of a diagonal tile for wave role ROLE: the ring of the other
+// tiles (same slots, same one barrier per stage, the stage's DMA split over
+// its two k-steps) carrying the row operand only (opA, panel stride lda).
+// FOLD (poly): block column j also adds f A at its accumulator positions
+// while stage fs[j] is resident (the stage holding its 32 columns as k).
+template <int OP, int ROLE, bool FOLD>
+__device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, const char* opA, int64_t lda,
+                                           int nst, bool dma_wave, const DiagGeo& geo, int fs0, int fs1,
+                                           float f) {
+  using R = DiagRole<ROLE>;
+  constexpr int DPS = 16 / DMA_WAVES;  // row-operand pieces per DMA wave per stage
+  constexpr int H = DPS / 2;           // pieces per k-step
+  static_assert(H == 2, "two chunks per k-step");
+#pragma unroll
+  for (int p = 0; p < NS - 2; ++p)
+#pragma unroll
+    for (int q = 0; q < DPS; ++q)
+      if (dma_wave) dma_piece<false>(lds + p * STAGE, opA, lda, opA, lda, int64_t(p) * KS, q);
+#pragma unroll
+  for (int q = 0; q < H; ++q)
+    if (dma_wave) dma_piece<false>(lds + (NS - 2) * STAGE, opA, lda, opA, lda, int64_t(NS - 2) * KS, q);
+  MUON_WAIT_VMCNT(DPS * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
+  asm volatile("s_barrier" ::: "memory");
+  constexpr int NA = R::NR0 > R::NR1 ? R::NR0 : R::NR1;
+  Frag f0, f1;
+  f0.b[0] = frag_rows(lds, 0, geo.cb0);
+  if constexpr (R::NJ == 2) f0.b[1] = frag_rows(lds, 0, geo.cb1);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) f0.a[i] = frag_rows(lds, 0, geo.rbase + 32 * i);
+  int cur = 0;
+  // one pass over stage g; J >= 0 also folds block column J (see the other
+  // tiles' loop: the fold passes are loops of their own)
+  auto pass = [&](int g, auto fold_j) {
+    constexpr int J = decltype(fold_j)::value;
+    const int nxt = cur == NS - 1 ? 0 : cur + 1;
+    const int old = cur == 0 ? NS - 1 : cur - 1;
+    {
+      const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
+      const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
+      kstep_diag<OP, ROLE>(acc, f0, f1, lds + cur * STAGE, 1, geo, [&](int c) {
+        if (dma_wave) dma_piece<false>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c);
+      });
+    }
+    MUON_WAIT_VMCNT(DPS * (NS - 3));
+    asm volatile("s_barrier" ::: "memory");
+    {
+      const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
+      kstep_diag<OP, ROLE>(acc, f1, f0, lds + nxt * STAGE, 0, geo, [&](int c) {
+        if (dma_wave) dma_piece<false>(lds + old * STAGE, opA, lda, opA, lda, k3, c);
+      });
+    }
+    if constexpr (J >= 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      fold_rows<OP, J, J == 0 ? R::NR0 : R::NR1>(acc, lds + cur * STAGE, geo.rbase, f);
+    }
+    cur = nxt;
+  };
+  using NoFold = std::integral_constant<int, -1>;
+  int g = 0;
+  if (FOLD && fs0 >= 0) {
+    for (; g < fs0; ++g) pass(g, NoFold{});
+    pass(g++, std::integral_constant<int, 0>{});
+    if constexpr (R::NJ == 2) {
+      for (; g < fs1; ++g) pass(g, NoFold{});
+      pass(g++, std::integral_constant<int, 1>{});
+    }
+  }
+  for (; g < nst; ++g) pass(g, NoFold{});
+  MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
+}
 
 
 
@@ -1049,7 +1195,40 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   // Every pass issues one stage, so the wait count is the same in every pass;
   // past the end the DMA repeats the last stage (valid addresses, unused).
   const bool fold = KIND == POLY && P.c != 0.f;
-  if (!reducing) {
+  // This wave's blocks: acc[i][j] is rows rbase + 32 i .. of the tile and
+  // columns cb0 .. (j = 0) or cb1 .. (j = 1), for i < nr0 / nr1. Diagonal
+  // tiles of the symmetric products share their 36 needed blocks out by
+  // role (kloop_diag); every other tile is wm, wn's 128 x 64.
+  int rbase = wm * 128, cb0 = wn * 64, cb1 = wn * 64 + 32, nr0 = 4, nr1 = 4;
+  bool diag = false;
+  if constexpr ((KIND == GRAM || KIND == POLY) && !SK) {
+    if (TI == TJ) {
+      diag = true;
+      const DiagGeo geo = diag_geo(wave);
+      const int role = diag_role(wave);
+      rbase = geo.rbase;
+      cb0 = geo.cb0;
+      cb1 = geo.cb1;
+      const int nst = static_cast<int>(K / KS);
+      // poly: block column j's 32 columns are the k of stage TJ * 8 + cb / 32
+      const int fs0 = TJ * (TN / KS) + cb0 / KS, fs1 = TJ * (TN / KS) + cb1 / KS;
+      // (without the fold, fs0 = fs1 = -1 never match a stage)
+      const float fb = fold ? P.b / P.c : 0.f;
+      const int f0s = fold ? fs0 : -1, f1s = fold ? fs1 : -1;
+      constexpr bool FOLD = KIND == POLY;
+      if (role == 0) {
+        nr0 = DiagRole<0>::NR0, nr1 = DiagRole<0>::NR1;
+        kloop_diag<OP, 0, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+      } else if (role == 1) {
+        nr0 = DiagRole<1>::NR0, nr1 = DiagRole<1>::NR1;
+        kloop_diag<OP, 1, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+      } else {
+        nr0 = DiagRole<2>::NR0, nr1 = DiagRole<2>::NR1;
+        kloop_diag<OP, 2, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+      }
+    }
+  }
+  if (!reducing && !diag) {
   const int nst = static_cast<int>(K / KS);
   constexpr int H = DMA_PER_STAGE / 2;  // pieces per k-step (the DMA of a stage is split over two)
   static_assert(DMA_PER_STAGE % 2 == 0 && 4 % H == 0, "DMA split");
@@ -1072,7 +1251,12 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   Frag f0, f1;
   frag_load<KN>(f0, lds, 0, wm, wn);
   int cur = 0;  // ring slot of stage g
-  for (int g = 0; g < nst; ++g) {
+  // One pass over stage g. Poly's b A term is folded into the accumulators
+  // of block column J in the pass over the stage that holds those columns
+  // as k; those two passes are loops of their own, so that no other pass
+  // carries the fold's branch.
+  auto pass = [&](int g, auto fold_j) {
+    constexpr int J = decltype(fold_j)::value;
     const int nxt = cur == NS - 1 ? 0 : cur + 1;  // slot of stage g+1
     const int old = cur == 0 ? NS - 1 : cur - 1;  // slot of stage g-1 (unused for g = 0)
     {
@@ -1100,15 +1284,23 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
         if (dma_wave) dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
       });
     }
-    if constexpr (KIND == POLY) {
+    if constexpr (J >= 0) {
       // (stage g stays in its slot until every wave has passed the next
       // barrier)
       __builtin_amdgcn_sched_barrier(0);
-      const int jb = g - bias0;
-      if (jb == 0) fold_bias<OP, 0>(acc, lds + cur * STAGE, wm, fb);
-      else if (jb == 1) fold_bias<OP, 1>(acc, lds + cur * STAGE, wm, fb);
+      fold_rows<OP, J, 4>(acc, lds + cur * STAGE, wm * 128, fb);
     }
     cur = nxt;
+  };
+  using NoFold = std::integral_constant<int, -1>;
+  if (fold) {
+    int g = 0;
+    for (; g < bias0; ++g) pass(g, NoFold{});
+    pass(g++, std::integral_constant<int, 0>{});
+    pass(g++, std::integral_constant<int, 1>{});
+    for (; g < nst; ++g) pass(g, NoFold{});
+  } else {
+    for (int g = 0; g < nst; ++g) pass(g, NoFold{});
   }
   MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
   }
@@ -1123,7 +1315,6 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   constexpr int ROWB = TN * 2;   // bytes per staged row
   constexpr int CPR = TN / 8;    // 16-byte chunks per staged row
   const int m0 = TI * TM, n0 = TJ * TN;  // tile origin
-  const int mb = m0 + wm * 128, nb = n0 + wn * 64;
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // every wave is done reading the operand stages
 
@@ -1162,14 +1353,16 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        if (i >= (j ? nr1 : nr0)) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int r = wm * 128 + 32 * i + l32, c = wn * 8 + 4 * j + g;
+          const int r = rbase + 32 * i + l32, c = (j ? cb1 : cb0) / 8 + g;
           *reinterpret_cast<uint2*>(lds + soff(r, c) + lh * 8) =
               e16::pack4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3], f16);
         }
+      }
   };
   // Visits the staged tile by rows: fn(m, n, 16 bytes of n..n+7).
   auto rows_out = [&](auto&& fn) {
@@ -1213,16 +1406,18 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j) {
+            if (i >= (j ? nr1 : nr0)) continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 float v = P.c * acc[i][j][4 * g + r];
-                const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh + r;
+                const int m = m0 + rbase + 32 * i + l32, n = n0 + (j ? cb1 : cb0) + 8 * g + 4 * lh + r;
                 if (m == n && m < M.m) v += P.a;  // padding stays zero
                 acc[i][j][4 * g + r] = v;
               }
+          }
         stage16(true);
       } else {
       // c = 0: the A tile goes into the staging layout by DMA (whole rows,
@@ -1246,14 +1441,16 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          if (i >= (j ? nr1 : nr0)) continue;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            char* sp = lds + soff(wm * 128 + 32 * i + l32, wn * 8 + 4 * j + g) + lh * 8;
+            const int cb = j ? cb1 : cb0;
+            char* sp = lds + soff(rbase + 32 * i + l32, cb / 8 + g) + lh * 8;
             const u32x2 bq = *reinterpret_cast<const u32x2*>(sp);
             const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
                                  Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
-            const int m = mb + 32 * i + l32, n = nb + 32 * j + 8 * g + 4 * lh;
+            const int m = m0 + rbase + 32 * i + l32, n = n0 + cb + 8 * g + 4 * lh;
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1262,6 +1459,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
             }
             *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], true);
           }
+        }
       }
     } else if (SK && reducing) {
       // one 128 x 128 quarter (qr, qc) of the tile: its 64 KB of each part's
@@ -1304,36 +1502,68 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       stage16(true);
     }
     __syncthreads();
-    // (the reduce pass of a split tile stores its quarter only)
-    auto in_quarter = [&](int m, int n) {
-      if constexpr (!SK) return true;
-      if (!reducing) return true;
-      return ((m - m0) >> 7) == (sp >> 1) && ((n - n0) >> 7) == (sp & 1);
-    };
-    // C[m][n..n+7] where m <= n
-    rows_out([&](int m, int n, const uint4& v) {
-      if (!in_quarter(m, n)) return;
-      uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(m, n, mp);
-      if (strict || m <= n) {
-        *reinterpret_cast<uint4*>(d) = v;
-      } else {
+    if (!strict && !(SK && reducing)) {
+      // Diagonal tile: only its upper triangle is staged (and only it is
+      // needed). The lower triangle is completed inside LDS from the upper
+      // one (so C stays bitwise symmetric): the 16 bytes at row n, columns
+      // m .. m+7 (m + 7 < n) are column n of rows m .. m+7, read transposed;
+      // a chunk that the diagonal crosses (m <= n <= m+7) takes its columns
+      // below n the same way and keeps the rest. Then every row goes out
+      // with whole 16-byte stores and no mirror pass is needed.
+      cols_out([&](int n, int m, const uint4& v) {
+        const int rn = n - n0, cm = m - m0;
+        if (cm >= rn) return;
+        uint4* d = reinterpret_cast<uint4*>(lds + soff(rn, cm >> 3));
+        if (cm + 7 < rn) {
+          *d = v;
+        } else {
+          const uint4 t = *d;
+          uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (m <= n + e) d[e] = static_cast<uint16_t>(half(v, e));
-      }
-    });
-    // mirror: C[n][m..m+7] = C[m..m+7][n] where m < n
-    cols_out([&](int n, int m, const uint4& v) {
-      if (!in_quarter(m, n)) return;
-      uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(n, m, mp);
-      if (strict || m + 7 < n) {
-        *reinterpret_cast<uint4*>(d) = v;
-      } else {
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = cm + 2 * q < rn ? half(v, 2 * q) : half(t, 2 * q);
+            const uint32_t hi = cm + 2 * q + 1 < rn ? half(v, 2 * q + 1) : half(t, 2 * q + 1);
+            w[q] = lo | (hi << 16);
+          }
+          *d = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      });
+      __syncthreads();
+      rows_out([&](int m, int n, const uint4& v) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + pidx(m, n, mp)) = v;
+      });
+    } else {
+      // (the reduce pass of a split tile stores its quarter only)
+      auto in_quarter = [&](int m, int n) {
+        if constexpr (!SK) return true;
+        if (!reducing) return true;
+        return ((m - m0) >> 7) == (sp >> 1) && ((n - n0) >> 7) == (sp & 1);
+      };
+      // C[m][n..n+7] where m <= n
+      rows_out([&](int m, int n, const uint4& v) {
+        if (!in_quarter(m, n)) return;
+        uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(m, n, mp);
+        if (strict || m <= n) {
+          *reinterpret_cast<uint4*>(d) = v;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (m + e < n) d[e] = static_cast<uint16_t>(half(v, e));
-      }
-    });
+          for (int e = 0; e < 8; ++e)
+            if (m <= n + e) d[e] = static_cast<uint16_t>(half(v, e));
+        }
+      });
+      // mirror: C[n][m..m+7] = C[m..m+7][n] where m < n
+      cols_out([&](int n, int m, const uint4& v) {
+        if (!in_quarter(m, n)) return;
+        uint16_t* d = reinterpret_cast<uint16_t*>(C) + pidx(n, m, mp);
+        if (strict || m + 7 < n) {
+          *reinterpret_cast<uint4*>(d) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (m + e < n) d[e] = static_cast<uint16_t>(half(v, e));
+        }
+      });
+    }
   } else {
     // UPDATE. The low bytes are read (and, unless this is the last step,
     // written back) in accumulator order, one 16-byte access per lane and

@@ -75,7 +75,7 @@ struct Schedule {
 // Large sets are split into groups of matrices that run concurrently on
 // streams of their own, so one group's kernels fill the CUs that the other
 // group's tail (the last, partial wave of tiles) and launch gaps leave idle.
-constexpr int kMaxGroups = 2;
+constexpr int kMaxGroups = 3;
 constexpr int kGroupMinTiles = 512;  // matrix-core tiles per update launch to split
 
 struct HostPlan {

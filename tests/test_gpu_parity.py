@@ -567,7 +567,7 @@ def test_max_elements_orthonormal_rows(tall):
 # ------------------------------------------------------------ HIP graphs
 
 def test_graph_capture_replays_match_eager():
-    """A whole step (the GPT-2-124M set: two groups of matrices forked onto
+    """A whole step (the GPT-2-124M set: groups of matrices forked onto
     their own streams and joined back) captured once as a HIP graph: three
     replays, with eager work and synchronisations in between, give bitwise
     the outputs and momentum buffers of three eager steps from the same
