@@ -21,9 +21,10 @@
  * significands at bf16's MFMA rate; every iterate is bounded by the
  * normalisation, so fp16's range suffices), and between steps X is kept as
  * its fp16 rounding hi plus one OCP e4m3 byte holding (X - hi) * 2^18
- * (about 15 significant bits together; the byte saturates at +-448, which
- * only an entry |X| >= 4 can reach). fp32 sets use fp32 operands and an
- * fp32 X throughout.
+ * (about 15 significant bits together). The byte's range (448) holds the
+ * residual of any entry below 4 in magnitude; validation of the
+ * coefficients (below) keeps every iterate's entries below 2. fp32 sets use
+ * fp32 operands and an fp32 X throughout.
  *
  * Conventions shared by every entry point:
  *  - Pointers in muon_matrix, `workspace` and `stream` are device-side

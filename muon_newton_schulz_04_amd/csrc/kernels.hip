@@ -85,26 +85,33 @@ template <> struct Op<OP_F16> {
   }
   // The X master of fp16-operand sets: X = hi + lo 2^-18 with hi = RN16(X)
   // and lo one byte, the OCP e4m3 rounding (to nearest even) of
-  // (X - hi) 2^18: 4 significant bits below hi's last one. |X - hi| <=
-  // ulp(hi) / 2 = 2^-11 for |X| < 2 keeps |lo| <= 2^7; larger residuals are
-  // clamped to the format's largest finite value, 448, first (the
-  // conversion would make them NaN).
+  // (X - hi) 2^18: 4 significant bits below hi's last one. Validation keeps
+  // every iterate's entries below 2 in magnitude (singular values of the
+  // accepted polynomials stay in [-2, 2]), so |X - hi| <= ulp(hi) / 2 <=
+  // 2^-10 and |lo| <= 2^8, inside the format's range (448).
   static constexpr float kLoScale = 262144.f;  // 2^18
   // the four lo bytes of residuals r0..r3 (x - hi, exact in fp32), byte q
-  // holding r_q
+  // holding r_q: gfx950's scaled conversion divides by its scale operand,
+  // so a scale of 2^-18 gives e4m3(r 2^18) in one instruction per pair
+  // (bitwise the separate multiply and conversion)
   static __device__ __forceinline__ uint32_t lo4(float r0, float r1, float r2, float r3) {
-    auto c = [](float r) { return fminf(fmaxf(r * kLoScale, -448.f), 448.f); };
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(r0), c(r1), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(c(r2), c(r3), w, true);
-    return static_cast<uint32_t>(w);
+    typedef short s2_t __attribute__((ext_vector_type(2)));
+    const s2_t z = {0, 0};
+    const s2_t a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, r0, r1, 1.f / kLoScale, false);
+    const s2_t b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, r2, r3, 1.f / kLoScale, true);
+    return __builtin_bit_cast(uint32_t, b);
   }
-  // the four lo bytes of w as floats (lo, not yet scaled by 2^-18)
+  // the four lo bytes of w as floats (lo, not yet scaled by 2^-18), two per
+  // conversion
   static __device__ __forceinline__ void lo_vals(uint32_t w, float (&v)[4]) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
     const int x = static_cast<int>(w);
-    v[0] = __builtin_amdgcn_cvt_f32_fp8(x, 0);
-    v[1] = __builtin_amdgcn_cvt_f32_fp8(x, 1);
-    v[2] = __builtin_amdgcn_cvt_f32_fp8(x, 2);
-    v[3] = __builtin_amdgcn_cvt_f32_fp8(x, 3);
+    const f2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+    const f2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = b.x;
+    v[3] = b.y;
   }
   static __device__ __forceinline__ uint16_t bits(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));  // RNE
@@ -907,11 +914,18 @@ __device__ __forceinline__ void kstep_dma(f32x16_t (&acc)[4][2], const Frag& fm,
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// RN16(x0) | RN16(x1) << 16: one v_cvt_pk_f16_f32 (round to nearest even)
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk16(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0, x1}, h2_t));
+}
+
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool f16) {
   uint2 r;
   if (f16) {
-    r.x = uint32_t(Op<OP_F16>::bits(a)) | (uint32_t(Op<OP_F16>::bits(b)) << 16);
-    r.y = uint32_t(Op<OP_F16>::bits(c)) | (uint32_t(Op<OP_F16>::bits(d)) << 16);
+    r.x = pk16(a, b);
+    r.y = pk16(c, d);
   } else {
     r.x = uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
     r.y = uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16);
@@ -919,11 +933,9 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d, bool 
   return r;
 }
 
-// Mixed-precision FMAs (v_fma_mix*) for the fp16 update epilogue: each one
-// rounds once, so hi = RN16(x) and the residual x - hi come out with no
-// separate conversions or packing. VALU-only asm (no memory access).
-//   sub_l / sub_h:  x - f16(low / high half of h), as fp32 (exact here)
-//   pk16:           RN16(x0 s) | RN16(x1 s) << 16
+// Mixed-precision FMAs (v_fma_mix_f32) for the fp16 update epilogue: the
+// residual x - f16(low / high half of h) in one rounding (exact here).
+// VALU-only asm (no memory access).
 __device__ __forceinline__ float sub_l(float x, uint32_t h) {
   float r;
   asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
@@ -932,11 +944,6 @@ __device__ __forceinline__ float sub_l(float x, uint32_t h) {
 __device__ __forceinline__ float sub_h(float x, uint32_t h) {
   float r;
   asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
-}
-__device__ __forceinline__ uint32_t pk16(float x0, float x1, float s) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, %3, 0\n\tv_fma_mixhi_f16 %0, %2, %3, 0" : "=&v"(r) : "v"(x0), "v"(x1), "v"(s));
   return r;
 }
 
@@ -1597,7 +1604,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
 #pragma unroll
               for (int q = 0; q < 2; ++q) {
                 const float v0 = acc[i][j][4 * g + 2 * q], v1 = acc[i][j][4 * g + 2 * q + 1];
-                hp[q] = e16::pk16(v0, v1, 1.f);
+                hp[q] = e16::pk16(v0, v1);
                 rs[2 * q] = e16::sub_l(v0, hp[q]);
                 rs[2 * q + 1] = e16::sub_h(v1, hp[q]);
               }

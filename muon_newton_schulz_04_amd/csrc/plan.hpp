@@ -43,8 +43,7 @@ struct MatInfo {
   int32_t tall;      // rows > cols: the iteration runs on the transpose
   int32_t vec_ok;    // 16-byte vector access legal for grad/mom/out
   int64_t xl_off;    // bf16 sets: low part of X, one OCP e4m3 byte per
-                     // element holding (X - hi) 2^18 (saturating at +-448,
-                     // reached only when |X| >= 4), -1 otherwise
+                     // element holding (X - hi) 2^18, -1 otherwise
   int64_t xo_off[2]; // bf16 sets: ping-pong high parts (the matrix-core
                      // operand); fp32 sets: ping-pong fp32 X
   int64_t a_off;     // A = X X^T
