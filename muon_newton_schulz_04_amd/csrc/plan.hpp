@@ -71,9 +71,11 @@ struct Schedule {
   std::vector<WorkItem> items;  // launch order; block i runs items[i]; mat < 0 = empty
 };
 
-// Large sets are split into groups of matrices that run concurrently on
-// streams of their own, so one group's kernels fill the CUs that the other
-// group's tail (the last, partial wave of tiles) and launch gaps leave idle.
+// Sets whose update launch is a few waves of tiles deep are split into
+// groups of matrices that run concurrently on streams of their own, so one
+// group's kernels fill the CUs that another group's tail (the last, partial
+// wave of tiles) and launch gaps leave idle: three groups below 8 waves of
+// 256 tiles, two below 24, one beyond (build_plan).
 constexpr int kMaxGroups = 3;
 constexpr int kGroupMinTiles = 512;  // matrix-core tiles per update launch to split
 
