@@ -45,25 +45,35 @@ def kernel_work(shapes, steps, dtype):
     Bytes count each operand read once and each result written once, in the
     library's formats: bf16 sets (fp16 operands) keep X as a 16-bit high part
     (the matrix-core operand) and a one-byte low part (the residual), and A, B
-    as 16-bit; fp32 sets keep everything in fp32. The Newton-Schulz kernels
-    run `steps` times; the last update writes `out` instead of X's parts."""
+    as 16-bit; fp32 sets keep everything in fp32. With at least one step,
+    bf16 sets write X0's operand in the momentum pass (no low part), the
+    normalise slot only reduces per-tile sums (no matrix bytes; its operand
+    rewrites, when the plan's guess of X0's power of two was wrong, are not
+    algorithmic work), and the first update reads no low part. The
+    Newton-Schulz kernels run `steps` times; the last update writes `out`
+    instead of X's parts."""
     es = 2 if dtype == "bf16" else 4
     xb = 3 if dtype == "bf16" else 4        # X per element: hi + lo byte, or fp32
     xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
+    fused = dtype == "bf16" and steps > 0
     w = {k: [0.0, 0.0] for k in ("momentum", "normalize", "gram", "poly", "update")}
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
         mn, mm = float(m * n), float(m * m)
-        w["momentum"][1] += 3 * es * mn          # read G, buf; write buf'
-        w["normalize"][1] += 2 * es * mn + xb * mn   # read G, buf'; write X
+        if fused:
+            w["momentum"][1] += 3 * es * mn + xop * mn   # read G, buf; write buf', X0 operand
+        else:
+            w["momentum"][1] += 3 * es * mn              # read G, buf; write buf'
+            w["normalize"][1] += 2 * es * mn + xb * mn   # read G, buf'; write X
         w["gram"][0] += steps * m * (m + 1) * n
         w["gram"][1] += steps * (xop * mn + es * mm)       # read X operand; write A
         w["poly"][0] += steps * m * m * (m + 1)
         w["poly"][1] += steps * 2 * es * mm                # read A; write B
         w["update"][0] += steps * 2 * m * m * n
-        reg = es * mm + xb * mn + xb * mn        # read B, X; write X
-        last = es * mm + xb * mn + es * mn       # read B, X; write out
-        w["update"][1] += reg * (steps - 1) + last if steps else 0.0
+        x_in = [xop if (fused and t == 0) else xb for t in range(steps)]   # X read by update t
+        for t in range(steps):
+            out = es if t == steps - 1 else xb                             # write out, or X
+            w["update"][1] += es * mm + x_in[t] * mn + out * mn
     return {k: (v[0], v[1]) for k, v in w.items()}
 
 
@@ -400,7 +410,7 @@ def main():
         step_s = tot_ms / args.steps * 1e-3
         flops, nbytes = work[name]
         ent = {"launches_per_step": n / args.steps, "us_per_step": step_s * 1e6,
-               "GB/s": nbytes / step_s / 1e9}
+               "GB/s": nbytes / step_s / 1e9 if nbytes else None}
         if flops:
             ent["TFLOP/s"] = flops / step_s / 1e12
         per_kernel[name] = ent

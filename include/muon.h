@@ -23,8 +23,15 @@
  * its fp16 rounding hi plus one OCP e4m3 byte holding (X - hi) * 2^18
  * (about 15 significant bits together). The byte's range (448) holds the
  * residual of any entry below 4 in magnitude; validation of the
- * coefficients (below) keeps every iterate's entries below 2. fp32 sets use
- * fp32 operands and an fp32 X throughout.
+ * coefficients (below) keeps every iterate's entries below 2. With at least
+ * one step, X0 of a bf16 set is held as sigma * fp16(u * p) instead (the
+ * momentum pass writes it before the norm is known): p is the power of two
+ * that puts the matrix's largest |u| in [2^12, 2^13), sigma = 1 / ((||u||
+ * + eps) p), and the first Gram and update multiply their fp32 sums by
+ * sigma^2 and sigma. A plan remembers each matrix's largest |u| to guess p;
+ * a guess that differs from this call's p costs one more pass over that
+ * matrix, never a different result. fp32 sets use fp32 operands and an fp32
+ * X throughout.
  *
  * Conventions shared by every entry point:
  *  - Pointers in muon_matrix, `workspace` and `stream` are device-side
@@ -52,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum {
@@ -176,8 +183,11 @@ muon_status muon_plan_step(muon_plan* plan, const muon_config* cfg, void* worksp
 muon_status muon_plan_step_noalloc(muon_plan* plan, const muon_config* cfg, void* stream);
 
 /* Frees a plan after waiting for the device (NULL is a no-op). Plans own
- * only their descriptor tables and, for sets split into concurrent groups,
- * one stream and event per group (at most three). */
+ * only their descriptor tables, one float per matrix (the largest |u| of
+ * the last call, the guess of X0's power of two: calls that overlap in time
+ * may race on it, which can cost a rewrite but never changes a result) and,
+ * for sets split into concurrent groups, one stream and event per group (at
+ * most three). */
 void muon_plan_destroy(muon_plan* plan);
 
 /* One Muon update of `mats` (the whole optimizer step of the Muon path for
@@ -251,10 +261,15 @@ muon_status muon_plan_step_apply(muon_plan* plan, const muon_config* cfg, const 
 /* ---- introspection (tests, benchmarks, profiling) ---------------------- */
 
 /* Kernels of one step, in launch order: momentum, normalise, then per
- * Newton-Schulz step gram, poly, update. */
+ * Newton-Schulz step gram, poly, update. bf16 sets with at least one step
+ * run, in the first two slots, the momentum step together with X0's
+ * operand fp16(u p) (schedule: the normalise tiles), then the scale pass
+ * (sigma and p per matrix; schedule kind MUON_K_COUNT + 1) and the rewrite
+ * of the operand of the matrices whose p the plan guessed wrong (over the
+ * normalise tiles again). */
 typedef enum {
-  MUON_K_MOMENTUM = 0, /* buf' and per-block sums of u^2            (HBM)  */
-  MUON_K_NORMALIZE = 1,/* X0 = u/(||u||+eps), fp32 master + operand (HBM)  */
+  MUON_K_MOMENTUM = 0, /* buf', sums of u^2 (bf16, k>0: + X0 operand) (HBM) */
+  MUON_K_NORMALIZE = 1,/* X0 = u/(||u||+eps) (bf16, k>0: scale pass) (HBM) */
   MUON_K_GRAM = 2,     /* A = X X^T, upper-triangle tiles mirrored (MFMA) */
   MUON_K_POLY = 3,     /* B = b A + c A A, upper tiles mirrored    (MFMA) */
   MUON_K_UPDATE = 4,   /* X = a X + B X (last step writes out)     (MFMA) */
@@ -276,7 +291,9 @@ typedef enum {
  * writing an fp32 partial tile to the workspace, and kind == MUON_K_COUNT
  * queries the second Gram pass that sums them, four items {matrix, tile
  * row, tile col, pbase << 16 | q << 8 | S} per split tile, one per 128 x 128
- * quarter q (empty when nothing splits).
+ * quarter q (empty when nothing splits). kind == MUON_K_COUNT + 1 queries
+ * the scale pass of bf16 sets: one item {matrix, 0, 0, 0} per matrix
+ * (empty for fp32 sets).
  * Writes min(cap, count) items to `items` (may be NULL when cap == 0) and
  * the total to *count. No device calls. */
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,
@@ -309,10 +326,16 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
  * is at element index ((c / 32) * mp + r) * 32 + c % 32. poly holds
  * a I + B (the a X term of the high part rides in the product). fp32 sets:
  * x_op0/x_op1 are fp32 X (ping-pong), gram/poly (B) fp32, all row-major,
- * x_lo = -1. After a step of k iterations X is in x_op[k % 2]. */
+ * x_lo = -1. After a step of k iterations X is in x_op[k % 2].
+ * x0_scale (bf16 sets): four floats {sigma, p, p guessed, 1 if the
+ * operand was rewritten because the guess was wrong, else 0}; after a call
+ * with k >= 1 and until the first update has run, x_op0 holds X0's
+ * operand fp16(u p) and X0 = sigma * x_op0 (x_lo not used for X0). -1 for
+ * fp32 sets. */
 typedef struct {
   int64_t m, n, mp, np;
   int64_t x_lo, x_op0, x_op1, gram, poly;
+  int64_t x0_scale;
 } muon_buffer_info;
 
 muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffer_info* info);

@@ -75,7 +75,7 @@ class MuonAdamConfig(ctypes.Structure):
 
 class MuonBufferInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("m", "n", "mp", "np", "x_lo", "x_op0", "x_op1", "gram", "poly")]
+                ("m", "n", "mp", "np", "x_lo", "x_op0", "x_op1", "gram", "poly", "x0_scale")]
 
 
 _lib = None

@@ -29,6 +29,7 @@ struct muon_plan_s {
   const MatInfo* d_mats = nullptr;
   const WorkItem* d_items[muon::kKinds] = {};
   const WorkItem* d_whole[muon::kKinds] = {};  // one-group schedules (timing)
+  float* d_hint = nullptr;                    // per matrix: largest |u| of the last call (0: none)
   // groups > 1: one stream per group (default priority) and the events that
   // fork them from, and join them back to, the caller's stream
   hipStream_t gstream[muon::kMaxGroups] = {};
@@ -68,6 +69,9 @@ muon_status upload(muon_plan_s* p) {
     woffs[k] = bytes;
     bytes += sizeof(WorkItem) * std::max<size_t>(1, p->host.whole[k].items.size());
   }
+  bytes = (bytes + 255) / 256 * 256;
+  const size_t hint_off = bytes;
+  bytes += sizeof(float) * std::max<size_t>(1, p->host.info.size());
   std::vector<char> h(bytes, 0);
   if (!p->host.info.empty())
     std::memcpy(h.data(), p->host.info.data(), sizeof(MatInfo) * p->host.info.size());
@@ -105,6 +109,7 @@ muon_status upload(muon_plan_s* p) {
     p->d_items[k] = reinterpret_cast<const WorkItem*>(base + offs[k]);
     p->d_whole[k] = reinterpret_cast<const WorkItem*>(base + woffs[k]);
   }
+  p->d_hint = reinterpret_cast<float*>(base + hint_off);
   return MUON_OK;
 }
 
@@ -167,47 +172,79 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.use_mom = use_mom ? 1 : 0;
   a.direct = cfg->steps == 0 ? 1 : 0;
   a.split_off = H.split_off;
+  // bf16 sets with at least one step: the momentum pass also stores X0's
+  // operand (scaled by a power of two), the normalise slot runs the scale
+  // pass, and the first Gram and update apply the scale
+  const bool fused = H.dtype == MUON_BF16 && cfg->steps > 0 && H.x0s_off >= 0;
+  a.tsum_off = H.tsum_off;
+  a.tmax_off = H.tmax_off;
+  a.x0s_off = H.x0s_off;
+  a.hint = p->d_hint;
   if (ap) {
     a.apply = 1;
     a.lr = ap->lr;
     a.wd = ap->wd;
   }
 
-  // Schedule `kind` (a muon_kernel_kind, or the sums of split Gram tiles,
-  // which run as a second pass of the Gram kernel) -> kernel and flag.
-  auto kernel_of = [](int kind) { return kind == muon::kGramReduce ? int(MUON_K_GRAM) : kind; };
-  // One launch of kernel `kind` for group g on stream `q`.
-  auto launch = [&](int kind, int g, hipStream_t q) -> muon_status {
-    const int32_t b = H.gbeg[g][kind], e = H.gbeg[g + 1][kind];
-    if (e == b) return MUON_OK;
-    a.items = p->d_items[kind] + b;
-    a.reduce = kind == muon::kGramReduce ? 1 : 0;
-    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, a, e - b, q);
-    a.reduce = 0;
-    return r == hipSuccess ? MUON_OK : MUON_E_LAUNCH;
+  // Step slot `kind` (a muon_kernel_kind, or the sums of split Gram tiles,
+  // which run as a second pass of the Gram kernel) -> its kernels (one, or
+  // two in a row), the schedule each runs, and the kind its time is
+  // reported under.
+  struct Slot {
+    int report, n;
+    int kernel[2], sched[2];
   };
-  // Per-kernel timing: kernel `kind` over the whole set in one launch on
-  // the caller's stream (the one-group schedule), bracketed by HIP events.
+  auto slot_of = [fused](int kind) -> Slot {
+    if (kind == muon::kGramReduce) return {MUON_K_GRAM, 1, {MUON_K_GRAM, 0}, {kind, 0}};
+    if (fused && kind == MUON_K_MOMENTUM)
+      return {MUON_K_MOMENTUM, 1, {muon::kKernelMomentumX0, 0}, {MUON_K_NORMALIZE, 0}};
+    if (fused && kind == MUON_K_NORMALIZE)
+      return {MUON_K_NORMALIZE, 2, {muon::kKernelX0Scale, muon::kKernelX0Rewrite},
+              {muon::kX0Scale, MUON_K_NORMALIZE}};
+    return {kind, 1, {kind, 0}, {kind, 0}};
+  };
+  // Kernel `kernel` over `count` items from `items` on stream `q`.
+  auto run = [&](int kind, int kernel, const WorkItem* items, int32_t count, hipStream_t q) -> hipError_t {
+    a.items = items;
+    a.n_items = count;
+    a.reduce = kind == muon::kGramReduce ? 1 : 0;
+    const hipError_t r = muon::launch_kernel(kernel, H.dtype, a, count, q);
+    a.reduce = 0;
+    return r;
+  };
+  // The launches of step slot `kind` for group g on stream `q`.
+  auto launch = [&](int kind, int g, hipStream_t q) -> muon_status {
+    const Slot o = slot_of(kind);
+    for (int k = 0; k < o.n; ++k) {
+      const int32_t b = H.gbeg[g][o.sched[k]], e = H.gbeg[g + 1][o.sched[k]];
+      if (e == b) continue;
+      if (run(kind, o.kernel[k], p->d_items[o.sched[k]] + b, e - b, q) != hipSuccess) return MUON_E_LAUNCH;
+    }
+    return MUON_OK;
+  };
+  // Per-kernel timing: step slot `kind` over the whole set (the one-group
+  // schedules) on the caller's stream, bracketed by HIP events.
   auto timed = [&](int kind) -> muon_status {
-    const int grid = static_cast<int>(H.whole[kind].items.size());
-    if (grid == 0) return MUON_OK;
-    TimedLaunch t{kernel_of(kind), get_event(p), get_event(p)};
+    const Slot o = slot_of(kind);
+    if (H.whole[o.sched[0]].items.empty()) return MUON_OK;
+    TimedLaunch t{o.report, get_event(p), get_event(p)};
     auto give_back = [&]() {
       if (t.start) p->free_events.push_back(t.start);
       if (t.stop) p->free_events.push_back(t.stop);
       return MUON_E_LAUNCH;
     };
     if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return give_back();
-    a.items = p->d_whole[kind];
-    a.reduce = kind == muon::kGramReduce ? 1 : 0;
-    const hipError_t r = muon::launch_kernel(kernel_of(kind), H.dtype, a, grid, s);
-    a.reduce = 0;
+    hipError_t r = hipSuccess;
+    for (int k = 0; k < o.n && r == hipSuccess; ++k) {
+      const auto& w = H.whole[o.sched[k]].items;
+      if (!w.empty()) r = run(kind, o.kernel[k], p->d_whole[o.sched[k]], static_cast<int32_t>(w.size()), s);
+    }
     if (r != hipSuccess || hipEventRecord(t.stop, s) != hipSuccess) return give_back();
     p->pending.push_back(t);
     return MUON_OK;
   };
-  // The whole sequence of one group on stream q: momentum, normalise,
-  // k x (gram, poly, update).
+  // The whole sequence of one group on stream q: momentum, normalise (or
+  // the scale pass), k x (gram, poly, update).
   auto sequence = [&](int g, hipStream_t q) -> muon_status {
     muon_status r;
     if ((r = launch(MUON_K_MOMENTUM, g, q)) != MUON_OK) return r;
@@ -215,6 +252,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     for (int t = 0; t < cfg->steps; ++t) {
       a.cur = t & 1;
       a.last = t == cfg->steps - 1 ? 1 : 0;
+      a.x0_scaled = fused && t == 0 ? 1 : 0;
       for (int kind : {int(MUON_K_GRAM), muon::kGramReduce, int(MUON_K_POLY), int(MUON_K_UPDATE)})
         if ((r = launch(kind, g, q)) != MUON_OK) return r;
     }
@@ -228,6 +266,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     for (int t = 0; t < cfg->steps; ++t) {
       a.cur = t & 1;
       a.last = t == cfg->steps - 1 ? 1 : 0;
+      a.x0_scaled = fused && t == 0 ? 1 : 0;
       for (int kind : {int(MUON_K_GRAM), muon::kGramReduce, int(MUON_K_POLY), int(MUON_K_UPDATE)})
         if ((r = timed(kind)) != MUON_OK) return r;
     }
@@ -435,7 +474,7 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
 
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype, int32_t kind,
                                 int32_t* items, int64_t cap, int64_t* count) {
-  if (count == nullptr || kind < 0 || kind > MUON_K_COUNT || cap < 0 ||
+  if (count == nullptr || kind < 0 || kind > MUON_K_COUNT + 1 || cap < 0 ||
       (cap > 0 && items == nullptr))
     return MUON_E_INVALID;
   HostPlan P;
@@ -493,6 +532,7 @@ muon_status muon_plan_buffer_info(const muon_plan* plan, int32_t idx, muon_buffe
   info->x_op1 = I.xo_off[1];
   info->gram = I.a_off;
   info->poly = I.b_off;
+  info->x0_scale = I.m > 0 && plan->host.x0s_off >= 0 ? plan->host.x0s_off + 16 * int64_t(idx) : -1;
   return MUON_OK;
 }
 

@@ -450,6 +450,205 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   }
 }
 
+// ------------------------------------------ X0's operand of bf16 sets
+//
+// With at least one Newton-Schulz step, bf16 sets do not store X0 = u /
+// (||u|| + eps) itself (the norm is known only after a pass over u): the
+// momentum pass stores the fp16 rounding of u p, p a power of two, and the
+// first Gram and update scale their fp32 sums by sigma^2 and sigma, sigma
+// = 1 / ((||u|| + eps) p). p puts the matrix's largest |u| in [2^12, 2^13):
+// fp16's range holds it, and entries down to 2^-26 of the largest stay
+// normal fp16 numbers. The momentum pass takes p from the previous call's
+// largest |u| (a hint the plan keeps); the scale pass compares it with the
+// p of this call's largest |u| and rewrites the operand of the matrices
+// where the two differ, so the operand depends on this call's inputs only.
+
+// 2^k with mx 2^k in [2^12, 2^13) (k clamped to normal floats); 1 when mx
+// is zero, NaN or infinite.
+__device__ __forceinline__ float x0_pow2(float mx) {
+  if (!(mx > 0.f) || !(mx <= 3.40282347e38f)) return 1.f;
+  const int e = static_cast<int>((__float_as_uint(mx) >> 23) & 255u) - 127;
+  const int k = min(max(12 - e, -126), 126);
+  return __uint_as_float(static_cast<uint32_t>(k + 127) << 23);
+}
+
+// max that keeps a NaN once seen
+__device__ __forceinline__ float nan_max(float m, float v) { return (v > m || v != v) ? v : m; }
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = nan_max(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  return nan_max(nan_max(red[0], red[1]), nan_max(red[2], red[3]));
+}
+
+// u of one 64 x 64 tile of X0's orientation, read from the caller's layout
+// (caller rows cr0.., columns cc0..; transposed for tall matrices): thread t
+// holds two runs of 8 consecutive caller columns, run h at caller row
+// (t + 256 h) / 8 of the tile and columns 8 (t % 8) ... Zero outside the
+// matrix. STEP: the momentum step happens here (buf' written back);
+// otherwise u is formed from the stored buf'.
+template <bool STEP>
+__device__ __forceinline__ void tile_u_bf16(const StepArgs& A, const MatInfo& M, int32_t cr0, int32_t cc0,
+                                            float (&u)[2][8]) {
+  const uint16_t* g = static_cast<const uint16_t*>(M.grad);
+  uint16_t* mb = static_cast<uint16_t*>(M.mom);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int32_t cr = cr0 + (v >> 3), cc = cc0 + (v & 7) * 8;
+    const int64_t off = int64_t(cr) * M.ld + cc;
+    if (cr < M.rows && M.vec_ok && cc + 8 <= M.cols) {
+      const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(g + off);
+      u32x4_t bw = {0u, 0u, 0u, 0u};
+      if (A.use_mom) bw = *reinterpret_cast<const u32x4_t*>(mb + off);
+      u32x4_t nw = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gf = bf2f(static_cast<uint16_t>(gw[e >> 1] >> (16 * (e & 1))));
+        float nb = bf2f(static_cast<uint16_t>(bw[e >> 1] >> (16 * (e & 1))));
+        if (STEP && A.use_mom) {
+          nb = momentum_new<uint16_t>(A.mu, nb, gf);
+          nw[e >> 1] |= uint32_t(f2bf(nb)) << (16 * (e & 1));
+        }
+        u[h][e] = form_u(gf, nb, A);
+      }
+      if (STEP && A.use_mom) *reinterpret_cast<u32x4_t*>(mb + off) = nw;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = 0.f;
+        if (cr < M.rows && cc + e < M.cols) {
+          const float gf = bf2f(g[off + e]);
+          float nb = A.use_mom ? bf2f(mb[off + e]) : 0.f;
+          if (STEP && A.use_mom) {
+            nb = momentum_new<uint16_t>(A.mu, nb, gf);
+            mb[off + e] = f2bf(nb);
+          }
+          x = form_u(gf, nb, A);
+        }
+        u[h][e] = x;
+      }
+    }
+  }
+}
+
+// fp16(u p) of the tile at rows i0.., columns j0.. of X0's orientation into
+// the first operand buffer (panels); tall tiles are transposed through LDS.
+__device__ __forceinline__ void tile_store_x0(const StepArgs& A, const MatInfo& M, int32_t i0, int32_t j0,
+                                              float (&u)[2][8], float p, float (*tile)[65]) {
+  if (M.tall) {
+    __syncthreads();  // an earlier tile's reads of `tile` are done
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[(v & 7) * 8 + e][v >> 3] = u[h][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[h][e] = tile[v >> 3][(v & 7) * 8 + e];
+    }
+  }
+  uint16_t* x = reinterpret_cast<uint16_t*>(A.ws + M.xo_off[0]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    u32x4_t w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = uint32_t(Op<OP_F16>::bits(u[h][2 * q] * p)) | (uint32_t(Op<OP_F16>::bits(u[h][2 * q + 1] * p)) << 16);
+    *reinterpret_cast<u32x4_t*>(x + pidx(i0 + (v >> 3), j0 + (v & 7) * 8, M.mp)) = w;
+  }
+}
+
+// Momentum step and X0's operand in one pass. Item {mat, ti, tj}: one 64 x
+// 64 tile of mp x np (X0's orientation; tiles in the padding store zeros).
+// Per tile: the sum of u^2 (each thread's 16 terms in order, then the
+// block's fixed tree) and the largest |u|.
+__global__ __launch_bounds__(256) void momentum_x0_kernel(StepArgs A) {
+  const WorkItem it = A.items[blockIdx.x];
+  if (it.mat < 0) return;
+  const MatInfo& M = A.mats[it.mat];
+  __shared__ float red[4];
+  __shared__ float tile[64][65];
+  const int32_t i0 = it.a * 64, j0 = it.b * 64;
+  float u[2][8];
+  tile_u_bf16<true>(A, M, M.tall ? j0 : i0, M.tall ? i0 : j0, u);
+  float ss = 0.f, mx = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ss = __fmaf_rn(u[h][e], u[h][e], ss);
+      mx = nan_max(mx, fabsf(u[h][e]));
+    }
+  ss = block_sum_256(ss, red);
+  mx = block_max_256(mx, red);
+  const float p = x0_pow2(A.hint[it.mat]);
+  if (threadIdx.x == 0) {
+    const int32_t slot = M.tile_off + it.a * (M.np / 64) + it.b;
+    reinterpret_cast<float*>(A.ws + A.tsum_off)[slot] = ss;
+    reinterpret_cast<float*>(A.ws + A.tmax_off)[slot] = mx;
+    if (it.a == 0 && it.b == 0) reinterpret_cast<float*>(A.ws + A.x0s_off)[4 * it.mat + 2] = p;
+  }
+  tile_store_x0(A, M, i0, j0, u, p, tile);
+}
+
+// Scale pass. Item {mat}: one workgroup per matrix sums its tile sums
+// (fixed order) and takes the largest |u|, then stores {sigma, p, p of the
+// momentum pass, rewrite flag} and the new hint. The flag is set where the
+// momentum pass's p differs from this one.
+__global__ __launch_bounds__(256) void x0_scale_kernel(StepArgs A) {
+  const WorkItem it = A.items[blockIdx.x];
+  if (it.mat < 0) return;
+  const MatInfo& M = A.mats[it.mat];
+  __shared__ float red[4];
+  const float* ts = reinterpret_cast<const float*>(A.ws + A.tsum_off) + M.tile_off;
+  const float* tm = reinterpret_cast<const float*>(A.ws + A.tmax_off) + M.tile_off;
+  float s = 0.f, mx = 0.f;
+  for (int32_t q = threadIdx.x; q < M.tile_cnt; q += 256) {
+    s += ts[q];
+    mx = nan_max(mx, tm[q]);
+  }
+  s = block_sum_256(s, red);
+  mx = block_max_256(mx, red);
+  if (threadIdx.x == 0) {
+    const float scale = 1.0f / (sqrtf(s) + A.eps);
+    const float p = x0_pow2(mx);
+    float* xs = reinterpret_cast<float*>(A.ws + A.x0s_off) + 4 * it.mat;
+    xs[0] = scale / p;  // exact (p is a power of two) unless it underflows
+    xs[1] = p;
+    xs[3] = xs[2] == p ? 0.f : 1.f;
+    if (mx > 0.f && mx <= 3.40282347e38f) A.hint[it.mat] = mx;
+  }
+}
+
+// Operand rewrite: the tiles of the matrices whose flag is set, u again
+// from G and the stored buf'. Runs over the momentum pass's tile schedule
+// with a smaller grid, block b taking items b, b + grid, ... (grid a
+// multiple of 8, so each item stays on the XCD the schedule placed it on);
+// where no flag is set it only reads the items and flags.
+__global__ __launch_bounds__(256) void x0_rewrite_kernel(StepArgs A) {
+  __shared__ float tile[64][65];
+  const float* x0s = reinterpret_cast<const float*>(A.ws + A.x0s_off);
+  for (int32_t q = blockIdx.x; q < A.n_items; q += gridDim.x) {
+    const WorkItem it = A.items[q];
+    if (it.mat < 0 || x0s[4 * it.mat + 3] == 0.f) continue;
+    const MatInfo& M = A.mats[it.mat];
+    const int32_t i0 = it.a * 64, j0 = it.b * 64;
+    if (i0 >= M.m || j0 >= M.n) continue;  // padding: zeros already
+    float u[2][8];
+    tile_u_bf16<false>(A, M, M.tall ? j0 : i0, M.tall ? i0 : j0, u);
+    tile_store_x0(A, M, i0, j0, u, x0s[4 * it.mat + 1], tile);
+  }
+}
+
 // ------------------------------------------------------ matrix-core engine
 
 enum GemmKind { GRAM = 0, POLY = 1, UPDATE = 2 };
@@ -1127,7 +1326,7 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
 // (n, m). UPDATE: X = a X + B X on all tiles.
 // SK (Gram only): the variant that also runs split tiles and the reduce
 // pass, launched for plans that split Gram tiles.
-template <typename T, int OP, int KIND, bool LAST, bool SK = false>
+template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false>
 __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   using namespace e16;
   const WorkItem it = P.items[blockIdx.x];
@@ -1474,6 +1673,12 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       // part order by all threads, 16 bytes (4 floats of one lane and block)
       // at a time, into the staged tile
       const int qr = sp >> 1, qc = sp & 1;
+      // the first step's Gram: A0 = sigma^2 (sum of the operand's products)
+      float gsc = 1.f;
+      if (P.x0_scaled) {
+        const float sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
+        gsc = sg * sg;
+      }
       const char* qbase = P.ws + P.split_off + int64_t(pbase) * (TM * TN * 4) + (qr * 4 + 2 * qc) * 32768;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1502,10 +1707,21 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
           const int r = qr * 128 + 32 * (blk >> 1) + (ln & 31);
           const int c = (2 * qc + wl) * 8 + 4 * (blk & 1) + v;
           *reinterpret_cast<uint2*>(lds + soff(r, c) + (ln >> 5) * 8) =
-              e16::pack4(sum[u][0], sum[u][1], sum[u][2], sum[u][3], true);
+              e16::pack4(sum[u][0] * gsc, sum[u][1] * gsc, sum[u][2] * gsc, sum[u][3] * gsc, true);
         }
       }
     } else {
+      if (P.x0_scaled) {
+        // the first step's Gram: A0 = sigma^2 (sum of the operand's products)
+        const float sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
+        const float s2 = sg * sg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] *= s2;
+      }
       stage16(true);
     }
     __syncthreads();
@@ -1579,10 +1795,23 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       char* lo_t = P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) + lane * 16;
       auto lo_ptr = [&](int i, int j) { return lo_t + (((wm * 4 + i) * WN + wn) * 2 + j) * 1024; };
       u32x4 lq[4][2];
+      // The first step (X0S, a kernel of its own so that the other steps'
+      // register allocation is untouched) starts from X0 = sigma * operand
+      // with no low bytes: X1 = sigma (B' operand).
+      if constexpr (!X0S) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) lq[i][j] = *reinterpret_cast<const u32x4*>(lo_ptr(i, j));
+          for (int j = 0; j < 2; ++j) lq[i][j] = *reinterpret_cast<const u32x4*>(lo_ptr(i, j));
+      } else {
+        const float sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] *= sg;
+      }
       // X' = B' hi + a 2^-18 lo  (B' = a I + B carries a hi)
       const float as = P.a * (1.f / Op<OP>::kLoScale);
 #pragma unroll
@@ -1592,10 +1821,12 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
           uint32_t qw[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            float lv[4];
-            Op<OP>::lo_vals(lq[i][j][g], lv);
+            if constexpr (!X0S) {
+              float lv[4];
+              Op<OP>::lo_vals(lq[i][j][g], lv);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][4 * g + r] = __fmaf_rn(as, lv[r], acc[i][j][4 * g + r]);
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * g + r] = __fmaf_rn(as, lv[r], acc[i][j][4 * g + r]);
+            }
             if constexpr (!LAST) {
               // split back into hi (staged straight into the LDS tile, the
               // ring is free) and the low bytes; x - hi is exact (sub_l/h)
@@ -1688,11 +1919,23 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
 template <typename T, int OP>
 static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  const bool engine16 = OP != OP_F32 && kind >= MUON_K_GRAM;
+  const bool engine16 = OP != OP_F32 && (kind == MUON_K_GRAM || kind == MUON_K_POLY || kind == MUON_K_UPDATE);
   dim3 g(grid), b(engine16 ? e16::NTHR : 256);
   switch (kind) {
     case MUON_K_MOMENTUM: hipLaunchKernelGGL(momentum_kernel<T>, g, b, 0, s, a); break;
     case MUON_K_NORMALIZE: hipLaunchKernelGGL((normalize_kernel<T, OP>), g, b, 0, s, a); break;
+    case kKernelMomentumX0:
+      if constexpr (OP == OP_F32) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL(momentum_x0_kernel, g, b, 0, s, a);
+      break;
+    case kKernelX0Scale:
+      if constexpr (OP == OP_F32) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL(x0_scale_kernel, g, b, 0, s, a);
+      break;
+    case kKernelX0Rewrite:
+      if constexpr (OP == OP_F32) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL(x0_rewrite_kernel, dim3(grid < kX0RewriteGrid ? grid : kX0RewriteGrid), b, 0, s, a);
+      break;
     case MUON_K_GRAM:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, GRAM>), g, b, 0, s, a);
       else if (a.split_off >= 0) hipLaunchKernelGGL((gemm16_kernel<T, OP, GRAM, false, true>), g, b, 0, s, a);
@@ -1704,6 +1947,8 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
       break;
     case MUON_K_UPDATE:
       if constexpr (OP == OP_F32) hipLaunchKernelGGL((gemm32_kernel<T, OP, UPDATE>), g, b, 0, s, a);
+      else if (a.x0_scaled && a.last) hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, true, false, true>), g, b, 0, s, a);
+      else if (a.x0_scaled) hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, false, false, true>), g, b, 0, s, a);
       else if (a.last) hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, true>), g, b, 0, s, a);
       else hipLaunchKernelGGL((gemm16_kernel<T, OP, UPDATE, false>), g, b, 0, s, a);
       break;

@@ -23,6 +23,13 @@ struct StepArgs {
   float lr, wd;
   int32_t reduce;   // Gram: sum split partial tiles and store A (second pass)
   int64_t split_off;  // workspace offset of the split Gram partials (-1: none)
+  // bf16 sets with at least one step: X0 = sigma * (its fp16 operand),
+  // which holds u scaled by a power of two p; the first Gram scales its sums
+  // by sigma^2 and the first update by sigma (x0_scaled).
+  int32_t x0_scaled;
+  int64_t tsum_off, tmax_off, x0s_off;  // workspace offsets (see HostPlan)
+  float* hint;  // plan memory, per matrix: the largest |u| of the last call (0: none)
+  int32_t n_items;  // items of the schedule (kernels whose grid is smaller)
 };
 
 hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s);

@@ -294,6 +294,11 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     I.part_off = nparts;
     I.part_cnt = static_cast<int32_t>((M.rows + rows_per_item - 1) / rows_per_item);
     nparts += I.part_cnt;
+    if (bf16) {
+      I.tile_off = P.total_tiles;
+      I.tile_cnt = (I.mp / kNormTile) * (I.np / kNormTile);
+      P.total_tiles += I.tile_cnt;
+    }
   }
   P.total_partials = nparts;
   size_t off = round_up(static_cast<int64_t>(nparts) * 4, kWsAlign);
@@ -302,6 +307,11 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     off = round_up(static_cast<int64_t>(off + bytes), kWsAlign);
     return o;
   };
+  if (bf16 && P.total_tiles > 0) {
+    P.tsum_off = take(static_cast<size_t>(P.total_tiles) * 4);
+    P.tmax_off = take(static_cast<size_t>(P.total_tiles) * 4);
+    P.x0s_off = take(static_cast<size_t>(n) * 16);
+  }
   for (int32_t i = 0; i < n; ++i) {
     MatInfo& I = P.info[i];
     if (I.m == 0) continue;
@@ -344,6 +354,11 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
         per[MUON_K_NORMALIZE][i].push_back({i, ti, tj, 0});
         cost[MUON_K_NORMALIZE][i].push_back(1.0);
       }
+    // scale pass: one workgroup per matrix
+    if (bf16) {
+      per[kX0Scale][i].push_back({i, 0, 0, 0});
+      cost[kX0Scale][i].push_back(double(I.tile_cnt));
+    }
     // Tiles of tm x tn; gram/poly keep the tiles that reach the upper
     // triangle (first row <= last column: tj * tn + tn - 1 >= ti * tm).
     const int32_t tm = bf16 ? kTileM16 : kGemmTile, tn = bf16 ? kTileN16 : kGemmTile;
@@ -477,7 +492,8 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
         add_matrix_chunks(chunks, i, per[k][i], cost[k][i], max_cost);
     return assign_xcd(std::move(chunks));
   };
-  for (int k = 0; k < MUON_K_COUNT; ++k) {
+  for (int k : {int(MUON_K_MOMENTUM), int(MUON_K_NORMALIZE), int(MUON_K_GRAM), int(MUON_K_POLY),
+                int(MUON_K_UPDATE), kX0Scale}) {
     P.sched[k].items.clear();
     for (int g = 0; g < P.ngroups; ++g) {
       P.gbeg[g][k] = static_cast<int32_t>(P.sched[k].items.size());

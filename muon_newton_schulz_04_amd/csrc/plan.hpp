@@ -22,10 +22,22 @@ constexpr int kNumCu = 256;            // compute units of an MI355X
 constexpr size_t kWsAlign = 256;
 // Size of the fixed device scratch array of muon_plan_step_noalloc.
 constexpr size_t kScratchBytes = size_t(MUON_SCRATCH_BYTES);
-// Internal schedule after the public kernel kinds: the sums of split Gram
-// tiles (bf16 sets), launched as a second Gram pass.
+// Internal schedules after the public kernel kinds: the sums of split Gram
+// tiles (bf16 sets), launched as a second Gram pass, and the scale pass of
+// X0 (bf16 sets with at least one step: one item per matrix).
 constexpr int kGramReduce = MUON_K_COUNT;
-constexpr int kKinds = MUON_K_COUNT + 1;
+constexpr int kX0Scale = MUON_K_COUNT + 1;
+constexpr int kKinds = MUON_K_COUNT + 2;
+// Kernels beyond the public kinds (launch_kernel): bf16 sets with at least
+// one step run the momentum step and X0's operand in one pass over the
+// normalise tiles, then the scale pass (normalisation scale and power of
+// two per matrix) and the operand rewrite of the matrices whose power of
+// two the momentum pass guessed wrong (over the normalise tiles with a grid
+// of at most kX0RewriteGrid).
+constexpr int kKernelMomentumX0 = 16;
+constexpr int kKernelX0Scale = 17;
+constexpr int kKernelX0Rewrite = 18;
+constexpr int kX0RewriteGrid = 2048;
 // Split Gram tiles: k ranges of at least 8 stages of 32; each partial is a
 // 256 x TN fp32 tile in the workspace.
 constexpr int32_t kSplitMaxParts = 32767;
@@ -50,6 +62,8 @@ struct MatInfo {
   int64_t b_off;     // B = b A + c A A
   int32_t part_off;  // first slot of this matrix's sum-of-squares partials
   int32_t part_cnt;
+  int32_t tile_off;  // bf16 sets: first slot of this matrix's per-tile sums
+  int32_t tile_cnt;  // and maxima (64 x 64 tiles of mp x np, row-major)
   // Weight application (muon_plan_step_apply): W in the caller's dtype and
   // orientation, row-major with leading dimension wld; lr and wd multipliers.
   void* w;
@@ -92,6 +106,11 @@ struct HostPlan {
   // whole set in one launch).
   Schedule whole[kKinds];
   int32_t total_partials = 0;
+  // bf16 sets: per normalise tile, the sum of u^2 and the largest |u|
+  // (momentum pass), and per matrix four floats {sigma, p, p of the
+  // momentum pass, 0} (scale pass): X0 = sigma * (fp16 operand).
+  int32_t total_tiles = 0;
+  int64_t tsum_off = -1, tmax_off = -1, x0s_off = -1;
   // Split Gram tiles (small bf16 sets whose longest Gram tiles would set
   // the launch time): partial tiles in the workspace at split_off.
   int32_t split_parts = 0;

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert mu.muon_abi_version() == 2
+    assert mu.muon_abi_version() == 3
     for code in range(10):
         s = mu.muon_status_str(code)
         assert s and s != "unknown status"
@@ -141,6 +141,15 @@ def expected_ws(shapes, dtype):
         rpi = max(1, 16384 // c)
         parts += (r + rpi - 1) // rpi
     off = ru(parts * 4, 256)
+    if dtype == mu.MUON_BF16:
+        # per 64 x 64 tile of each padded matrix: sum of u^2 and largest |u|;
+        # per matrix: {sigma, p, p guessed, 0}
+        tiles = sum(ru(min(r, c), 256) // 64 * (ru(max(r, c), 256) // 64)
+                    for r, c in shapes if r and c)
+        if tiles:
+            off = ru(off + tiles * 4, 256)
+            off = ru(off + tiles * 4, 256)
+            off = ru(off + len(shapes) * 16, 256)
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
         t = 256 if dtype == mu.MUON_BF16 else 128
@@ -212,12 +221,13 @@ def test_schedules_of_random_sets(lib):
 
 def check_schedules(shapes, dtype):
     tm = tn = 256 if dtype == mu.MUON_BF16 else 128
-    scheds = [mu.muon_schedule_query(shapes, dtype, k) for k in range(5)]
+    scheds = [mu.muon_schedule_query(shapes, dtype, k) for k in (0, 1, 2, 3, 4, 6)]
     for k, s in enumerate(scheds):
         assert len(s) % 8 == 0, "grid is a multiple of the XCD count"
         empty = s[:, 0] < 0
         assert np.all(s[empty] == -1)
-    mom, nrm, gram, poly, upd = (s[s[:, 0] >= 0] for s in scheds)
+    mom, nrm, gram, poly, upd, scale = (s[s[:, 0] >= 0] if len(s) else np.zeros((0, 4), int)
+                                        for s in scheds)
     slots = mom[:, 3]
     assert len(np.unique(slots)) == len(slots) and slots.min() == 0 and slots.max() == len(slots) - 1
     for i, (r, c) in enumerate(shapes):
@@ -258,9 +268,6 @@ def check_schedules(shapes, dtype):
             assert sorted((c >> 8) & 255 for c in cs) == list(range(S))
             assert len({c >> 16 for c in cs}) == 1 and red[t] == ((cs[0] >> 16) << 16 | S)
         assert set(red) <= set(tiles)
-    if dtype == mu.MUON_BF16:
-        spans = sorted({(c >> 16, (c >> 16) + (c & 255)) for *_, c in split_reduce_items(shapes)})
-        assert all(e0 <= b1 for (_, e0), (b1, _) in zip(spans, spans[1:]))   # disjoint partial slots
         for s in (gram, poly):
             si = s[s[:, 0] == i]
             cover = np.zeros((mp, mp), int)
@@ -273,6 +280,15 @@ def check_schedules(shapes, dtype):
         assert sorted(map(tuple, pi[:, 1:3])) == want_tri
         ui = upd[upd[:, 0] == i]
         assert sorted(map(tuple, ui[:, 1:3])) == [(a, b) for a in range(mp // tm) for b in range(np_ // tn)]
+        # scale pass (bf16): one item {i, 0, 0, 0} per matrix
+        si = scale[scale[:, 0] == i]
+        if dtype == mu.MUON_BF16 and m > 0:
+            assert si.tolist() == [[i, 0, 0, 0]]
+        else:
+            assert len(si) == 0
+    if dtype == mu.MUON_BF16:
+        spans = sorted({(c >> 16, (c >> 16) + (c & 255)) for *_, c in split_reduce_items(shapes)})
+        assert all(e0 <= b1 for (_, e0), (b1, _) in zip(spans, spans[1:]))   # disjoint partial slots
 
 
 def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):

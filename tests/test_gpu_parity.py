@@ -231,35 +231,119 @@ def lo_byte_index(mp, np_):
             + ((nn // 8) % 4) * 4 + nn % 4)
 
 
-def test_x0_master_parts():
-    """After a one-step call the workspace still holds X0 (the last update
-    reads it and writes `out`): its fp16 high part (panels) plus its e4m3
-    low byte times 2^-18 must give the oracle's X0 = u / (||u|| + eps) to
-    the format's precision, |error| <= ulp16(x) / 32 <= 2^-15 |x| (the e4m3
-    rounding, 4 significant bits, of a residual of at most half an ulp)."""
+def x0_record(ws, info):
+    """{sigma, p, p guessed, rewrite flag} of a matrix (x0_scale)."""
+    off = info["x0_scale"]
+    return ws[off: off + 16].view(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def test_x0_operand_and_scale():
+    """After a one-step call the workspace still holds X0's operand (the
+    momentum pass writes it, the last update only reads it): x_op0 =
+    fp16(u p) with p the power of two that puts max |u| in [2^12, 2^13), and
+    sigma * x_op0 is the oracle's X0 = u / (||u|| + eps) to fp16's rounding,
+    |error| <= 2^-11 |x| (half an ulp; the fp32 norm adds about 2^-20) plus
+    half of fp16's subnormal spacing 2^-24, times sigma. A fresh plan has no
+    guess of p (guessed 1); the second call on the same set guesses right."""
     shapes = [(200, 333), (333, 200), (256, 512), (40, 700)]
     grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=9, shapes=shapes)]
     outs = [torch.empty_like(g) for g in grads]
     plan = mu.MuonPlan(grads, None, outs)
-    ws = plan.step(mu.make_config(*QUINTIC, 1))
+    for call in range(2):
+        ws = plan.step(mu.make_config(*QUINTIC, 1))
+        torch.cuda.synchronize()
+        for i, g in enumerate(grads):
+            info = plan.buffer_info(i)
+            m, n, mp, np_ = info["m"], info["n"], info["mp"], info["np"]
+            x0 = oracle.frobenius_normalize(to_f64(g), 1e-7)
+            if g.shape[0] > g.shape[1]:
+                x0 = x0.T
+            want = np.zeros((mp, np_))
+            want[:m, :n] = x0
+            sigma, p, guess, flag = x0_record(ws, info)
+            frac, _ = np.frexp(p)
+            assert frac == 0.5, "p is a power of two"
+            assert guess == (1.0 if call == 0 else p)
+            assert flag == (1.0 if guess != p else 0.0)
+            off = info["x_op0"]
+            hi = unpanel(ws[off: off + mp * np_ * 2].view(torch.float16), mp, np_).double().cpu().numpy()
+            top = np.abs(hi).max()
+            assert 2.0 ** 12 * (1 - 2.0 ** -11) <= top <= 2.0 ** 13, top
+            got = sigma * hi
+            bound = (2.0 ** -11 + 2.0 ** -19) * np.abs(want) + sigma * 2.0 ** -24
+            err = np.abs(got - want)
+            assert np.all(err <= bound), (i, float(np.max(err / bound)))
+            assert not np.any(hi[m:, :]) and not np.any(hi[:, n:])   # padding stays zero
+    plan.destroy()
+
+
+def test_x1_low_bytes_are_residuals():
+    """After a two-step call, X1 is in x_op1 (fp16 hi) and x_lo (e4m3 bytes
+    in the update's accumulator order): every byte, read through that
+    layout, must be the rounded residual of its own element, |lo 2^-18| <=
+    (1 + 2^-3) ulp16(hi) / 2 (plus e4m3's smallest step, 2^-27), with most
+    bytes nonzero, zero padding, and hi + lo 2^-18 within the bf16 bar of the
+    oracle's X1."""
+    shapes = [(200, 333), (333, 200), (256, 512)]
+    grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=4, shapes=shapes)]
+    outs = [torch.empty_like(g) for g in grads]
+    plan = mu.MuonPlan(grads, None, outs)
+    ws = plan.step(mu.make_config(*QUINTIC, 2))
     torch.cuda.synchronize()
+    a, b, c = (f32(x) for x in QUINTIC)
     for i, g in enumerate(grads):
         info = plan.buffer_info(i)
         m, n, mp, np_ = info["m"], info["n"], info["mp"], info["np"]
         x0 = oracle.frobenius_normalize(to_f64(g), 1e-7)
-        if g.shape[0] > g.shape[1]:
-            x0 = x0.T
-        want = np.zeros((mp, np_))
-        want[:m, :n] = x0
-        off = info["x_op0"]
+        x1 = oracle.newton_schulz(x0.T if g.shape[0] > g.shape[1] else x0, a, b, c, 1)
+        off = info["x_op1"]
         hi = unpanel(ws[off: off + mp * np_ * 2].view(torch.float16), mp, np_).double().cpu().numpy()
         lob = ws[info["x_lo"]: info["x_lo"] + mp * np_].cpu().numpy()[lo_byte_index(mp, np_)]
         lo = torch.from_numpy(np.ascontiguousarray(lob)).view(torch.float8_e4m3fn).double().numpy()
-        got = hi + lo * 2.0 ** -18
-        bound = 1.1 * 2.0 ** -15 * np.abs(want) + 2.0 ** -26
-        err = np.abs(got - want)
-        assert np.all(err <= bound), (i, float(np.max(err / (bound))))
-        assert not np.any(got[m:, :]) and not np.any(got[:, n:])   # padding stays zero
+        r = lo * 2.0 ** -18
+        ah = np.abs(hi)
+        ulp = np.where(ah >= 2.0 ** -14, 2.0 ** (np.floor(np.log2(np.maximum(ah, 2.0 ** -14))) - 10),
+                       2.0 ** -24)
+        assert np.all(np.abs(r) <= (1 + 2.0 ** -3) * ulp / 2 + 2.0 ** -27)
+        assert np.count_nonzero(lo[:m, :n]) > 0.5 * m * n
+        assert not np.any(hi[m:, :]) and not np.any(hi[:, n:])
+        assert not np.any(lo[m:, :]) and not np.any(lo[:, n:])
+        assert rel((hi + r)[:m, :n], x1) < TOL["bf16"]
+    plan.destroy()
+
+
+def test_x0_guess_never_changes_results():
+    """X0's power of two is guessed from the plan's previous call and
+    corrected by the scale pass: a plan that has seen other gradient scales
+    (smaller by 2^-20, where every guess is wrong and the operand is
+    rewritten, larger by 3, the same again, far larger) gives bitwise the
+    outputs and momentum buffers of a fresh plan on each call's inputs."""
+    shapes = [(200, 333), (333, 200), (64, 1100), (520, 96)]
+    base = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=21, shapes=shapes)]
+    grads = [g.clone() for g in base]
+    bufs = [torch.zeros_like(g) for g in grads]
+    outs = [torch.empty_like(g) for g in grads]
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True)
+    plan = mu.MuonPlan(grads, bufs, outs)
+    for call, f in enumerate((1.0, 2.0 ** -20, 3.0, 3.0, 1e4)):
+        say(f"x0 guess: call {call}, gradient scale {f}")
+        for g, b0 in zip(grads, base):
+            g.copy_((b0.float() * f).to(torch.bfloat16))
+        bufs_fresh = [b.clone() for b in bufs]
+        ws = plan.step(cfg)
+        torch.cuda.synchronize()
+        rec = [x0_record(ws, plan.buffer_info(i)) for i in range(len(shapes))]
+        if call == 1:
+            assert all(r[1] != r[2] and r[3] == 1 for r in rec), "a scale 2^-20 away: every guess is wrong"
+        got_o = [o.clone() for o in outs]
+        got_b = [b.clone() for b in bufs]
+        outs_fresh = [torch.empty_like(g) for g in grads]
+        fresh = mu.MuonPlan(grads, bufs_fresh, outs_fresh)
+        fresh.step(cfg)
+        torch.cuda.synchronize()
+        fresh.destroy()
+        for a, b in zip(got_o + got_b, outs_fresh + bufs_fresh):
+            assert torch.equal(a, b)
     plan.destroy()
 
 
