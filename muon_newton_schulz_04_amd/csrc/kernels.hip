@@ -1020,6 +1020,18 @@ __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda
     dma16(opB + (g >> 2) * ldb + (k0 + kr) * 64 + (g & 3) * 16, dst);
   }
 }
+// The same piece q of a stage-sized (32 KB) contiguous block at src: stage
+// byte offset (q < 4 ? 0 : 16 KB) + 1 KB (w + 4 (q % 4)) for DMA wave w,
+// the offset it also has at src (the update's low bytes of X, prefetched
+// through the ring in the k loop's last passes).
+__device__ __forceinline__ void dma_block_piece(char* st, const char* src, int q) {
+  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+  constexpr int QA = 16 / DMA_WAVES;
+  const int off = (q < QA ? 0 : HALF_A) + (w + DMA_WAVES * (q < QA ? q : q - QA)) * 1024;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + off);
+  dma16(src + off + i * 16, dst);
+}
+static_assert(HALF_A == 16384 && STAGE == 32768, "the low-byte prefetch fills whole stages");
 template <bool KN>
 __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0) {
@@ -1245,6 +1257,9 @@ __device__ __forceinline__ void kstep_diag(f32x16_t (&acc)[4][2], const Frag& fm
 
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
 #define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+// s_waitcnt lgkmcnt(0) only (LDS and scalar memory; vector memory may stay
+// in flight).
+#define MUON_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // The k loop of a diagonal tile for wave role ROLE: the ring of the other
 // tiles (same slots, same one barrier per stage, the stage's DMA split over
@@ -1457,12 +1472,20 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   Frag f0, f1;
   frag_load<KN>(f0, lds, 0, wm, wn);
   int cur = 0;  // ring slot of stage g
+  // The update's low bytes of X (64 KB per tile, contiguous) take the place
+  // of stages nst and nst+1 (slots nst % NS and (nst+1) % NS), which
+  // otherwise repeat the last stage: the epilogue reads them from LDS.
+  constexpr bool LO_DMA = KIND == UPDATE && !X0S;
+  const char* lo_src = LO_DMA ? P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) : nullptr;
   // One pass over stage g. Poly's b A term is folded into the accumulators
   // of block column J in the pass over the stage that holds those columns
   // as k; those two passes are loops of their own, so that no other pass
-  // carries the fold's branch.
-  auto pass = [&](int g, auto fold_j) {
+  // carries the fold's branch. TAIL (the update's last three passes, 1 .. 3
+  // for g = nst-3 .. nst-1): the DMA of stages nst and nst+1 fetches the low
+  // bytes, and the last pass issues no repeat (nothing waits for it).
+  auto pass = [&](int g, auto fold_j, auto tail) {
     constexpr int J = decltype(fold_j)::value;
+    constexpr int TAIL = decltype(tail)::value;
     const int nxt = cur == NS - 1 ? 0 : cur + 1;  // slot of stage g+1
     const int old = cur == 0 ? NS - 1 : cur - 1;  // slot of stage g-1 (unused for g = 0)
     {
@@ -1471,7 +1494,11 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, [&](int c) {
-        if (dma_wave) dma_piece<KN>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
+        if constexpr (TAIL >= 2) {  // stage nst or nst+1: low bytes, second half
+          if (dma_wave) dma_block_piece(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c);
+        } else {
+          if (dma_wave) dma_piece<KN>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
+        }
       });
     }
     // This wave's pieces of stage g+1 have landed (stages up to g+NS-2 may
@@ -1487,7 +1514,11 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
     {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, [&](int c) {
-        if (dma_wave) dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
+        if constexpr (TAIL == 1 || TAIL == 2) {  // stage nst or nst+1: low bytes, first half
+          if (dma_wave) dma_block_piece(lds + old * STAGE, lo_src + (TAIL - 1) * STAGE, c);
+        } else if constexpr (TAIL == 0) {
+          if (dma_wave) dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
+        }
       });
     }
     if constexpr (J >= 0) {
@@ -1499,14 +1530,21 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
     cur = nxt;
   };
   using NoFold = std::integral_constant<int, -1>;
+  using T0 = std::integral_constant<int, 0>;
   if (fold) {
     int g = 0;
-    for (; g < bias0; ++g) pass(g, NoFold{});
-    pass(g++, std::integral_constant<int, 0>{});
-    pass(g++, std::integral_constant<int, 1>{});
-    for (; g < nst; ++g) pass(g, NoFold{});
+    for (; g < bias0; ++g) pass(g, NoFold{}, T0{});
+    pass(g++, std::integral_constant<int, 0>{}, T0{});
+    pass(g++, std::integral_constant<int, 1>{}, T0{});
+    for (; g < nst; ++g) pass(g, NoFold{}, T0{});
+  } else if constexpr (LO_DMA) {
+    int g = 0;
+    for (; g < nst - 3; ++g) pass(g, NoFold{}, T0{});
+    pass(g++, NoFold{}, std::integral_constant<int, 1>{});
+    pass(g++, NoFold{}, std::integral_constant<int, 2>{});
+    pass(g++, NoFold{}, std::integral_constant<int, 3>{});
   } else {
-    for (int g = 0; g < nst; ++g) pass(g, NoFold{});
+    for (int g = 0; g < nst; ++g) pass(g, NoFold{}, T0{});
   }
   MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
   }
@@ -1799,10 +1837,21 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       // register allocation is untouched) starts from X0 = sigma * operand
       // with no low bytes: X1 = sigma (B' operand).
       if constexpr (!X0S) {
+        // the low bytes arrived with the k loop's last passes: block bi
+        // (1 KB, 16 bytes per lane) is at offset (bi % 32) KB of ring slot
+        // (nst + bi / 32) % NS; every wave reads its blocks before any wave
+        // stages its result over the ring
+        const int nst = static_cast<int>(K / KS);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) lq[i][j] = *reinterpret_cast<const u32x4*>(lo_ptr(i, j));
+          for (int j = 0; j < 2; ++j) {
+            const int bi = ((wm * 4 + i) * WN + wn) * 2 + j;
+            lq[i][j] = *reinterpret_cast<const u32x4*>(lds + ((nst + (bi >> 5)) % NS) * STAGE + (bi & 31) * 1024 +
+                                                       lane * 16);
+          }
+        MUON_WAIT_LGKMCNT0();
+        asm volatile("s_barrier" ::: "memory");
       } else {
         const float sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
 #pragma unroll
@@ -1847,7 +1896,11 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
           if constexpr (!LAST) *reinterpret_cast<u32x4*>(lo_ptr(i, j)) = u32x4{qw[0], qw[1], qw[2], qw[3]};
         }
       if constexpr (!LAST) {
-        __syncthreads();
+        // the staged hi tile is complete once every wave's LDS writes are;
+        // a bare barrier, so the low-byte stores above stay in flight (the
+        // workgroup fence of __syncthreads would wait for them)
+        MUON_WAIT_LGKMCNT0();
+        asm volatile("s_barrier" ::: "memory");
         uint16_t* xn = reinterpret_cast<uint16_t*>(P.ws + M.xo_nxt);
         rows_out([&](int m, int n, const uint4& v) {
           *reinterpret_cast<uint4*>(xn + pidx(m, n, M.mp)) = v;
