@@ -46,12 +46,11 @@ def kernel_work(shapes, steps, dtype):
     library's formats: bf16 sets (fp16 operands) keep X as a 16-bit high part
     (the matrix-core operand) and a one-byte low part (the residual), and A, B
     as 16-bit; fp32 sets keep everything in fp32. With at least one step,
-    bf16 sets write X0's operand in the momentum pass (no low part), the
-    normalise slot only reduces per-tile sums (no matrix bytes; its operand
-    rewrites, when the plan's guess of X0's power of two was wrong, are not
-    algorithmic work), and the first update reads no low part. The
-    Newton-Schulz kernels run `steps` times; the last update writes `out`
-    instead of X's parts."""
+    bf16 sets write X0 (scaled by a power of two: high part and low byte) in
+    the momentum pass, and the normalise slot only reduces per-tile sums (no
+    matrix bytes; its rewrites, when the plan's guess of X0's power of two
+    was wrong, are not algorithmic work). The Newton-Schulz kernels run
+    `steps` times; the last update writes `out` instead of X's parts."""
     es = 2 if dtype == "bf16" else 4
     xb = 3 if dtype == "bf16" else 4        # X per element: hi + lo byte, or fp32
     xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
@@ -61,7 +60,7 @@ def kernel_work(shapes, steps, dtype):
         m, n = min(r, c), max(r, c)
         mn, mm = float(m * n), float(m * m)
         if fused:
-            w["momentum"][1] += 3 * es * mn + xop * mn   # read G, buf; write buf', X0 operand
+            w["momentum"][1] += 3 * es * mn + xb * mn    # read G, buf; write buf', X0
         else:
             w["momentum"][1] += 3 * es * mn              # read G, buf; write buf'
             w["normalize"][1] += 2 * es * mn + xb * mn   # read G, buf'; write X
@@ -70,10 +69,9 @@ def kernel_work(shapes, steps, dtype):
         w["poly"][0] += steps * m * m * (m + 1)
         w["poly"][1] += steps * 2 * es * mm                # read A; write B
         w["update"][0] += steps * 2 * m * m * n
-        x_in = [xop if (fused and t == 0) else xb for t in range(steps)]   # X read by update t
         for t in range(steps):
             out = es if t == steps - 1 else xb                             # write out, or X
-            w["update"][1] += es * mm + x_in[t] * mn + out * mn
+            w["update"][1] += es * mm + xb * mn + out * mn                 # read B, X
     return {k: (v[0], v[1]) for k, v in w.items()}
 
 

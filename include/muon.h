@@ -24,14 +24,15 @@
  * (about 15 significant bits together). The byte's range (448) holds the
  * residual of any entry below 4 in magnitude; validation of the
  * coefficients (below) keeps every iterate's entries below 2. With at least
- * one step, X0 of a bf16 set is held as sigma * fp16(u * p) instead (the
- * momentum pass writes it before the norm is known): p is the power of two
- * that puts the matrix's largest |u| in [2^12, 2^13), sigma = 1 / ((||u||
- * + eps) p), and the first Gram and update multiply their fp32 sums by
- * sigma^2 and sigma. A plan remembers each matrix's largest |u| to guess p;
- * a guess that differs from this call's p costs one more pass over that
- * matrix, never a different result. fp32 sets use fp32 operands and an fp32
- * X throughout.
+ * one step, X0 of a bf16 set is held as sigma * U instead (the momentum pass
+ * writes it before the norm is known): U = u p is kept as its fp16
+ * rounding hi plus one e4m3 byte holding (U - hi) * 2^5, p is the power of
+ * two that puts the matrix's largest |u| in [2^12, 2^13), sigma = 1 /
+ * ((||u|| + eps) p), and the first Gram and update multiply their fp32 sums
+ * by sigma^2 and sigma. A plan remembers each matrix's largest |u| to guess
+ * p; a guess that differs from this call's p costs one more pass over that
+ * matrix, never a different result. fp32 sets use fp32 operands and an
+ * fp32 X throughout.
  *
  * Conventions shared by every entry point:
  *  - Pointers in muon_matrix, `workspace` and `stream` are device-side
@@ -329,9 +330,9 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
  * x_lo = -1. After a step of k iterations X is in x_op[k % 2].
  * x0_scale (bf16 sets): four floats {sigma, p, p guessed, 1 if the
  * operand was rewritten because the guess was wrong, else 0}; after a call
- * with k >= 1 and until the first update has run, x_op0 holds X0's
- * operand fp16(u p) and X0 = sigma * x_op0 (x_lo not used for X0). -1 for
- * fp32 sets. */
+ * with k >= 1 and until the first update has run, x_op0 and x_lo hold X0
+ * as X0 = sigma * (hi + byte * 2^-5) (same layouts, the byte's scale
+ * relative to U = u p). -1 for fp32 sets. */
 typedef struct {
   int64_t m, n, mp, np;
   int64_t x_lo, x_op0, x_op1, gram, poly;

@@ -454,14 +454,19 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
 //
 // With at least one Newton-Schulz step, bf16 sets do not store X0 = u /
 // (||u|| + eps) itself (the norm is known only after a pass over u): the
-// momentum pass stores the fp16 rounding of u p, p a power of two, and the
-// first Gram and update scale their fp32 sums by sigma^2 and sigma, sigma
-// = 1 / ((||u|| + eps) p). p puts the matrix's largest |u| in [2^12, 2^13):
-// fp16's range holds it, and entries down to 2^-26 of the largest stay
-// normal fp16 numbers. The momentum pass takes p from the previous call's
-// largest |u| (a hint the plan keeps); the scale pass compares it with the
-// p of this call's largest |u| and rewrites the operand of the matrices
-// where the two differ, so the operand depends on this call's inputs only.
+// momentum pass stores U = u p, p a power of two, as its fp16 rounding hi
+// (the matrix-core operand) and one e4m3 byte holding (U - hi) 2^5, and
+// the first Gram and update scale their fp32 sums by sigma^2 and sigma,
+// sigma = 1 / ((||u|| + eps) p). p puts the matrix's largest |u| in
+// [2^12, 2^13): fp16's range holds it, entries down to 2^-26 of the largest
+// stay normal fp16 numbers, and |U - hi| <= 2 keeps the byte below 64. The
+// momentum pass takes p from the previous call's largest |u| (a hint the
+// plan keeps); the scale pass compares it with the p of this call's largest
+// |u| and the operand and bytes of the matrices where the two differ are
+// written again, so they depend on this call's inputs only. The byte
+// matters: the polynomial amplifies X0's rounding noise in the directions
+// of small singular values by up to a^k, which an fp16 X0 alone leaves far
+// above the bf16 tolerance for low-rank inputs.
 
 // 2^k with mx 2^k in [2^12, 2^13) (k clamped to normal floats); 1 when mx
 // is zero, NaN or infinite.
@@ -535,8 +540,11 @@ __device__ __forceinline__ void tile_u_bf16(const StepArgs& A, const MatInfo& M,
   }
 }
 
-// fp16(u p) of the tile at rows i0.., columns j0.. of X0's orientation into
-// the first operand buffer (panels); tall tiles are transposed through LDS.
+// U = u p of the tile at rows i0.., columns j0.. of X0's orientation: its
+// fp16 rounding into the first operand buffer (panels; tall tiles are
+// transposed through LDS) and the byte e4m3((U - hi) 2^5) into the low-byte
+// layout (accumulator order, as the update reads it).
+constexpr float kX0LoScale = 32.f;  // 2^5
 __device__ __forceinline__ void tile_store_x0(const StepArgs& A, const MatInfo& M, int32_t i0, int32_t j0,
                                               float (&u)[2][8], float p, float (*tile)[65]) {
   if (M.tall) {
@@ -561,10 +569,42 @@ __device__ __forceinline__ void tile_store_x0(const StepArgs& A, const MatInfo& 
     const int v = threadIdx.x + 256 * h;
     u32x4_t w;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = uint32_t(Op<OP_F16>::bits(u[h][2 * q] * p)) | (uint32_t(Op<OP_F16>::bits(u[h][2 * q + 1] * p)) << 16);
+    for (int q = 0; q < 4; ++q) {
+      u[h][2 * q] *= p;  // exact: a power of two
+      u[h][2 * q + 1] *= p;
+      w[q] = uint32_t(Op<OP_F16>::bits(u[h][2 * q])) | (uint32_t(Op<OP_F16>::bits(u[h][2 * q + 1])) << 16);
+    }
     *reinterpret_cast<u32x4_t*>(x + pidx(i0 + (v >> 3), j0 + (v & 7) * 8, M.mp)) = w;
   }
+  // Low bytes in accumulator order: each 32-row half of the tile is one
+  // contiguous 2 KB run of that layout (64 columns: one wave column, both
+  // column blocks j); thread t writes the 16 bytes of lane t % 64 of block
+  // j = t / 64 % 2 of half b = t / 128: row 32 b + t % 32, columns
+  // 32 j + 8 g + 4 (t / 32 % 2) + r at byte 4 g + r.
+  __syncthreads();  // the tall path above has finished reading the tile
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[v >> 3][(v & 7) * 8 + e] = u[h][e];
+  }
+  __syncthreads();
+  const int t = threadIdx.x, b = t >> 7, j = (t >> 6) & 1, ln = t & 63;
+  const int row = 32 * b + (ln & 31), col = 32 * j + 4 * (ln >> 5);
+  uint32_t w[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float U = tile[row][col + 8 * g + q];
+      // U - hi is exact; 2^5 / 2^18 puts it at lo4's fixed 2^18
+      r[q] = (U - Op<OP_F16>::load16(Op<OP_F16>::bits(U))) * (kX0LoScale / Op<OP_F16>::kLoScale);
+    }
+    w[g] = Op<OP_F16>::lo4(r[0], r[1], r[2], r[3]);
+  }
+  char* lo = A.ws + M.xl_off + lo8_index(i0 + 32 * b, j0, M.np);
+  *reinterpret_cast<u32x4_t*>(lo + (j * 64 + ln) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
 // Momentum step and X0's operand in one pass. Item {mat, ti, tj}: one 64 x
@@ -1475,7 +1515,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   // The update's low bytes of X (64 KB per tile, contiguous) take the place
   // of stages nst and nst+1 (slots nst % NS and (nst+1) % NS), which
   // otherwise repeat the last stage: the epilogue reads them from LDS.
-  constexpr bool LO_DMA = KIND == UPDATE && !X0S;
+  constexpr bool LO_DMA = KIND == UPDATE;
   const char* lo_src = LO_DMA ? P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) : nullptr;
   // One pass over stage g. Poly's b A term is folded into the accumulators
   // of block column J in the pass over the stage that holds those columns
@@ -1833,10 +1873,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       char* lo_t = P.ws + M.xl_off + (int64_t(TI) * (M.np / TN) + TJ) * (TM * TN) + lane * 16;
       auto lo_ptr = [&](int i, int j) { return lo_t + (((wm * 4 + i) * WN + wn) * 2 + j) * 1024; };
       u32x4 lq[4][2];
-      // The first step (X0S, a kernel of its own so that the other steps'
-      // register allocation is untouched) starts from X0 = sigma * operand
-      // with no low bytes: X1 = sigma (B' operand).
-      if constexpr (!X0S) {
+      {
         // the low bytes arrived with the k loop's last passes: block bi
         // (1 KB, 16 bytes per lane) is at offset (bi % 32) KB of ring slot
         // (nst + bi / 32) % NS; every wave reads its blocks before any wave
@@ -1852,17 +1889,14 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
           }
         MUON_WAIT_LGKMCNT0();
         asm volatile("s_barrier" ::: "memory");
-      } else {
-        const float sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] *= sg;
       }
-      // X' = B' hi + a 2^-18 lo  (B' = a I + B carries a hi)
-      const float as = P.a * (1.f / Op<OP>::kLoScale);
+      // X' = B' hi + a 2^-18 lo  (B' = a I + B carries a hi). The first step
+      // (X0S, a kernel of its own so that the other steps' register
+      // allocation is untouched) starts from X0 = sigma (U) with U = hi +
+      // lo 2^-5: X1 = sigma (B' hi + a 2^-5 lo).
+      const float as = P.a * (X0S ? 1.f / kX0LoScale : 1.f / Op<OP>::kLoScale);
+      float sg = 1.f;
+      if constexpr (X0S) sg = reinterpret_cast<const float*>(P.ws + P.x0s_off)[4 * it.mat];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1870,11 +1904,14 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
           uint32_t qw[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            if constexpr (!X0S) {
+            {
               float lv[4];
               Op<OP>::lo_vals(lq[i][j][g], lv);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][4 * g + r] = __fmaf_rn(as, lv[r], acc[i][j][4 * g + r]);
+              for (int r = 0; r < 4; ++r) {
+                acc[i][j][4 * g + r] = __fmaf_rn(as, lv[r], acc[i][j][4 * g + r]);
+                if constexpr (X0S) acc[i][j][4 * g + r] *= sg;
+              }
             }
             if constexpr (!LAST) {
               // split back into hi (staged straight into the LDS tile, the

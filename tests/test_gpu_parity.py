@@ -216,6 +216,40 @@ def test_random_small_sets(seed):
     check_buffers(nb, wb, "bf16")
 
 
+def low_rank(rng, rows, cols, k):
+    """rows x cols of rank k: Haar U, V (QR with the signs of diag(R)
+    folded in), singular values linspace(1, 0.5, k)."""
+    def haar(n, r):
+        q, rr = np.linalg.qr(rng.standard_normal((n, r)))
+        return q * np.sign(np.diag(rr))
+    return haar(rows, k) @ np.diag(np.linspace(1.0, 0.5, k)) @ haar(cols, k).T
+
+
+def test_low_rank_and_power_law_inputs():
+    """Rank-deficient gradients (rank 1, 2 and 8, both orientations) and a
+    1/i power-law spectrum. The polynomial's slope at 0 is a, so rounding
+    noise in X0 along the zero singular directions grows by up to a^5 ~ 485
+    over five steps; X0's low byte (and every later iterate's) keeps it
+    under the bar. Relative Frobenius error and the largest elementwise
+    error over the largest entry, both within 2e-2, with Nesterov momentum
+    from a zero buffer (u = g + 0.95 g in fp32: bits beyond fp16)."""
+    rng = np.random.default_rng(31)
+    specs = [(4, 300, 1), (300, 4, 1), (8, 100, 2), (64, 256, 1), (256, 1024, 8), (1024, 256, 8)]
+    mats = [low_rank(rng, r, c, k) for r, c, k in specs]
+    q1 = np.linalg.qr(rng.standard_normal((512, 512)))[0]
+    q2 = np.linalg.qr(rng.standard_normal((2048, 512)))[0]
+    mats.append(q1 @ np.diag(1.0 / np.arange(1, 513)) @ q2.T)
+    grads = [torch.from_numpy(g).to(torch.bfloat16).to(DEV) for g in mats]
+    bufs = [torch.zeros_like(g) for g in grads]
+    say("low-rank and power-law inputs")
+    got, _ = gpu_call(grads, bufs, QUINTIC, 5, momentum=0.95, nesterov=True)
+    want, _ = oracle_call([to_f64(g) for g in grads], [np.zeros(g.shape) for g in grads], QUINTIC, 5,
+                          momentum=0.95, nesterov=True)
+    for g, o, w in zip(grads, got, want):
+        assert rel(o, w) < TOL["bf16"], tuple(g.shape)
+        assert np.max(np.abs(o - w)) < TOL["bf16"] * np.max(np.abs(w)), tuple(g.shape)
+
+
 def lo_byte_index(mp, np_):
     """Byte offset of X(m, n) in the fp16 path's low-byte layout: per 256 x 256
     tile (row-major over tiles), per 32-row block u, per 64-column wave
@@ -238,24 +272,35 @@ def x0_record(ws, info):
 
 
 def test_x0_operand_and_scale():
-    """After a one-step call the workspace still holds X0's operand (the
-    momentum pass writes it, the last update only reads it): x_op0 =
-    fp16(u p) with p the power of two that puts max |u| in [2^12, 2^13), and
-    sigma * x_op0 is the oracle's X0 = u / (||u|| + eps) to fp16's rounding,
-    |error| <= 2^-11 |x| (half an ulp; the fp32 norm adds about 2^-20) plus
-    half of fp16's subnormal spacing 2^-24, times sigma. A fresh plan has no
-    guess of p (guessed 1); the second call on the same set guesses right."""
+    """After a one-step call the workspace still holds X0 (the momentum pass
+    writes it, the last update only reads it): U = u p with p the power of
+    two that puts max |u| in [2^12, 2^13), as its fp16 rounding hi (x_op0)
+    plus the e4m3 byte of (U - hi) 2^5 (x_lo), and sigma (hi + byte 2^-5) is
+    the oracle's X0 = u / (||u|| + eps) to the format's precision: |error| <=
+    2^-15 |x| (the byte's 4 significant bits below hi's last one; the fp32
+    norm adds about 2^-20) plus sigma 2^-14 (the byte's smallest step). A
+    fresh plan has no guess of p (guessed 1); the second call on the same
+    inputs guesses right. With Nesterov momentum u = g + mu buf' carries
+    fp32 bits that fp16 drops, so the byte is exercised (for a bf16 u, U is
+    exact in fp16 and the byte is zero)."""
     shapes = [(200, 333), (333, 200), (256, 512), (40, 700)]
     grads = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=9, shapes=shapes)]
+    gen = torch.Generator().manual_seed(3)
+    buf0 = [torch.randn(g.shape, generator=gen).to(torch.bfloat16).to(DEV) for g in grads]
     outs = [torch.empty_like(g) for g in grads]
-    plan = mu.MuonPlan(grads, None, outs)
+    bufs = [b.clone() for b in buf0]
+    plan = mu.MuonPlan(grads, bufs, outs)
+    cfg = mu.make_config(*QUINTIC, 1, 0.95, True)
     for call in range(2):
-        ws = plan.step(mu.make_config(*QUINTIC, 1))
+        for b, b0 in zip(bufs, buf0):
+            b.copy_(b0)
+        ws = plan.step(cfg)
         torch.cuda.synchronize()
         for i, g in enumerate(grads):
             info = plan.buffer_info(i)
             m, n, mp, np_ = info["m"], info["n"], info["mp"], info["np"]
-            x0 = oracle.frobenius_normalize(to_f64(g), 1e-7)
+            u, _ = oracle.momentum_update(to_f64(g), to_f64(buf0[i]), f32(0.95), True, "bf16")
+            x0 = oracle.frobenius_normalize(u, 1e-7)
             if g.shape[0] > g.shape[1]:
                 x0 = x0.T
             want = np.zeros((mp, np_))
@@ -269,11 +314,17 @@ def test_x0_operand_and_scale():
             hi = unpanel(ws[off: off + mp * np_ * 2].view(torch.float16), mp, np_).double().cpu().numpy()
             top = np.abs(hi).max()
             assert 2.0 ** 12 * (1 - 2.0 ** -11) <= top <= 2.0 ** 13, top
-            got = sigma * hi
-            bound = (2.0 ** -11 + 2.0 ** -19) * np.abs(want) + sigma * 2.0 ** -24
+            lob = ws[info["x_lo"]: info["x_lo"] + mp * np_].cpu().numpy()[lo_byte_index(mp, np_)]
+            lo = torch.from_numpy(np.ascontiguousarray(lob)).view(torch.float8_e4m3fn).double().numpy()
+            assert np.all(np.abs(lo) <= 64)
+            got = sigma * (hi + lo * 2.0 ** -5)
+            bound = (2.0 ** -15 + 2.0 ** -19) * np.abs(want) + sigma * 2.0 ** -14
             err = np.abs(got - want)
             assert np.all(err <= bound), (i, float(np.max(err / bound)))
+            # the byte carries what fp16 drops: hi alone is off by up to 2^-11
+            assert np.max(np.abs(sigma * hi - want)) > 4 * np.max(err)
             assert not np.any(hi[m:, :]) and not np.any(hi[:, n:])   # padding stays zero
+            assert not np.any(lo[m:, :]) and not np.any(lo[:, n:])
     plan.destroy()
 
 
