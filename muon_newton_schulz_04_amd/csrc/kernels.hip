@@ -1686,21 +1686,24 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       // B = c (A A) + b A (+ a I for fp16 operands, so that the update is
       // B' X).
       if (fold) {
-        // acc = A A + (b / c) A already
+        // acc = A A + (b / c) A already. Only a 32 x 32 block that a diagonal
+        // tile's diagonal crosses (its rows and columns start together; the
+        // offsets are wave-uniform) holds elements of a I.
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             if (i >= (j ? nr1 : nr0)) continue;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int e = 0; e < 16; ++e) acc[i][j][e] *= P.c;
+            if (TI == TJ && rbase + 32 * i == (j ? cb1 : cb0)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                float v = P.c * acc[i][j][4 * g + r];
-                const int m = m0 + rbase + 32 * i + l32, n = n0 + (j ? cb1 : cb0) + 8 * g + 4 * lh + r;
-                if (m == n && m < M.m) v += P.a;  // padding stays zero
-                acc[i][j][4 * g + r] = v;
-              }
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (l32 == 8 * g + 4 * lh + r && m0 + rbase + 32 * i + l32 < M.m)  // padding stays zero
+                    acc[i][j][4 * g + r] += P.a;
+            }
           }
         stage16(true);
       } else {
@@ -1735,11 +1738,13 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
             const float a4[4] = {Op<OP>::load16(bq.x & 0xffffu), Op<OP>::load16(bq.x >> 16),
                                  Op<OP>::load16(bq.y & 0xffffu), Op<OP>::load16(bq.y >> 16)};
             const int m = m0 + rbase + 32 * i + l32, n = n0 + cb + 8 * g + 4 * lh;
+            // (a I only in the blocks a diagonal tile's diagonal crosses)
+            const bool dblk = TI == TJ && rbase + 32 * i == cb;
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               v[r] = __fmaf_rn(P.c, acc[i][j][4 * g + r], P.b * a4[r]);
-              if (m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
+              if (dblk && m == n + r && m < M.m) v[r] += P.a;  // padding stays zero
             }
             *reinterpret_cast<uint2*>(sp) = e16::pack4(v[0], v[1], v[2], v[3], true);
           }
