@@ -16,7 +16,9 @@
  *
  * Arithmetic: the stored buffer buf' is the exact mu * buf + G rounded once
  * to the buffer's dtype (round to nearest, ties to even); u and the norm are
- * fp32. The matrix products run on the matrix cores with fp32
+ * fp32, the sum of u^2 kept relative to a power of two so that no finite u
+ * overflows it (a matrix whose norm itself exceeds fp32's range gives
+ * zeros). The matrix products run on the matrix cores with fp32
  * accumulation. bf16 sets: the operands X, A and B are fp16 (11-bit
  * significands at bf16's MFMA rate; every iterate is bounded by the
  * normalisation, so fp16's range suffices), and between steps X is kept as

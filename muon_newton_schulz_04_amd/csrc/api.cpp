@@ -163,6 +163,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.mats = p->d_mats;
   a.ws = static_cast<char*>(ws);
   a.parts = static_cast<float*>(ws);
+  a.part_exp = a.parts + H.total_partials;
   a.a = cfg->a;
   a.b = cfg->b;
   a.c = cfg->c;

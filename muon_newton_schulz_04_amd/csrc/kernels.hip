@@ -134,6 +134,50 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return s;
 }
 
+// Sums of squares relative to a power of two: a partial sum s with exponent
+// e stands for s 4^e, e being the exponent of the largest |u| it covers, so
+// its terms stay below 4 and no finite u overflows fp32 (a plain fp32 sum of
+// u^2 does once entries pass about 2^60). Scaling by powers of two is exact,
+// so away from fp32's range limits every partial, and the norm, is bitwise
+// that of the plain sum in the same order.
+// The exponent e of x in [2^e, 2^(e+1)), clamped to [-126, 126]; 0 for
+// zero, NaN and infinities.
+__device__ __forceinline__ int exp_of(float x) {
+  if (!(x > 0.f) || !(x <= 3.40282347e38f)) return 0;
+  const int e = static_cast<int>((__float_as_uint(x) >> 23) & 255u) - 127;
+  return min(max(e, -126), 126);
+}
+// 2^k for k in [-126, 127]
+__device__ __forceinline__ float pow2i(int k) { return __uint_as_float(static_cast<uint32_t>(k + 127) << 23); }
+// Running sum of squares of one thread, relative to 4^e (e the largest
+// exponent seen so far, starting at -126).
+struct ScaledSsq {
+  float s = 0.f;
+  int e = -126;
+  __device__ __forceinline__ void add(float u) {
+    const int eu = exp_of(fabsf(u));
+    if (u != 0.f && eu > e) {  // rescale what was summed so far (exact unless it underflows)
+      s = ldexpf(s, 2 * (e - eu));
+      e = eu;
+    }
+    const float x = u * pow2i(-e);
+    s = __fmaf_rn(x, x, s);
+  }
+};
+// Block combination of the threads' scaled sums (fixed order): {s, e}.
+__device__ __forceinline__ ScaledSsq block_ssq_256(ScaledSsq t, float* red, int* ered) {
+  int e = t.e;
+  for (int o = 32; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o, 64));
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) ered[w] = e;
+  __syncthreads();
+  ScaledSsq r;
+  r.e = max(max(ered[0], ered[1]), max(ered[2], ered[3]));
+  r.s = block_sum_256(ldexpf(t.s, 2 * (t.e - r.e)), red);
+  return r;
+}
+
 // StepArgs (kernel arguments) is declared in launch.hpp.
 
 // Component e (compile-time after unrolling) of a 16-byte register vector.
@@ -219,7 +263,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
   if (it.mat < 0) return;
   const MatInfo& M = A.mats[it.mat];
   const int32_t r0 = it.a, nr = it.b;
-  float acc = 0.f;
+  ScaledSsq acc;
   const T* g = static_cast<const T*>(M.grad);
   T* mb = static_cast<T*>(M.mom);
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
@@ -241,16 +285,12 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
           const float gf = Elem<T>::load(ge, e);
           const float nb = momentum_new<T>(A.mu, Elem<T>::load(be, e), gf);
           Elem<T>::store(oe, e, nb);
-          const float u = form_u(gf, nb, A);
-          acc = __fmaf_rn(u, u, acc);
+          acc.add(form_u(gf, nb, A));
         }
         *reinterpret_cast<uint4*>(mb + off) = ov;
       } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float u = Elem<T>::load(ge, e);
-          acc = __fmaf_rn(u, u, acc);
-        }
+        for (int e = 0; e < V; ++e) acc.add(Elem<T>::load(ge, e));
       }
     }
   } else {
@@ -264,12 +304,16 @@ __global__ __launch_bounds__(256) void momentum_kernel(StepArgs A) {
         Elem<T>::store(mb, off, nb);
         u = form_u(gf, nb, A);
       }
-      acc = __fmaf_rn(u, u, acc);
+      acc.add(u);
     }
   }
   __shared__ float red[4];
-  const float s = block_sum_256(acc, red);
-  if (threadIdx.x == 0) A.parts[it.c] = s;
+  __shared__ int ered[4];
+  const ScaledSsq b = block_ssq_256(acc, red, ered);
+  if (threadIdx.x == 0) {
+    A.parts[it.c] = b.s;
+    A.part_exp[it.c] = static_cast<float>(b.e);
+  }
 }
 
 // -------------------------------------------------------- normalize kernel
@@ -304,11 +348,20 @@ __global__ __launch_bounds__(256) void normalize_kernel(StepArgs A) {
   __shared__ float red[4];
   __shared__ float tile[64][65];
 
-  // 1. scale from this matrix's partial sums, in slot order
+  // 1. scale from this matrix's partial sums (each relative to 4^e), in
+  //    slot order, relative to 4^E for the largest e
+  __shared__ int ered[4];
+  int E = -126;
+  for (int32_t p = threadIdx.x; p < M.part_cnt; p += 256) E = max(E, static_cast<int>(A.part_exp[M.part_off + p]));
+  for (int o = 32; o > 0; o >>= 1) E = max(E, __shfl_xor(E, o, 64));
+  if ((threadIdx.x & 63) == 0) ered[threadIdx.x >> 6] = E;
+  __syncthreads();
+  E = max(max(ered[0], ered[1]), max(ered[2], ered[3]));
   float s = 0.f;
-  for (int32_t p = threadIdx.x; p < M.part_cnt; p += 256) s += A.parts[M.part_off + p];
+  for (int32_t p = threadIdx.x; p < M.part_cnt; p += 256)
+    s += ldexpf(A.parts[M.part_off + p], 2 * (static_cast<int>(A.part_exp[M.part_off + p]) - E));
   s = block_sum_256(s, red);
-  const float scale = 1.0f / (sqrtf(s) + A.eps);
+  const float scale = 1.0f / (ldexpf(sqrtf(s), E) + A.eps);
 
   // 2. caller-side tile rows cr0.., cols cc0..; thread handles 2 runs of 8
   //    consecutive caller columns: run h covers row (tid + 256 h) / 8,
@@ -609,8 +662,8 @@ __device__ __forceinline__ void tile_store_x0(const StepArgs& A, const MatInfo& 
 
 // Momentum step and X0's operand in one pass. Item {mat, ti, tj}: one 64 x
 // 64 tile of mp x np (X0's orientation; tiles in the padding store zeros).
-// Per tile: the sum of u^2 (each thread's 16 terms in order, then the
-// block's fixed tree) and the largest |u|.
+// Per tile: the largest |u| and the sum of u^2 relative to 4^e for e its
+// exponent (each thread's 16 terms in order, then the block's fixed tree).
 __global__ __launch_bounds__(256) void momentum_x0_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
   if (it.mat < 0) return;
@@ -620,16 +673,23 @@ __global__ __launch_bounds__(256) void momentum_x0_kernel(StepArgs A) {
   const int32_t i0 = it.a * 64, j0 = it.b * 64;
   float u[2][8];
   tile_u_bf16<true>(A, M, M.tall ? j0 : i0, M.tall ? i0 : j0, u);
-  float ss = 0.f, mx = 0.f;
+  float mx = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = nan_max(mx, fabsf(u[h][e]));
+  mx = block_max_256(mx, red);
+  // the tile's sum of squares relative to 4^e, e = exp_of(largest |u|)
+  const float inv = pow2i(-exp_of(mx));
+  float ss = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ss = __fmaf_rn(u[h][e], u[h][e], ss);
-      mx = nan_max(mx, fabsf(u[h][e]));
+      const float x = u[h][e] * inv;
+      ss = __fmaf_rn(x, x, ss);
     }
   ss = block_sum_256(ss, red);
-  mx = block_max_256(mx, red);
   const float p = x0_pow2(A.hint[it.mat]);
   if (threadIdx.x == 0) {
     const int32_t slot = M.tile_off + it.a * (M.np / 64) + it.b;
@@ -640,8 +700,8 @@ __global__ __launch_bounds__(256) void momentum_x0_kernel(StepArgs A) {
   tile_store_x0(A, M, i0, j0, u, p, tile);
 }
 
-// Scale pass. Item {mat}: one workgroup per matrix sums its tile sums
-// (fixed order) and takes the largest |u|, then stores {sigma, p, p of the
+// Scale pass. Item {mat}: one workgroup per matrix takes the largest |u|
+// and sums its tile sums (fixed order), then stores {sigma, p, p of the
 // momentum pass, rewrite flag} and the new hint. The flag is set where the
 // momentum pass's p differs from this one.
 __global__ __launch_bounds__(256) void x0_scale_kernel(StepArgs A) {
@@ -651,15 +711,17 @@ __global__ __launch_bounds__(256) void x0_scale_kernel(StepArgs A) {
   __shared__ float red[4];
   const float* ts = reinterpret_cast<const float*>(A.ws + A.tsum_off) + M.tile_off;
   const float* tm = reinterpret_cast<const float*>(A.ws + A.tmax_off) + M.tile_off;
-  float s = 0.f, mx = 0.f;
-  for (int32_t q = threadIdx.x; q < M.tile_cnt; q += 256) {
-    s += ts[q];
-    mx = nan_max(mx, tm[q]);
-  }
-  s = block_sum_256(s, red);
+  float mx = 0.f;
+  for (int32_t q = threadIdx.x; q < M.tile_cnt; q += 256) mx = nan_max(mx, tm[q]);
   mx = block_max_256(mx, red);
+  // tile sums are relative to 4^exp_of(tile max); sum them relative to the
+  // matrix's 4^E
+  const int E = exp_of(mx);
+  float s = 0.f;
+  for (int32_t q = threadIdx.x; q < M.tile_cnt; q += 256) s += ldexpf(ts[q], 2 * (exp_of(tm[q]) - E));
+  s = block_sum_256(s, red);
   if (threadIdx.x == 0) {
-    const float scale = 1.0f / (sqrtf(s) + A.eps);
+    const float scale = 1.0f / (ldexpf(sqrtf(s), E) + A.eps);
     const float p = x0_pow2(mx);
     float* xs = reinterpret_cast<float*>(A.ws + A.x0s_off) + 4 * it.mat;
     xs[0] = scale / p;  // exact (p is a power of two) unless it underflows

@@ -13,6 +13,7 @@ struct StepArgs {
   const WorkItem* items;   // device schedule of this launch
   char* ws;                // workspace base
   float* parts;            // sum-of-squares partials (workspace head)
+  float* part_exp;         // their exponents: a partial s with exponent e stands for s 4^e
   float a, b, c, mu, eps;
   int32_t nesterov;
   int32_t use_mom;  // momentum state present and mu != 0

@@ -301,7 +301,8 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     }
   }
   P.total_partials = nparts;
-  size_t off = round_up(static_cast<int64_t>(nparts) * 4, kWsAlign);
+  // partial sums of u^2, then their exponents
+  size_t off = round_up(static_cast<int64_t>(nparts) * 8, kWsAlign);
   auto take = [&off](size_t bytes) {
     int64_t o = static_cast<int64_t>(off);
     off = round_up(static_cast<int64_t>(off + bytes), kWsAlign);

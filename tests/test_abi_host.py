@@ -140,7 +140,7 @@ def expected_ws(shapes, dtype):
     for r, c in shapes:
         rpi = max(1, 16384 // c)
         parts += (r + rpi - 1) // rpi
-    off = ru(parts * 4, 256)
+    off = ru(parts * 8, 256)        # partial sums of u^2 and their exponents
     if dtype == mu.MUON_BF16:
         # per 64 x 64 tile of each padded matrix: sum of u^2 and largest |u|;
         # per matrix: {sigma, p, p guessed, 0}

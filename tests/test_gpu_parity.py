@@ -617,6 +617,30 @@ def test_config_wide_powerlaw():
     run_config("wide_2048x8192_powerlaw", sample=pick, device_gen=DEV)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("steps", [0, 5])
+def test_extreme_gradient_scales(dtype, steps):
+    """Gradients scaled by 2^100 and 2^-20 (exact scalings of both dtypes).
+    A plain fp32 sum of u^2 overflows once entries pass about 2^60, which
+    would turn out into zeros; the partial sums are kept relative to a power
+    of two, so the norm and out match the oracle on the scaled inputs, with
+    Nesterov momentum from a zero buffer. (Inputs whose norm falls below eps
+    are another matter: X0 = u / (||u|| + eps) is then tiny, and the fp16
+    iterates of bf16 sets flush it.)"""
+    shapes = [(200, 333), (333, 200), (64, 1100)]
+    base = make_gradients(CONFIGS["gpt2_small_block"], step=17, shapes=shapes)
+    for scale in (2.0 ** 100, 2.0 ** -20):
+        grads = [(g.double() * scale).to(TDT[dtype]).to(DEV) for g in base]
+        bufs = [torch.zeros_like(g) for g in grads]
+        say(f"scale 2^{int(np.log2(scale))} {dtype} k={steps}")
+        got, _ = gpu_call(grads, bufs, QUINTIC, steps, momentum=0.95, nesterov=True)
+        want, _ = oracle_call([to_f64(g) for g in grads], [np.zeros(s) for s in shapes], QUINTIC, steps,
+                              momentum=0.95, nesterov=True, buf_dtype=dtype)
+        for shp, o, w in zip(shapes, got, want):
+            assert np.all(np.isfinite(o)), shp
+            assert rel(o, w) < TOL[dtype], (shp, scale, rel(o, w))
+
+
 def test_nan_and_inf_propagate():
     """NaN and Inf in a gradient propagate to that matrix's whole output
     (a NaN or infinite norm makes every entry of X0 NaN or zero times
