@@ -366,9 +366,9 @@ def test_x1_low_bytes_are_residuals():
 def test_x0_guess_never_changes_results():
     """X0's power of two is guessed from the plan's previous call and
     corrected by the scale pass: a plan that has seen other gradient scales
-    (smaller by 2^-20, where every guess is wrong and the operand is
-    rewritten, larger by 3, the same again, far larger) gives bitwise the
-    outputs and momentum buffers of a fresh plan on each call's inputs."""
+    (smaller by 2^-20, where guesses miss and operands are rewritten, larger
+    by 3, the same again, far larger) gives bitwise the outputs and momentum
+    buffers of a fresh plan on each call's inputs."""
     shapes = [(200, 333), (333, 200), (64, 1100), (520, 96)]
     base = [g.to(DEV) for g in make_gradients(CONFIGS["gpt2_small_block"], step=21, shapes=shapes)]
     grads = [g.clone() for g in base]
@@ -384,8 +384,12 @@ def test_x0_guess_never_changes_results():
         ws = plan.step(cfg)
         torch.cuda.synchronize()
         rec = [x0_record(ws, plan.buffer_info(i)) for i in range(len(shapes))]
+        # the flag marks exactly the matrices whose guess missed; the call
+        # after the 2^-20 scaling (u shrinks to about mu^2 / (1 + mu) of its
+        # size: the buffer still holds the large gradient) rewrites some
+        assert all(r[3] == (1.0 if r[1] != r[2] else 0.0) for r in rec)
         if call == 1:
-            assert all(r[1] != r[2] and r[3] == 1 for r in rec), "a scale 2^-20 away: every guess is wrong"
+            assert any(r[3] == 1 for r in rec), "the rewrite path ran"
         got_o = [o.clone() for o in outs]
         got_b = [b.clone() for b in bufs]
         outs_fresh = [torch.empty_like(g) for g in grads]
