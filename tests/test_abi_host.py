@@ -291,6 +291,22 @@ def check_schedules(shapes, dtype):
         assert all(e0 <= b1 for (_, e0), (b1, _) in zip(spans, spans[1:]))   # disjoint partial slots
 
 
+def test_schedule_query_kinds(lib):
+    """Kinds 0 .. MUON_K_COUNT + 1 (the split-Gram sums and the scale pass of
+    X0) are queried; anything else is MUON_E_INVALID, before any work."""
+    shapes = [(200, 333), (768, 768)]
+    for kind in range(7):
+        mu.muon_schedule_query(shapes, mu.MUON_BF16, kind)
+    for kind in (-1, 7, 100):
+        with pytest.raises(mu.MuonError) as e:
+            mu.muon_schedule_query(shapes, mu.MUON_BF16, kind)
+        assert e.value.code == 1
+    # the scale pass exists for bf16 sets only, one item per non-empty matrix
+    s = mu.muon_schedule_query(shapes + [(0, 64)], mu.MUON_BF16, 6)
+    assert sorted(s[s[:, 0] >= 0][:, 0].tolist()) == [0, 1]
+    assert len(mu.muon_schedule_query(shapes, mu.MUON_F32, 6)) == 0
+
+
 def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):
     shapes = SHAPE_SETS["gpt2_124m"]
     s = mu.muon_schedule_query(shapes, mu.MUON_BF16, 2)
