@@ -254,7 +254,12 @@ def main():
     torch.cuda.set_device(dev)
     # one plan over fixed gradient buffers, as in training (backward rewrites
     # the same .grad tensors every step); the momentum buffers evolve
-    grads = [g.to(dev) for g in make_gradients(wl, step=0, device="cpu")]
+    # (sets beyond 2^28 elements are generated on the GPU: the host's QR
+    # factorisations of the power-law set take minutes)
+    gen_dev = "cuda" if sum(r * c for r, c in wl.shapes) > (1 << 28) else "cpu"
+    print(f"bench: generating {wl.n_matrices} matrices of {wl.name} on {gen_dev}", file=sys.stderr, flush=True)
+    grads = [g.to(dev) for g in make_gradients(wl, step=0, device=gen_dev)]
+    print("bench: inputs ready", file=sys.stderr, flush=True)
     bufs = [torch.zeros_like(g) for g in grads] if wl.momentum else None
     outs = [torch.empty_like(g) for g in grads]
     plan = mu.MuonPlan(grads, bufs, outs)
