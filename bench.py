@@ -14,7 +14,9 @@ the largest share of the step's time against its matrix-core roof (HBM under
 `roofline.other`), timed with HIP events recorded around
 each launch in a second pass of the same length (in that pass the launches
 run one at a time on the step's stream, so each interval holds one launch;
-the timed pass runs large sets as two concurrent groups); the
+the timed pass runs the Newton-Schulz steps as one chained launch where the
+plan has one, else as separate launches with large sets in concurrent
+groups; `separate_launches_ms_per_step` times the latter for comparison); the
 CPU baseline times the float64 oracle on a bounded sample of the same
 matrices. `roofline.traffic` is the dominant kernel's HBM bytes per launch
 from the committed rocprofv3 counter summary (null if that summary was taken
@@ -316,6 +318,23 @@ def main():
         torch.cuda.synchronize()
         hip_graph = {"error": str(exc)[:200]}
 
+    # the step form the timed pass used (the chained launch where the plan
+    # has one), and the same step with the separate launches (three per
+    # Newton-Schulz step, large sets as concurrent groups) for comparison
+    chained, chain_err = plan.chain_state()
+    separate = None
+    if chained:
+        plan.set_chained(False)
+        e0.record(stream)
+        for _ in range(args.steps):
+            plan.step(cfg, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        separate = e0.elapsed_time(e1) / args.steps
+        plan.set_chained(True)
+    if chain_err:
+        raise SystemExit(f"bench: chained launch reported error {chain_err}")
+
     # second pass of the same length with per-launch HIP events
     plan.set_timing(True)
     plan.kernel_times()
@@ -447,7 +466,8 @@ def main():
                    "shapes": "48x768x768 + 12x768x3072 + 12x3072x768"
                    if wl.name == "gpt2_124m_matrix_set" else str(sorted(set(wl.shapes))),
                    "ns_steps": wl.steps, "coeffs": list(wl.coeffs), "momentum": wl.momentum,
-                   "nesterov": wl.nesterov, "falg_gflop_per_step": falg / 1e9},
+                   "nesterov": wl.nesterov, "falg_gflop_per_step": falg / 1e9,
+                   "schedule": "chained" if chained else "separate launches"},
         "pct_bf16_dense_peak": 100.0 * value / PEAK["bf16"],
         "matrices_per_s": wl.n_matrices / (ms * 1e-3),
         "step_ms": {"n": int(step_ms.size), "mean": float(step_ms.mean()),
@@ -455,6 +475,7 @@ def main():
                     "min": float(step_ms.min())},
         "wall_s_timed": wall,
         "hip_graph": hip_graph,
+        "separate_launches_ms_per_step": separate,
         "kernels": per_kernel,
         "roofline": roof,
         "next": {"rank_share": {

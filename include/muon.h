@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum {
@@ -296,7 +296,13 @@ typedef enum {
  * row, tile col, pbase << 16 | q << 8 | S} per split tile, one per 128 x 128
  * quarter q (empty when nothing splits). kind == MUON_K_COUNT + 1 queries
  * the scale pass of bf16 sets: one item {matrix, 0, 0, 0} per matrix
- * (empty for fp32 sets).
+ * (empty for fp32 sets). kind == MUON_K_COUNT + 2 queries the chained
+ * schedule (muon_plan_set_chained; empty where the set has none): the
+ * lists of XCDs 0 .. 7 one after the other, each item of one step
+ * {matrix, tile row << 16 | tile col, xcd << 8 | kernel kind (MUON_K_GRAM,
+ * MUON_K_POLY or MUON_K_UPDATE), need}, where the item of step s waits
+ * until its matrix has completed s * (its Gram, poly and update tiles per
+ * step) + need tiles.
  * Writes min(cap, count) items to `items` (may be NULL when cap == 0) and
  * the total to *count. No device calls. */
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype,
@@ -314,6 +320,34 @@ muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype d
  * or last read (reading resets). Off by default. */
 muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable);
 muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches);
+
+/* Chained schedule. A bf16 plan with at least eight non-empty matrices
+ * whose work spreads evenly over the eight XCDs (and no split Gram tiles)
+ * runs the Newton-Schulz steps of muon_plan_step as one launch instead of
+ * three per step: every Gram, poly and update tile of all k steps, with
+ * all tiles of a matrix on one XCD. The workgroups on an XCD take the
+ * XCD's tiles in a fixed order, and a tile starts once its matrix has
+ * finished the tiles it reads (Gram of step s after the update of step
+ * s - 1, poly after Gram, the update after poly). The kernels of the two
+ * forms compute each tile identically, so results are bitwise the same
+ * (the order of the steps of the iteration, "How to train a GPT model in 3
+ * minutes", section 2, is unchanged; only independent tiles of different
+ * matrices overlap). Each wait is bounded (2 s unless set otherwise with
+ * muon_plan_set_chain_timeout, 0 to 3600 s in microseconds, else
+ * MUON_E_INVALID); a wait past its bound records an error in the plan and
+ * ends the launch early, leaving `out` and the workspace undefined (the
+ * momentum buffers are updated before the chained launch starts).
+ * muon_plan_set_chained(plan, 0) makes the plan use the separate launches
+ * (1, the default, uses the chained launch where the plan has one); per-
+ * kernel timing always uses the separate launches.
+ * muon_plan_chain_state waits for the device, then reports in *chained
+ * whether steps of this plan use the chained launch (1) or not (0), and
+ * in *error the plan's error word since the last query (0: none; 1: a
+ * wait passed its bound; 2: a workgroup ran on a die the schedule does not
+ * know), which it clears. */
+muon_status muon_plan_set_chained(muon_plan* plan, int32_t enable);
+muon_status muon_plan_set_chain_timeout(muon_plan* plan, int64_t microseconds);
+muon_status muon_plan_chain_state(muon_plan* plan, int32_t* chained, int32_t* error);
 
 /* Workspace layout of matrix `idx` of a plan (byte offsets from the
  * workspace base; -1 where a buffer does not exist). All buffers use the

@@ -19,6 +19,7 @@ __all__ = [
     "muon_workspace_bytes", "muon_plan_create", "muon_plan_step", "muon_plan_destroy",
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
+    "muon_plan_set_chained", "muon_plan_set_chain_timeout", "muon_plan_chain_state",
     "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
     "muon_plan_step_noalloc", "MUON_SCRATCH_BYTES",
     "MuonAdamTensor", "MuonAdamConfig", "AdamPlan", "muon_adam_plan_create",
@@ -106,6 +107,9 @@ def load_library(path: str = LIB_PATH):
         "muon_plan_set_timing": (i32, [vp, i32]),
         "muon_plan_kernel_times": (i32, [vp, P(ctypes.c_double), P(i64)]),
         "muon_plan_buffer_info": (i32, [vp, i32, P(MuonBufferInfo)]),
+        "muon_plan_set_chained": (i32, [vp, i32]),
+        "muon_plan_set_chain_timeout": (i32, [vp, i64]),
+        "muon_plan_chain_state": (i32, [vp, P(i32), P(i32)]),
         "muon_plan_set_weights": (i32, [vp, P(MuonWeight), i32]),
         "muon_plan_step_apply": (i32, [vp, P(MuonConfig), P(MuonApply), vp, sz, vp]),
         "muon_adam_plan_create": (i32, [P(MuonAdamTensor), i32, i32, P(vp)]),
@@ -325,6 +329,24 @@ class MuonPlan:
         _check(load_library().muon_plan_kernel_times(self.handle, ms, n), "muon_plan_kernel_times")
         return {KERNEL_NAMES[k]: (ms[k], n[k]) for k in range(5)}
 
+    def set_chained(self, on: bool):
+        """Use the chained launch where the plan has one (default) or the separate launches."""
+        _check(load_library().muon_plan_set_chained(self.handle, 1 if on else 0),
+               "muon_plan_set_chained")
+
+    def set_chain_timeout(self, microseconds: int):
+        """Bound of one wait of the chained launch (default 2 s)."""
+        _check(load_library().muon_plan_set_chain_timeout(self.handle, int(microseconds)),
+               "muon_plan_set_chain_timeout")
+
+    def chain_state(self):
+        """(chained, error): whether steps use the chained launch, and the plan's error
+        word since the last query (0: none; waits for the device, clears the word)."""
+        c, e = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(load_library().muon_plan_chain_state(self.handle, ctypes.byref(c), ctypes.byref(e)),
+               "muon_plan_chain_state")
+        return int(c.value), int(e.value)
+
     def buffer_info(self, idx: int) -> dict:
         info = MuonBufferInfo()
         _check(load_library().muon_plan_buffer_info(self.handle, idx, ctypes.byref(info)),
@@ -374,6 +396,18 @@ def muon_plan_set_timing(plan: MuonPlan, on: bool):
 
 def muon_plan_kernel_times(plan: MuonPlan):
     return plan.kernel_times()
+
+
+def muon_plan_set_chained(plan: MuonPlan, on: bool):
+    plan.set_chained(on)
+
+
+def muon_plan_set_chain_timeout(plan: MuonPlan, microseconds: int):
+    plan.set_chain_timeout(microseconds)
+
+
+def muon_plan_chain_state(plan: MuonPlan):
+    return plan.chain_state()
 
 
 def muon_plan_buffer_info(plan: MuonPlan, idx: int) -> dict:

@@ -30,6 +30,10 @@ struct muon_plan_s {
   const WorkItem* d_items[muon::kKinds] = {};
   const WorkItem* d_whole[muon::kKinds] = {};  // one-group schedules (timing)
   float* d_hint = nullptr;                    // per matrix: largest |u| of the last call (0: none)
+  const muon::ChainItem* d_chain = nullptr;   // chained schedule: the per-XCD lists
+  int32_t* d_err = nullptr;                   // chained launches: a wait past its bound (sticky)
+  bool chain_on = true;                       // muon_plan_set_chained
+  int64_t chain_wait_us = 2000000;            // muon_plan_set_chain_timeout
   // groups > 1: one stream per group (default priority) and the events that
   // fork them from, and join them back to, the caller's stream
   hipStream_t gstream[muon::kMaxGroups] = {};
@@ -72,7 +76,14 @@ muon_status upload(muon_plan_s* p) {
   bytes = (bytes + 255) / 256 * 256;
   const size_t hint_off = bytes;
   bytes += sizeof(float) * std::max<size_t>(1, p->host.info.size());
+  bytes = (bytes + 255) / 256 * 256;
+  const size_t err_off = bytes;
+  bytes += 256;
+  const size_t chain_off = bytes;
+  bytes += sizeof(muon::ChainItem) * std::max<size_t>(1, p->host.chain.size());
   std::vector<char> h(bytes, 0);
+  if (!p->host.chain.empty())
+    std::memcpy(h.data() + chain_off, p->host.chain.data(), sizeof(muon::ChainItem) * p->host.chain.size());
   if (!p->host.info.empty())
     std::memcpy(h.data(), p->host.info.data(), sizeof(MatInfo) * p->host.info.size());
   for (int k = 0; k < muon::kKinds; ++k) {
@@ -110,6 +121,8 @@ muon_status upload(muon_plan_s* p) {
     p->d_whole[k] = reinterpret_cast<const WorkItem*>(base + woffs[k]);
   }
   p->d_hint = reinterpret_cast<float*>(base + hint_off);
+  p->d_err = reinterpret_cast<int32_t*>(base + err_off);
+  p->d_chain = reinterpret_cast<const muon::ChainItem*>(base + chain_off);
   return MUON_OK;
 }
 
@@ -181,6 +194,10 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.tmax_off = H.tmax_off;
   a.x0s_off = H.x0s_off;
   a.hint = p->d_hint;
+  // the chained schedule (not under per-kernel timing, which times each
+  // kernel's own launch)
+  const bool chain = fused && H.chained && p->chain_on && !(p->timing && allow_timing);
+  a.chain_off = chain ? H.chain_off : -1;
   if (ap) {
     a.apply = 1;
     a.lr = ap->lr;
@@ -271,6 +288,35 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
       for (int kind : {int(MUON_K_GRAM), muon::kGramReduce, int(MUON_K_POLY), int(MUON_K_UPDATE)})
         if ((r = timed(kind)) != MUON_OK) return r;
     }
+    return MUON_OK;
+  }
+  if (chain) {
+    // momentum, the scale pass (which clears the chain's counters) and the
+    // rewrite over the whole set (the one-group schedules), then every Gram,
+    // poly and update tile of all steps in one launch with a workgroup per
+    // ticket of the longest XCD list
+    for (int kind : {int(MUON_K_MOMENTUM), int(MUON_K_NORMALIZE)}) {
+      const Slot o = slot_of(kind);
+      for (int k = 0; k < o.n; ++k) {
+        const auto& w = H.whole[o.sched[k]].items;
+        if (!w.empty() &&
+            run(kind, o.kernel[k], p->d_whole[o.sched[k]], static_cast<int32_t>(w.size()), s) != hipSuccess)
+          return MUON_E_LAUNCH;
+      }
+    }
+    muon::ChainArgs c{};
+    c.items = p->d_chain;
+    c.steps = cfg->steps;
+    c.err = p->d_err;
+    c.wait_ticks = static_cast<uint64_t>(p->chain_wait_us) * 100u;
+    int64_t longest = 0;
+    for (int x = 0; x <= muon::kNumXcd; ++x) c.beg[x] = H.chain_beg[x];
+    for (int x = 0; x < muon::kNumXcd; ++x)
+      longest = std::max<int64_t>(longest, int64_t(H.chain_beg[x + 1] - H.chain_beg[x]) * cfg->steps);
+    a.cur = 0;
+    a.last = 0;
+    a.x0_scaled = 1;
+    if (muon::launch_chain(a, c, static_cast<int>(longest * muon::kNumXcd), s) != hipSuccess) return MUON_E_LAUNCH;
     return MUON_OK;
   }
   if (H.ngroups == 1) return sequence(0, s);
@@ -475,12 +521,26 @@ muon_status muon_orthogonalize(const muon_matrix* mats, int32_t n, muon_dtype dt
 
 muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype dtype, int32_t kind,
                                 int32_t* items, int64_t cap, int64_t* count) {
-  if (count == nullptr || kind < 0 || kind > MUON_K_COUNT + 1 || cap < 0 ||
+  if (count == nullptr || kind < 0 || kind > MUON_K_COUNT + 2 || cap < 0 ||
       (cap > 0 && items == nullptr))
     return MUON_E_INVALID;
   HostPlan P;
   muon_status st = muon::build_plan(mats, n, dtype, &P);
   if (st != MUON_OK) return st;
+  if (kind == MUON_K_COUNT + 2) {  // the chained schedule's lists, XCD by XCD
+    *count = static_cast<int64_t>(P.chain.size());
+    const int64_t w = std::min<int64_t>(cap, *count);
+    int x = 0;
+    for (int64_t i = 0; i < w; ++i) {
+      while (i >= P.chain_beg[x + 1]) ++x;
+      const muon::ChainItem& c = P.chain[i];
+      items[4 * i + 0] = c.mat;
+      items[4 * i + 1] = (int32_t(c.ti) << 16) | int32_t(c.tj);
+      items[4 * i + 2] = (x << 8) | (c.kind_n & 255);
+      items[4 * i + 3] = c.need;
+    }
+    return MUON_OK;
+  }
   const auto& v = P.sched[kind].items;
   *count = static_cast<int64_t>(v.size());
   const int64_t w = std::min<int64_t>(cap, *count);
@@ -516,6 +576,34 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
     launches[k] = plan->acc_n[k];
     plan->acc_ms[k] = 0.0;
     plan->acc_n[k] = 0;
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_set_chained(muon_plan* plan, int32_t enable) {
+  if (plan == nullptr) return MUON_E_INVALID;
+  plan->chain_on = enable != 0;
+  return MUON_OK;
+}
+
+muon_status muon_plan_set_chain_timeout(muon_plan* plan, int64_t microseconds) {
+  if (plan == nullptr || microseconds < 0 || microseconds > int64_t(3600) * 1000000) return MUON_E_INVALID;
+  plan->chain_wait_us = microseconds;
+  return MUON_OK;
+}
+
+muon_status muon_plan_chain_state(muon_plan* plan, int32_t* chained, int32_t* error) {
+  if (plan == nullptr || chained == nullptr || error == nullptr) return MUON_E_INVALID;
+  *chained = plan->host.chained && plan->chain_on ? 1 : 0;
+  *error = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return MUON_E_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(error, plan->d_err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(plan->d_err, 0, sizeof(int32_t)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return MUON_E_DEVICE;
   }
   return MUON_OK;
 }

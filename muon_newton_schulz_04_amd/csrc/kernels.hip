@@ -703,9 +703,18 @@ __global__ __launch_bounds__(256) void momentum_x0_kernel(StepArgs A) {
 // Scale pass. Item {mat}: one workgroup per matrix takes the largest |u|
 // and sums its tile sums (fixed order), then stores {sigma, p, p of the
 // momentum pass, rewrite flag} and the new hint. The flag is set where the
-// momentum pass's p differs from this one.
+// momentum pass's p differs from this one. With a chained schedule it also
+// clears the matrix's completion counter (and block 0 the tickets).
 __global__ __launch_bounds__(256) void x0_scale_kernel(StepArgs A) {
   const WorkItem it = A.items[blockIdx.x];
+  if (A.chain_off >= 0 && threadIdx.x < kNumXcd + 1) {
+    int32_t* ctr = reinterpret_cast<int32_t*>(A.ws + A.chain_off);
+    if (threadIdx.x < kNumXcd) {
+      if (blockIdx.x == 0) ctr[threadIdx.x] = 0;
+    } else if (it.mat >= 0) {
+      ctr[kNumXcd + it.mat] = 0;
+    }
+  }
   if (it.mat < 0) return;
   const MatInfo& M = A.mats[it.mat];
   __shared__ float red[4];
@@ -1076,14 +1085,27 @@ __device__ __forceinline__ int off_k(int k, int c) { return k * KROW + ((c ^ ((k
 // only writes are these), so the warning is silenced here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// COH: a device-scope load (sc1), which never hits an L1 copy older than
+// the XCD's L2 (the chained launch, whose tiles read what other CUs of the
+// XCD wrote earlier in the same launch).
+template <bool COH = false>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
-      : "s"(lds_base), "v"(src)
-      : "memory", "m0");
+  if constexpr (COH)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off sc1"
+        :
+        : "s"(lds_base), "v"(src)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_base), "v"(src)
+        : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -1102,7 +1124,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 constexpr int DMA_WAVES = NWAVE / 2;
 static_assert(NWAVE % DMA_WAVES == 0 && (16 + TN / 16) % DMA_WAVES == 0 && 16 % DMA_WAVES == 0, "DMA waves");
 constexpr int DMA_PER_STAGE = (16 + TN / 16) / DMA_WAVES;  // pieces per DMA wave per stage
-template <bool KN>
+template <bool KN, bool COH = false>
 __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0, int q) {
   const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
@@ -1112,33 +1134,34 @@ __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + (q < QA ? 0 : HALF_A) + I * 1024);
   if (q < QA) {
     const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    dma16(opA + (k0 >> 5) * lda + row * 64 + g * 16, dst);
+    dma16<COH>(opA + (k0 >> 5) * lda + row * 64 + g * 16, dst);
   } else if constexpr (!KN) {
     const int row = 16 * I + (i >> 2), g = (i & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    dma16(opB + (k0 >> 5) * ldb + row * 64 + g * 16, dst);
+    dma16<COH>(opB + (k0 >> 5) * ldb + row * 64 + g * 16, dst);
   } else {
     constexpr int RPP = 1024 / KROW;  // k-rows per piece
     const int kr = RPP * I + i / (64 / RPP), g = (i % (64 / RPP)) ^ ((kr & 3) << 2);
-    dma16(opB + (g >> 2) * ldb + (k0 + kr) * 64 + (g & 3) * 16, dst);
+    dma16<COH>(opB + (g >> 2) * ldb + (k0 + kr) * 64 + (g & 3) * 16, dst);
   }
 }
 // The same piece q of a stage-sized (32 KB) contiguous block at src: stage
 // byte offset (q < 4 ? 0 : 16 KB) + 1 KB (w + 4 (q % 4)) for DMA wave w,
 // the offset it also has at src (the update's low bytes of X, prefetched
 // through the ring in the k loop's last passes).
+template <bool COH = false>
 __device__ __forceinline__ void dma_block_piece(char* st, const char* src, int q) {
   const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
   constexpr int QA = 16 / DMA_WAVES;
   const int off = (q < QA ? 0 : HALF_A) + (w + DMA_WAVES * (q < QA ? q : q - QA)) * 1024;
   const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + off);
-  dma16(src + off + i * 16, dst);
+  dma16<COH>(src + off + i * 16, dst);
 }
 static_assert(HALF_A == 16384 && STAGE == 32768, "the low-byte prefetch fills whole stages");
-template <bool KN>
+template <bool KN, bool COH = false>
 __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
                                           int64_t ldb, int64_t k0) {
 #pragma unroll
-  for (int q = 0; q < DMA_PER_STAGE; ++q) dma_piece<KN>(st, opA, lda, opB, ldb, k0, q);
+  for (int q = 0; q < DMA_PER_STAGE; ++q) dma_piece<KN, COH>(st, opA, lda, opB, ldb, k0, q);
 }
 
 template <int OP>
@@ -1368,7 +1391,7 @@ __device__ __forceinline__ void kstep_diag(f32x16_t (&acc)[4][2], const Frag& fm
 // its two k-steps) carrying the row operand only (opA, panel stride lda).
 // FOLD (poly): block column j also adds f A at its accumulator positions
 // while stage fs[j] is resident (the stage holding its 32 columns as k).
-template <int OP, int ROLE, bool FOLD>
+template <int OP, int ROLE, bool FOLD, bool COH = false>
 __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, const char* opA, int64_t lda,
                                            int nst, bool dma_wave, const DiagGeo& geo, int fs0, int fs1,
                                            float f) {
@@ -1380,10 +1403,10 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
   for (int p = 0; p < NS - 2; ++p)
 #pragma unroll
     for (int q = 0; q < DPS; ++q)
-      if (dma_wave) dma_piece<false>(lds + p * STAGE, opA, lda, opA, lda, int64_t(p) * KS, q);
+      if (dma_wave) dma_piece<false, COH>(lds + p * STAGE, opA, lda, opA, lda, int64_t(p) * KS, q);
 #pragma unroll
   for (int q = 0; q < H; ++q)
-    if (dma_wave) dma_piece<false>(lds + (NS - 2) * STAGE, opA, lda, opA, lda, int64_t(NS - 2) * KS, q);
+    if (dma_wave) dma_piece<false, COH>(lds + (NS - 2) * STAGE, opA, lda, opA, lda, int64_t(NS - 2) * KS, q);
   MUON_WAIT_VMCNT(DPS * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
   asm volatile("s_barrier" ::: "memory");
   constexpr int NA = R::NR0 > R::NR1 ? R::NR0 : R::NR1;
@@ -1403,7 +1426,7 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
       kstep_diag<OP, ROLE>(acc, f0, f1, lds + cur * STAGE, 1, geo, [&](int c) {
-        if (dma_wave) dma_piece<false>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c);
+        if (dma_wave) dma_piece<false, COH>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c);
       });
     }
     MUON_WAIT_VMCNT(DPS * (NS - 3));
@@ -1411,7 +1434,7 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
     {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
       kstep_diag<OP, ROLE>(acc, f1, f0, lds + nxt * STAGE, 0, geo, [&](int c) {
-        if (dma_wave) dma_piece<false>(lds + old * STAGE, opA, lda, opA, lda, k3, c);
+        if (dma_wave) dma_piece<false, COH>(lds + old * STAGE, opA, lda, opA, lda, k3, c);
       });
     }
     if constexpr (J >= 0) {
@@ -1443,10 +1466,13 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
 // (n, m). UPDATE: X = a X + B X on all tiles.
 // SK (Gram only): the variant that also runs split tiles and the reduce
 // pass, launched for plans that split Gram tiles.
-template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false>
-__global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
+// One work item (tile) of the 16-bit engine on the workgroup's LDS ring
+// `lds` (LDS_BYTES). The launches below run one item per workgroup; the
+// chained launch (chain16_kernel) runs the items of every step in one
+// launch.
+template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false, bool COH = false>
+__device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, char* lds) {
   using namespace e16;
-  const WorkItem it = P.items[blockIdx.x];
   if (it.mat < 0) return;
   // Matrix record fields read once into registers: re-reading them after a
   // global store would force a reload (the compiler cannot rule out aliasing).
@@ -1467,8 +1493,6 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
     M.keep = wa.keep; M.step = wa.step;
   }
   constexpr bool KN = KIND == UPDATE;
-
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   const int TI = it.a, TJ = it.b;
   const char* opA;
@@ -1541,13 +1565,13 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       constexpr bool FOLD = KIND == POLY;
       if (role == 0) {
         nr0 = DiagRole<0>::NR0, nr1 = DiagRole<0>::NR1;
-        kloop_diag<OP, 0, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 0, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
       } else if (role == 1) {
         nr0 = DiagRole<1>::NR0, nr1 = DiagRole<1>::NR1;
-        kloop_diag<OP, 1, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 1, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
       } else {
         nr0 = DiagRole<2>::NR0, nr1 = DiagRole<2>::NR1;
-        kloop_diag<OP, 2, FOLD>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 2, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
       }
     }
   }
@@ -1559,10 +1583,10 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   // goes out with the first k-step of stage 0)
 #pragma unroll
   for (int p = 0; p < NS - 2; ++p)
-    if (dma_wave) dma_stage<KN>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+    if (dma_wave) dma_stage<KN, COH>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
 #pragma unroll
   for (int q = 0; q < H; ++q)
-    if (dma_wave) dma_piece<KN>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
+    if (dma_wave) dma_piece<KN, COH>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
   MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
   asm volatile("s_barrier" ::: "memory");
   // POLY with c != 0 folds the b A term into the accumulators on the way:
@@ -1597,9 +1621,9 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, [&](int c) {
         if constexpr (TAIL >= 2) {  // stage nst or nst+1: low bytes, second half
-          if (dma_wave) dma_block_piece(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c);
+          if (dma_wave) dma_block_piece<COH>(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c);
         } else {
-          if (dma_wave) dma_piece<KN>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
+          if (dma_wave) dma_piece<KN, COH>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
         }
       });
     }
@@ -1617,9 +1641,9 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, [&](int c) {
         if constexpr (TAIL == 1 || TAIL == 2) {  // stage nst or nst+1: low bytes, first half
-          if (dma_wave) dma_block_piece(lds + old * STAGE, lo_src + (TAIL - 1) * STAGE, c);
+          if (dma_wave) dma_block_piece<COH>(lds + old * STAGE, lo_src + (TAIL - 1) * STAGE, c);
         } else if constexpr (TAIL == 0) {
-          if (dma_wave) dma_piece<KN>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
+          if (dma_wave) dma_piece<KN, COH>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
         }
       });
     }
@@ -1783,7 +1807,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
         const int x = ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
         const uint32_t base = __builtin_amdgcn_readfirstlane(
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + I * 1024);
-        e16::dma16(Am + pidx(m0 + r, n0 + 8 * (sl ^ x), mp) * 2, base);
+        e16::dma16<COH>(Am + pidx(m0 + r, n0 + 8 * (sl ^ x), mp) * 2, base);
       }
       MUON_WAIT_VMCNT(0);
       __syncthreads();
@@ -2071,6 +2095,101 @@ __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   }
 }
 
+template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false>
+__global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
+  __shared__ __attribute__((aligned(16))) char lds[e16::LDS_BYTES];
+  tile16<T, OP, KIND, LAST, SK, X0S>(P, P.items[blockIdx.x], lds);
+}
+
+// ------------------------------------------------------- chained schedule
+// One launch runs every Gram, poly and update tile of all steps (plan.hpp:
+// per-XCD lists, tickets, per-matrix completion counters). All tiles of a
+// matrix run on one XCD, so everything they pass to each other goes through
+// that XCD's L2, which every CU of the XCD shares: a tile's stores have
+// reached it once the wave's vector-memory count is zero, and a reader sees
+// them if it does not take an older copy from its CU's L1. The chained
+// tiles read their operands with device-scope loads (COH), which the L1
+// does not serve from an older copy. (An L1 invalidate is not the tool: the
+// workgroup-scope one need not touch the L1 of a workgroup that sits on one
+// CU, and tiles then read stale lines; the device-scope one also drops the
+// XCD's L2, which cost 10 % of the step.)
+
+// The XCD (accelerator complex die) this workgroup runs on: hardware
+// register XCC_ID, bits 3:0.
+__device__ __forceinline__ int xcc_id() {
+  return static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20));
+}
+
+// A wait is bounded (ChainArgs::wait_ticks of the 100 MHz real-time
+// counter); one that runs out records the fact in the plan's error word and
+// its workgroup skips its item, so a broken schedule ends the launch
+// instead of hanging it.
+__device__ __forceinline__ bool chain_wait(const int32_t* cnt, int32_t need, int32_t* err, uint64_t bound) {
+  if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(2);
+    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > bound) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+}
+
+// One workgroup per ticket: the launch has at least as many workgroups on
+// every XCD (block b runs on XCD b % 8) as that XCD's list holds tickets
+// for all steps; the rest find the list drained and exit.
+__global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, ChainArgs C) {
+  __shared__ __attribute__((aligned(16))) char lds[e16::LDS_BYTES];
+  __shared__ int32_t slot[2];
+  const int x = xcc_id();
+  if (x >= kNumXcd) {
+    if (threadIdx.x == 0) __hip_atomic_store(C.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  int32_t* tick = reinterpret_cast<int32_t*>(P.ws + P.chain_off);
+  int32_t* done = tick + kNumXcd;
+  const int32_t beg = C.beg[x], len = C.beg[x + 1] - beg, total = len * C.steps;
+  if (threadIdx.x == 0) {
+    const int32_t t = __hip_atomic_fetch_add(tick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    if (t < total) {
+      const int32_t step = t / len;
+      const ChainItem ci = C.items[beg + t - step * len];
+      ok = chain_wait(done + ci.mat, step * (ci.kind_n >> 8) + ci.need, C.err, C.wait_ticks);
+    }
+    slot[0] = t;
+    slot[1] = ok ? 1 : 0;
+  }
+  __syncthreads();
+  const int32_t t = __builtin_amdgcn_readfirstlane(slot[0]);
+  if (t >= total || __builtin_amdgcn_readfirstlane(slot[1]) == 0) return;
+  const int32_t step = t / len;
+  const ChainItem ci = C.items[beg + t - step * len];
+  StepArgs Q = P;
+  Q.cur = step & 1;
+  Q.last = step == C.steps - 1 ? 1 : 0;
+  Q.x0_scaled = step == 0 ? 1 : 0;
+  const WorkItem it{ci.mat, ci.ti, ci.tj, 0};
+  const int kind = ci.kind_n & 255;
+  if (kind == MUON_K_GRAM) {
+    tile16<uint16_t, OP_F16, GRAM, false, false, false, true>(Q, it, lds);
+  } else if (kind == MUON_K_POLY) {
+    tile16<uint16_t, OP_F16, POLY, false, false, false, true>(Q, it, lds);
+  } else if (step == 0) {
+    if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, true, true>(Q, it, lds);
+    else tile16<uint16_t, OP_F16, UPDATE, false, false, true, true>(Q, it, lds);
+  } else {
+    if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, false, true>(Q, it, lds);
+    else tile16<uint16_t, OP_F16, UPDATE, false, false, false, true>(Q, it, lds);
+  }
+  // release: every wave's stores have reached L2, then the count goes up
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(done + ci.mat, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // --------------------------------------------------------------- launchers
 
 template <typename T, int OP>
@@ -2111,6 +2230,12 @@ static hipError_t launch_t(int kind, const StepArgs& a, int grid, hipStream_t s)
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_chain(const StepArgs& a, const ChainArgs& c, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(chain16_kernel, dim3(grid), dim3(e16::NTHR), 0, s, a, c);
   return hipGetLastError();
 }
 

@@ -31,9 +31,26 @@ struct StepArgs {
   int64_t tsum_off, tmax_off, x0s_off;  // workspace offsets (see HostPlan)
   float* hint;  // plan memory, per matrix: the largest |u| of the last call (0: none)
   int32_t n_items;  // items of the schedule (kernels whose grid is smaller)
+  // chained schedule: workspace offset of its counters (the scale pass
+  // clears them), -1 without one
+  int64_t chain_off;
+};
+
+// The chained launch (plan.hpp): the lists, their bounds per XCD, the
+// number of steps, the plan word that records a wait past its bound, and
+// that bound.
+struct ChainArgs {
+  const ChainItem* items;
+  int32_t beg[kNumXcd + 1];
+  int32_t steps;
+  int32_t* err;
+  uint64_t wait_ticks;  // bound of one wait, in 100 MHz real-time counter ticks
 };
 
 hipError_t launch_kernel(int kind, muon_dtype dt, const StepArgs& a, int grid, hipStream_t s);
+// All Gram, poly and update tiles of every step in one launch of `grid`
+// workgroups (bf16 sets).
+hipError_t launch_chain(const StepArgs& a, const ChainArgs& c, int grid, hipStream_t s);
 
 // Device address of the current device's fixed scratch array (kScratchBytes,
 // 256-byte aligned), looked up on the first call per device and kept.

@@ -2,6 +2,7 @@
 #include "plan.hpp"
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <numeric>
 
@@ -252,6 +253,123 @@ Schedule place_reduce(const Schedule& gram, const std::vector<WorkItem>& reduce)
   for (int x = 0; x < kNumXcd; ++x)
     for (size_t p = 0; p < lists[x].size(); ++p) s.items[p * kNumXcd + x] = lists[x][p];
   return s;
+}
+
+// Chained schedule (plan.hpp). Item durations are rough estimates in
+// microseconds at full load (one stage of 32 k values takes about 1 us, a
+// diagonal tile's stage about 0.7 us, an epilogue about 5 us); they only
+// order the lists. Returns false (no chain) when the matrices cannot be
+// spread evenly over the XCDs.
+bool build_chain(HostPlan& P, const std::vector<std::vector<std::vector<WorkItem>>>& per) {
+  const int32_t n = static_cast<int32_t>(P.info.size());
+  constexpr int kPhases = 3;
+  const int kind_of[kPhases] = {MUON_K_GRAM, MUON_K_POLY, MUON_K_UPDATE};
+  auto dur = [&](int ph, const WorkItem& w) {
+    const MatInfo& I = P.info[w.mat];
+    const bool diag = ph < 2 && w.a == w.b;
+    const double st = (ph == 0 ? I.np : I.mp) / 32.0;
+    return (diag ? 0.7 : 1.0) * st + 5.0;
+  };
+  std::vector<double> work(n, 0.0);
+  std::vector<std::array<double, kPhases>> longest(n);
+  int32_t nonempty = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    longest[i].fill(0.0);
+    if (P.info[i].m == 0) continue;
+    ++nonempty;
+    for (int ph = 0; ph < kPhases; ++ph)
+      for (const WorkItem& w : per[kind_of[ph]][i]) {
+        work[i] += dur(ph, w);
+        longest[i][ph] = std::max(longest[i][ph], dur(ph, w));
+      }
+  }
+  if (nonempty < kNumXcd) return false;
+  // matrices onto XCDs, heaviest first onto the lightest XCD
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < n; ++i)
+    if (P.info[i].m > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return work[x] > work[y]; });
+  std::vector<double> load(kNumXcd, 0.0);
+  std::vector<std::vector<int32_t>> bins(kNumXcd);
+  double total = 0.0;
+  for (int32_t i : order) {
+    int best = 0;
+    for (int x = 1; x < kNumXcd; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += work[i];
+    bins[best].push_back(i);
+    total += work[i];
+  }
+  if (*std::max_element(load.begin(), load.end()) > kChainMaxImbalance * total / kNumXcd) return false;
+
+  P.chain.clear();
+  for (int x = 0; x < kNumXcd; ++x) {
+    P.chain_beg[x] = static_cast<int32_t>(P.chain.size());
+    // List scheduling of one step on the XCD's CUs: the CU that frees first
+    // takes the next item of the matrix with the longest remaining chain
+    // among those whose current phase is available, else of the matrix
+    // whose phase becomes available first. A phase is available once every
+    // item of the previous one has ended.
+    struct M {
+      int32_t mat, ph = 0;
+      size_t pos = 0;
+      double avail = 0.0, end = 0.0;
+      int32_t need = 0;
+    };
+    std::vector<M> ms;
+    for (int32_t i : bins[x]) ms.push_back(M{i});
+    auto rest = [&](const M& m) {
+      double r = 0.0;
+      for (int ph = m.ph; ph < kPhases; ++ph) r += longest[m.mat][ph];
+      return r;
+    };
+    std::vector<double> cu(kChainCus, 0.0);
+    for (;;) {
+      const size_t c = static_cast<size_t>(std::min_element(cu.begin(), cu.end()) - cu.begin());
+      const double now = cu[c];
+      int pick = -1;
+      for (size_t k = 0; k < ms.size(); ++k) {
+        const M& m = ms[k];
+        if (m.ph >= kPhases) continue;
+        if (pick < 0) {
+          pick = static_cast<int>(k);
+          continue;
+        }
+        const M& b = ms[pick];
+        const bool ra = m.avail <= now, rb = b.avail <= now;
+        if (ra != rb) {
+          if (ra) pick = static_cast<int>(k);
+        } else if (ra ? rest(m) > rest(b) : m.avail < b.avail) {
+          pick = static_cast<int>(k);
+        }
+      }
+      if (pick < 0) break;
+      M& m = ms[pick];
+      const std::vector<WorkItem>& items = per[kind_of[m.ph]][m.mat];
+      const WorkItem& w = items[m.pos++];
+      const double t0 = std::max(now, m.avail), t1 = t0 + dur(m.ph, w);
+      cu[c] = t1;
+      m.end = std::max(m.end, t1);
+      P.chain.push_back(ChainItem{m.mat, static_cast<int16_t>(w.a), static_cast<int16_t>(w.b), m.need, kind_of[m.ph]});
+      if (m.pos == items.size()) {
+        m.need += static_cast<int32_t>(items.size());
+        m.pos = 0;
+        m.avail = m.end;
+        m.end = 0.0;
+        ++m.ph;
+        while (m.ph < kPhases && per[kind_of[m.ph]][m.mat].empty()) ++m.ph;
+      }
+    }
+  }
+  P.chain_beg[kNumXcd] = static_cast<int32_t>(P.chain.size());
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t c = 0;
+    for (int ph = 0; ph < kPhases; ++ph) c += static_cast<int32_t>(per[kind_of[ph]][i].size());
+    P.info[i].chain_n = c;
+  }
+  // each item also carries its matrix's count (one load less before a wait)
+  for (ChainItem& c : P.chain) c.kind_n |= P.info[c.mat].chain_n << 8;
+  return true;
 }
 
 }  // namespace
@@ -524,6 +642,14 @@ muon_status build_plan(const muon_matrix* mats, int32_t n, muon_dtype dtype, Hos
     }
     P.gbeg[P.ngroups][k] = static_cast<int32_t>(P.sched[k].items.size());
     P.whole[k] = P.ngroups == 1 ? P.sched[k] : place_reduce(P.whole[MUON_K_GRAM], reduce_of(-1));
+  }
+  // The chained schedule (bf16 sets; no split Gram tiles, whose partial
+  // sums need a pass of their own)
+  if (bf16 && P.split_parts == 0 && P.x0s_off >= 0 && upd_tiles < int64_t(kChainMaxWaves) * kNumCu &&
+      build_chain(P, per)) {
+    P.chained = true;
+    P.chain_off = take(static_cast<size_t>(kNumXcd + n) * 4);
+    P.ws_bytes = off;
   }
   *out = std::move(P);
   return MUON_OK;

@@ -70,7 +70,7 @@ struct MatInfo {
   int64_t wld;
   float lr_mul, wd_mul;
   int32_t w_vec_ok;  // 16-byte vector access legal for W
-  int32_t pad_;
+  int32_t chain_n;   // chained schedule: Gram + poly + update items per step
 };
 
 // Gram items of bf16 sets: c = 0, or for a tile whose k range is split into
@@ -84,6 +84,34 @@ struct WorkItem {
 struct Schedule {
   std::vector<WorkItem> items;  // launch order; block i runs items[i]; mat < 0 = empty
 };
+
+// Chained schedule (bf16 sets with at least one step): one launch runs the
+// Gram, poly and update tiles of every Newton-Schulz step. All items of a
+// matrix go to one XCD, whose L2 then holds everything the matrix's tiles
+// pass to each other. Each XCD has a list, ordered by a list-scheduling
+// simulation of its CUs (every item after the items it depends on); the
+// workgroups running on an XCD take tickets from its list in order, ticket
+// t meaning item t % len of step t / len. An item waits until its matrix has
+// completed step * chain_n + need items: the Gram tiles of step s wait for
+// the updates of step s - 1, poly for Gram, the update for poly. Waits only
+// reach back to lower tickets, taken by running workgroups, so the launch
+// always progresses.
+struct ChainItem {
+  int32_t mat;
+  int16_t ti, tj;  // tile row and column
+  int32_t need;    // items of the matrix's own step to wait for
+  int32_t kind_n;  // MUON_K_GRAM, MUON_K_POLY or MUON_K_UPDATE | the matrix's chain_n << 8
+};
+constexpr int kChainCus = kNumCu / kNumXcd;  // CUs per XCD
+// Chained only when the matrices spread over the XCDs with the heaviest
+// XCD at most this much above the mean, and when the update launch is less
+// than kChainMaxWaves waves of tiles deep: there the separate launches lose
+// their tails and launch gaps (measured: GPT-2-124M, 5 waves, 3.5 % faster
+// chained; GPT-2-350M, 18 waves, 2 %), while deeper launches have little
+// tail and run faster separately (2048 x 8192 set, 64 waves: 5 % slower
+// chained, the tiles of an XCD then share less of its L2).
+constexpr double kChainMaxImbalance = 1.10;
+constexpr int kChainMaxWaves = 24;
 
 // Sets whose update launch is a few waves of tiles deep are split into
 // groups of matrices that run concurrently on streams of their own, so one
@@ -115,6 +143,13 @@ struct HostPlan {
   // the launch time): partial tiles in the workspace at split_off.
   int32_t split_parts = 0;
   int64_t split_off = -1;
+  // Chained schedule: per-XCD lists, chain[chain_beg[x] .. chain_beg[x + 1]);
+  // workspace at chain_off: one ticket counter per XCD, then one completion
+  // counter per matrix (int32 each, cleared by the scale pass of each call).
+  bool chained = false;
+  std::vector<ChainItem> chain;
+  int32_t chain_beg[kNumXcd + 1] = {};
+  int64_t chain_off = -1;
   size_t ws_bytes = 0;
 };
 

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert mu.muon_abi_version() == 3
+    assert mu.muon_abi_version() == 4
     for code in range(10):
         s = mu.muon_status_str(code)
         assert s and s != "unknown status"
@@ -165,7 +165,16 @@ def expected_ws(shapes, dtype):
         nparts = int(red[:, 3].astype(np.int64).__and__(255).sum()) // 4 if len(red) else 0
         if nparts:
             off = ru(off + nparts * 256 * 256 * 4, 256)
+        # chained schedule: a ticket counter per XCD and a completion
+        # counter per matrix (int32)
+        if len(chain_items(shapes)):
+            off = ru(off + (8 + len(shapes)) * 4, 256)
     return off
+
+
+def chain_items(shapes):
+    """The chained schedule's lists (schedule kind MUON_K_COUNT + 2)."""
+    return mu.muon_schedule_query(shapes, mu.MUON_BF16, 7)
 
 
 def split_reduce_items(shapes):
@@ -289,15 +298,52 @@ def check_schedules(shapes, dtype):
     if dtype == mu.MUON_BF16:
         spans = sorted({(c >> 16, (c >> 16) + (c & 255)) for *_, c in split_reduce_items(shapes)})
         assert all(e0 <= b1 for (_, e0), (b1, _) in zip(spans, spans[1:]))   # disjoint partial slots
+        check_chain(shapes, gram, poly, upd)
+
+
+def check_chain(shapes, gram, poly, upd):
+    """The chained schedule, where the set has one: every Gram, poly and
+    update tile of a step exactly once, all tiles of a matrix on one XCD,
+    each tile's wait count the number of its matrix's tiles in the earlier
+    kernels of the step, and every tile listed after all tiles it waits for
+    (so a workgroup only ever waits for lower tickets)."""
+    ch = chain_items(shapes)
+    if len(ch) == 0:
+        return
+    assert len(split_reduce_items(shapes)) == 0, "split Gram tiles are never chained"
+    mats, tile, xk, need = ch[:, 0], ch[:, 1], ch[:, 2], ch[:, 3]
+    xcd, kind = xk >> 8, xk & 255
+    assert np.all(np.diff(xcd) >= 0) and xcd.min() >= 0 and xcd.max() < 8, "lists in XCD order"
+    assert set(kind.tolist()) <= {2, 3, 4}
+    nonempty = [i for i, (r, c) in enumerate(shapes) if min(r, c) > 0]
+    assert sorted(set(mats.tolist())) == nonempty
+    for i in nonempty:
+        sel = mats == i
+        assert len(set(xcd[sel].tolist())) == 1, "one XCD per matrix"
+        want = {2: gram, 3: poly, 4: upd}
+        counts = {}
+        for k, src in want.items():
+            got = sorted(((t >> 16) & 0xffff, t & 0xffff) for t in tile[sel & (kind == k)])
+            exp = sorted(map(tuple, src[src[:, 0] == i][:, 1:3].tolist()))
+            assert got == exp, (i, k)
+            counts[k] = len(exp)
+        before = {2: 0, 3: counts[2], 4: counts[2] + counts[3]}
+        assert all(need[j] == before[kind[j]] for j in np.flatnonzero(sel))
+        pos = np.flatnonzero(sel)
+        k_of = kind[pos]
+        for k in (3, 4):
+            if np.any(k_of == k):
+                assert pos[k_of < k].max(initial=-1) < pos[k_of == k].min(), "dependencies listed first"
 
 
 def test_schedule_query_kinds(lib):
-    """Kinds 0 .. MUON_K_COUNT + 1 (the split-Gram sums and the scale pass of
-    X0) are queried; anything else is MUON_E_INVALID, before any work."""
+    """Kinds 0 .. MUON_K_COUNT + 2 (the split-Gram sums, the scale pass of X0
+    and the chained schedule) are queried; anything else is MUON_E_INVALID,
+    before any work."""
     shapes = [(200, 333), (768, 768)]
-    for kind in range(7):
+    for kind in range(8):
         mu.muon_schedule_query(shapes, mu.MUON_BF16, kind)
-    for kind in (-1, 7, 100):
+    for kind in (-1, 8, 100):
         with pytest.raises(mu.MuonError) as e:
             mu.muon_schedule_query(shapes, mu.MUON_BF16, kind)
         assert e.value.code == 1
@@ -305,6 +351,27 @@ def test_schedule_query_kinds(lib):
     s = mu.muon_schedule_query(shapes + [(0, 64)], mu.MUON_BF16, 6)
     assert sorted(s[s[:, 0] >= 0][:, 0].tolist()) == [0, 1]
     assert len(mu.muon_schedule_query(shapes, mu.MUON_F32, 6)) == 0
+
+
+def test_chained_schedule_where_the_set_spreads_over_the_xcds(lib):
+    """Chained: bf16 sets of at least eight matrices whose work spreads
+    evenly over the XCDs and whose update launch is under 24 waves of 256
+    tiles (the GPT-2-124M and 350M sets); not: deeper sets (the 2048 x 8192
+    set, 64 waves), fp32 sets, sets of fewer matrices, sets that split Gram
+    tiles."""
+    for name in ("gpt2_124m_matrix_set", "gpt2_350m_matrix_set"):
+        ch = chain_items(list(CONFIGS[name].shapes))
+        assert len(ch) > 0, name
+        per_xcd = np.bincount(ch[:, 2] >> 8, minlength=8)
+        assert per_xcd.max() <= 1.25 * per_xcd.mean(), name
+    assert len(chain_items(list(CONFIGS["wide_2048x8192_powerlaw"].shapes))) == 0
+    assert len(chain_items([(2048, 8192)] * 23)) > 0        # 23 waves
+    assert len(chain_items([(2048, 8192)] * 24)) == 0       # 24 waves
+    assert len(chain_items(list(CONFIGS["gpt2_small_block"].shapes))) == 0
+    assert len(chain_items([(768, 768)] * 7)) == 0
+    assert len(mu.muon_schedule_query([(768, 768)] * 16, mu.MUON_F32, 7)) == 0
+    # one huge matrix beside small ones cannot spread evenly
+    assert len(chain_items([(8192, 8192)] + [(256, 256)] * 8)) == 0
 
 
 def test_gram_schedule_balances_xcds_and_keeps_matrices_together(lib):

@@ -423,9 +423,10 @@ def test_deterministic_odd_and_scale_invariant(dtype):
 
 
 def test_grouped_concurrent_run_matches_timed_whole_set_run():
-    """Large sets run as concurrent groups; with per-kernel timing on, every
-    kernel runs over the whole set in one launch. Same kernels, same tiles:
-    the results must be bitwise equal (momentum buffers included)."""
+    """Without the chained launch, large sets run as concurrent groups; with
+    per-kernel timing on, every kernel runs over the whole set in one launch.
+    Same kernels, same tiles: the results must be bitwise equal (momentum
+    buffers included)."""
     wl = CONFIGS["gpt2_124m_matrix_set"]
     grads = [g.to(DEV) for g in make_gradients(wl, step=9)]
     res = []
@@ -433,6 +434,7 @@ def test_grouped_concurrent_run_matches_timed_whole_set_run():
         bufs = [torch.zeros_like(g) for g in grads]
         outs = [torch.empty_like(g) for g in grads]
         plan = mu.MuonPlan(grads, bufs, outs)
+        plan.set_chained(False)
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
         cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
         plan.set_timing(timing)
@@ -729,17 +731,19 @@ def test_max_elements_orthonormal_rows(tall):
 
 # ------------------------------------------------------------ HIP graphs
 
-def test_graph_capture_replays_match_eager():
-    """A whole step (the GPT-2-124M set: groups of matrices forked onto
-    their own streams and joined back) captured once as a HIP graph: three
-    replays, with eager work and synchronisations in between, give bitwise
-    the outputs and momentum buffers of three eager steps from the same
-    state."""
+@pytest.mark.parametrize("chained", [True, False], ids=["chained", "groups"])
+def test_graph_capture_replays_match_eager(chained):
+    """A whole step of the GPT-2-124M set (the chained launch, or groups of
+    matrices forked onto their own streams and joined back) captured once as
+    a HIP graph: three replays, with eager work and synchronisations in
+    between, give bitwise the outputs and momentum buffers of three eager
+    steps from the same state."""
     wl = CONFIGS["gpt2_124m_matrix_set"]
     grads = [g.to(DEV) for g in make_gradients(wl, step=0)]
     bufs = [torch.zeros_like(g) for g in grads]
     outs = [torch.empty_like(g) for g in grads]
     plan = mu.MuonPlan(grads, bufs, outs)
+    plan.set_chained(chained)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
     cfg = mu.make_config(*wl.coeffs, wl.steps, wl.momentum, wl.nesterov, wl.eps)
     say("graph capture: eager reference")
@@ -771,5 +775,6 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(o, r)
         for b, r in zip(bufs, ref[k][1]):
             assert torch.equal(b, r)
+    assert plan.chain_state() == ((1 if chained else 0), 0)
     del graph
     plan.destroy()
