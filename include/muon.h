@@ -344,7 +344,7 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
  * whether steps of this plan use the chained launch (1) or not (0), and
  * in *error the plan's error word since the last query (0: none; 1: a
  * wait passed its bound; 2: a workgroup ran on a die the schedule does not
- * know), which it clears. */
+ * know; 3: a workgroup found no new tile to take), which it clears. */
 muon_status muon_plan_set_chained(muon_plan* plan, int32_t enable);
 muon_status muon_plan_set_chain_timeout(muon_plan* plan, int64_t microseconds);
 muon_status muon_plan_chain_state(muon_plan* plan, int32_t* chained, int32_t* error);

@@ -293,8 +293,8 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   if (chain) {
     // momentum, the scale pass (which clears the chain's counters) and the
     // rewrite over the whole set (the one-group schedules), then every Gram,
-    // poly and update tile of all steps in one launch with a workgroup per
-    // ticket of the longest XCD list
+    // poly and update tile of all steps in one persistent launch of one
+    // workgroup per CU
     for (int kind : {int(MUON_K_MOMENTUM), int(MUON_K_NORMALIZE)}) {
       const Slot o = slot_of(kind);
       for (int k = 0; k < o.n; ++k) {
@@ -309,14 +309,11 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     c.steps = cfg->steps;
     c.err = p->d_err;
     c.wait_ticks = static_cast<uint64_t>(p->chain_wait_us) * 100u;
-    int64_t longest = 0;
     for (int x = 0; x <= muon::kNumXcd; ++x) c.beg[x] = H.chain_beg[x];
-    for (int x = 0; x < muon::kNumXcd; ++x)
-      longest = std::max<int64_t>(longest, int64_t(H.chain_beg[x + 1] - H.chain_beg[x]) * cfg->steps);
     a.cur = 0;
     a.last = 0;
     a.x0_scaled = 1;
-    if (muon::launch_chain(a, c, static_cast<int>(longest * muon::kNumXcd), s) != hipSuccess) return MUON_E_LAUNCH;
+    if (muon::launch_chain(a, c, muon::kNumCu, s) != hipSuccess) return MUON_E_LAUNCH;
     return MUON_OK;
   }
   if (H.ngroups == 1) return sequence(0, s);

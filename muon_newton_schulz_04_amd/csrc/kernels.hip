@@ -1126,8 +1126,8 @@ static_assert(NWAVE % DMA_WAVES == 0 && (16 + TN / 16) % DMA_WAVES == 0 && 16 % 
 constexpr int DMA_PER_STAGE = (16 + TN / 16) / DMA_WAVES;  // pieces per DMA wave per stage
 template <bool KN, bool COH = false>
 __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda, const char* opB,
-                                          int64_t ldb, int64_t k0, int q) {
-  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+                                          int64_t ldb, int64_t k0, int q, uint32_t tid) {
+  const int w = tid >> 6, i = tid & 63;
   constexpr int QA = 16 / DMA_WAVES;  // row-operand pieces per wave
   const int I = w + DMA_WAVES * (q < QA ? q : q - QA);
   const uint32_t dst = __builtin_amdgcn_readfirstlane(
@@ -1149,8 +1149,8 @@ __device__ __forceinline__ void dma_piece(char* st, const char* opA, int64_t lda
 // the offset it also has at src (the update's low bytes of X, prefetched
 // through the ring in the k loop's last passes).
 template <bool COH = false>
-__device__ __forceinline__ void dma_block_piece(char* st, const char* src, int q) {
-  const int w = threadIdx.x >> 6, i = threadIdx.x & 63;
+__device__ __forceinline__ void dma_block_piece(char* st, const char* src, int q, uint32_t tid) {
+  const int w = tid >> 6, i = tid & 63;
   constexpr int QA = 16 / DMA_WAVES;
   const int off = (q < QA ? 0 : HALF_A) + (w + DMA_WAVES * (q < QA ? q : q - QA)) * 1024;
   const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + off);
@@ -1159,9 +1159,9 @@ __device__ __forceinline__ void dma_block_piece(char* st, const char* src, int q
 static_assert(HALF_A == 16384 && STAGE == 32768, "the low-byte prefetch fills whole stages");
 template <bool KN, bool COH = false>
 __device__ __forceinline__ void dma_stage(char* st, const char* opA, int64_t lda, const char* opB,
-                                          int64_t ldb, int64_t k0) {
+                                          int64_t ldb, int64_t k0, uint32_t tid) {
 #pragma unroll
-  for (int q = 0; q < DMA_PER_STAGE; ++q) dma_piece<KN, COH>(st, opA, lda, opB, ldb, k0, q);
+  for (int q = 0; q < DMA_PER_STAGE; ++q) dma_piece<KN, COH>(st, opA, lda, opB, ldb, k0, q, tid);
 }
 
 template <int OP>
@@ -1180,15 +1180,15 @@ struct Frag {
 // Fragment reads of k-step ks (0/1) of the stage at `st`: row-operand block
 // i, column-operand block j. The reads stay in flight until the MFMAs that
 // use them.
-__device__ __forceinline__ void frag_load_a(Frag& f, const char* st, int ks, int wm, int i) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void frag_load_a(Frag& f, const char* st, int ks, int wm, int i, uint32_t tid) {
+  const int lane = tid & 63;
   const int ch = ks * 2 + (lane >> 5);  // 16-byte k chunk of this lane half
   f.a[i] = *reinterpret_cast<const u32x4*>(st + off_r(wm * 128 + i * 32 + (lane & 31), ch));
 }
 template <bool KN>
-__device__ __forceinline__ void frag_load_b(Frag& f, const char* st, int ks, int wn, int j) {
+__device__ __forceinline__ void frag_load_b(Frag& f, const char* st, int ks, int wn, int j, uint32_t tid) {
   const char* sB = st + HALF_A;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid & 63;
   if constexpr (KN) {
     const int s = lane & 15, h = lane >> 4;  // 16-lane group h
     const int krow = ks * 16 + (h >> 1) * 8 + (s >> 2);
@@ -1206,11 +1206,11 @@ __device__ __forceinline__ void frag_load_b(Frag& f, const char* st, int ks, int
   }
 }
 template <bool KN>
-__device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int wm, int wn) {
+__device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int wm, int wn, uint32_t tid) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) frag_load_b<KN>(f, st, ks, wn, j);
+  for (int j = 0; j < 2; ++j) frag_load_b<KN>(f, st, ks, wn, j, tid);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) frag_load_a(f, st, ks, wm, i);
+  for (int i = 0; i < 4; ++i) frag_load_a(f, st, ks, wm, i, tid);
 }
 
 // One k-step with DMA spread over it: the 8 MFMAs of fragment set fm, the
@@ -1221,7 +1221,7 @@ __device__ __forceinline__ void frag_load(Frag& f, const char* st, int ks, int w
 // between the chunks.
 template <int OP, bool KN, int NCH, typename D>
 __device__ __forceinline__ void kstep_dma(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
-                                          const char* st, int ks, int wm, int wn, D&& dma) {
+                                          const char* st, int ks, int wm, int wn, uint32_t tid, D&& dma) {
   static_assert(4 % NCH == 0, "row blocks per chunk");
   constexpr int IPC = 4 / NCH;
 #pragma unroll
@@ -1235,10 +1235,10 @@ __device__ __forceinline__ void kstep_dma(f32x16_t (&acc)[4][2], const Frag& fm,
         acc[c * IPC + ii][j] = mfma<OP>(fm.b[j], fm.a[c * IPC + ii], acc[c * IPC + ii][j]);
     if (c == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) frag_load_b<KN>(fl, st, ks, wn, j);
+      for (int j = 0; j < 2; ++j) frag_load_b<KN>(fl, st, ks, wn, j, tid);
     }
 #pragma unroll
-    for (int ii = 0; ii < IPC; ++ii) frag_load_a(fl, st, ks, wm, c * IPC + ii);
+    for (int ii = 0; ii < IPC; ++ii) frag_load_a(fl, st, ks, wm, c * IPC + ii, tid);
     constexpr int NM = 2 * IPC;
     const int nr = IPC + (c == 0 ? (KN ? 4 : 2) : 0);
 #pragma unroll
@@ -1288,8 +1288,9 @@ __device__ __forceinline__ float sub_h(float x, uint32_t h) {
 // row-operand half of the stage at `st`, which holds A[m][k] for the 32 k
 // that are these n (the caller picks the stage).
 template <int OP, int J, int NR>
-__device__ __forceinline__ void fold_rows(f32x16_t (&acc)[4][2], const char* st, int rbase, float f) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+__device__ __forceinline__ void fold_rows(f32x16_t (&acc)[4][2], const char* st, int rbase, float f,
+                                          uint32_t tid) {
+  const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     u32x2 v[4];
@@ -1335,8 +1336,8 @@ __device__ __forceinline__ DiagGeo diag_geo(int wave) {
 }
 
 // A fragment of 32 rows (row0 ..) of k-step ks from the row-operand half.
-__device__ __forceinline__ u32x4 frag_rows(const char* st, int ks, int row0) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ u32x4 frag_rows(const char* st, int ks, int row0, uint32_t tid) {
+  const int lane = tid & 63;
   return *reinterpret_cast<const u32x4*>(st + off_r(row0 + (lane & 31), ks * 2 + (lane >> 5)));
 }
 
@@ -1345,7 +1346,7 @@ __device__ __forceinline__ u32x4 frag_rows(const char* st, int ks, int row0) {
 // stage at `st`), interleaved.
 template <int OP, int ROLE, int C>
 __device__ __forceinline__ void kchunk_diag(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
-                                            const char* st, int ks, const DiagGeo& geo) {
+                                            const char* st, int ks, const DiagGeo& geo, uint32_t tid) {
   using R = DiagRole<ROLE>;
   constexpr int NM = R::NR0 + R::NR1;
   constexpr int NA = R::NR0 > R::NR1 ? R::NR0 : R::NR1;
@@ -1359,8 +1360,8 @@ __device__ __forceinline__ void kchunk_diag(f32x16_t (&acc)[4][2], const Frag& f
   }
 #pragma unroll
   for (int t = rb; t < re; ++t) {
-    if (t < R::NJ) fl.b[t] = frag_rows(st, ks, t == 0 ? geo.cb0 : geo.cb1);
-    else fl.a[t - R::NJ] = frag_rows(st, ks, geo.rbase + 32 * (t - R::NJ));
+    if (t < R::NJ) fl.b[t] = frag_rows(st, ks, t == 0 ? geo.cb0 : geo.cb1, tid);
+    else fl.a[t - R::NJ] = frag_rows(st, ks, geo.rbase + 32 * (t - R::NJ), tid);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -1370,13 +1371,13 @@ __device__ __forceinline__ void kchunk_diag(f32x16_t (&acc)[4][2], const Frag& f
 }
 template <int OP, int ROLE, typename D>
 __device__ __forceinline__ void kstep_diag(f32x16_t (&acc)[4][2], const Frag& fm, Frag& fl,
-                                           const char* st, int ks, const DiagGeo& geo, D&& dma) {
+                                           const char* st, int ks, const DiagGeo& geo, uint32_t tid, D&& dma) {
   __builtin_amdgcn_sched_barrier(0);
   dma(0);
-  kchunk_diag<OP, ROLE, 0>(acc, fm, fl, st, ks, geo);
+  kchunk_diag<OP, ROLE, 0>(acc, fm, fl, st, ks, geo, tid);
   __builtin_amdgcn_sched_barrier(0);
   dma(1);
-  kchunk_diag<OP, ROLE, 1>(acc, fm, fl, st, ks, geo);
+  kchunk_diag<OP, ROLE, 1>(acc, fm, fl, st, ks, geo, tid);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -1394,7 +1395,7 @@ __device__ __forceinline__ void kstep_diag(f32x16_t (&acc)[4][2], const Frag& fm
 template <int OP, int ROLE, bool FOLD, bool COH = false>
 __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, const char* opA, int64_t lda,
                                            int nst, bool dma_wave, const DiagGeo& geo, int fs0, int fs1,
-                                           float f) {
+                                           float f, uint32_t tid) {
   using R = DiagRole<ROLE>;
   constexpr int DPS = 16 / DMA_WAVES;  // row-operand pieces per DMA wave per stage
   constexpr int H = DPS / 2;           // pieces per k-step
@@ -1403,18 +1404,18 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
   for (int p = 0; p < NS - 2; ++p)
 #pragma unroll
     for (int q = 0; q < DPS; ++q)
-      if (dma_wave) dma_piece<false, COH>(lds + p * STAGE, opA, lda, opA, lda, int64_t(p) * KS, q);
+      if (dma_wave) dma_piece<false, COH>(lds + p * STAGE, opA, lda, opA, lda, int64_t(p) * KS, q, tid);
 #pragma unroll
   for (int q = 0; q < H; ++q)
-    if (dma_wave) dma_piece<false, COH>(lds + (NS - 2) * STAGE, opA, lda, opA, lda, int64_t(NS - 2) * KS, q);
+    if (dma_wave) dma_piece<false, COH>(lds + (NS - 2) * STAGE, opA, lda, opA, lda, int64_t(NS - 2) * KS, q, tid);
   MUON_WAIT_VMCNT(DPS * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
   asm volatile("s_barrier" ::: "memory");
   constexpr int NA = R::NR0 > R::NR1 ? R::NR0 : R::NR1;
   Frag f0, f1;
-  f0.b[0] = frag_rows(lds, 0, geo.cb0);
-  if constexpr (R::NJ == 2) f0.b[1] = frag_rows(lds, 0, geo.cb1);
+  f0.b[0] = frag_rows(lds, 0, geo.cb0, tid);
+  if constexpr (R::NJ == 2) f0.b[1] = frag_rows(lds, 0, geo.cb1, tid);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) f0.a[i] = frag_rows(lds, 0, geo.rbase + 32 * i);
+  for (int i = 0; i < NA; ++i) f0.a[i] = frag_rows(lds, 0, geo.rbase + 32 * i, tid);
   int cur = 0;
   // one pass over stage g; J >= 0 also folds block column J (see the other
   // tiles' loop: the fold passes are loops of their own)
@@ -1425,21 +1426,21 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
     {
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
-      kstep_diag<OP, ROLE>(acc, f0, f1, lds + cur * STAGE, 1, geo, [&](int c) {
-        if (dma_wave) dma_piece<false, COH>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c);
+      kstep_diag<OP, ROLE>(acc, f0, f1, lds + cur * STAGE, 1, geo, tid, [&](int c) {
+        if (dma_wave) dma_piece<false, COH>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c, tid);
       });
     }
     MUON_WAIT_VMCNT(DPS * (NS - 3));
     asm volatile("s_barrier" ::: "memory");
     {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
-      kstep_diag<OP, ROLE>(acc, f1, f0, lds + nxt * STAGE, 0, geo, [&](int c) {
-        if (dma_wave) dma_piece<false, COH>(lds + old * STAGE, opA, lda, opA, lda, k3, c);
+      kstep_diag<OP, ROLE>(acc, f1, f0, lds + nxt * STAGE, 0, geo, tid, [&](int c) {
+        if (dma_wave) dma_piece<false, COH>(lds + old * STAGE, opA, lda, opA, lda, k3, c, tid);
       });
     }
     if constexpr (J >= 0) {
       __builtin_amdgcn_sched_barrier(0);
-      fold_rows<OP, J, J == 0 ? R::NR0 : R::NR1>(acc, lds + cur * STAGE, geo.rbase, f);
+      fold_rows<OP, J, J == 0 ? R::NR0 : R::NR1>(acc, lds + cur * STAGE, geo.rbase, f, tid);
     }
     cur = nxt;
   };
@@ -1470,8 +1471,15 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
 // `lds` (LDS_BYTES). The launches below run one item per workgroup; the
 // chained launch (chain16_kernel) runs the items of every step in one
 // launch.
-template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false, bool COH = false>
-__device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, char* lds) {
+// at_epilogue() runs once the k loop is done, before the epilogue (the
+// chained launch fetches its next ticket there).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false, bool COH = false,
+          typename Hook = NoHook>
+__device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, char* lds, uint32_t tid,
+                                       Hook at_epilogue = Hook{}) {
   using namespace e16;
   if (it.mat < 0) return;
   // Matrix record fields read once into registers: re-reading them after a
@@ -1523,7 +1531,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
     K = M.mp;
   }
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const bool dma_wave = wave < DMA_WAVES;  // (waves 0 .. 3 sit on the four SIMDs)
   f32x16_t acc[4][2];
@@ -1565,13 +1573,13 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
       constexpr bool FOLD = KIND == POLY;
       if (role == 0) {
         nr0 = DiagRole<0>::NR0, nr1 = DiagRole<0>::NR1;
-        kloop_diag<OP, 0, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 0, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb, tid);
       } else if (role == 1) {
         nr0 = DiagRole<1>::NR0, nr1 = DiagRole<1>::NR1;
-        kloop_diag<OP, 1, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 1, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb, tid);
       } else {
         nr0 = DiagRole<2>::NR0, nr1 = DiagRole<2>::NR1;
-        kloop_diag<OP, 2, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb);
+        kloop_diag<OP, 2, FOLD, COH>(acc, lds, opA, lda, nst, dma_wave, geo, f0s, f1s, fb, tid);
       }
     }
   }
@@ -1583,10 +1591,10 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   // goes out with the first k-step of stage 0)
 #pragma unroll
   for (int p = 0; p < NS - 2; ++p)
-    if (dma_wave) dma_stage<KN, COH>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS);
+    if (dma_wave) dma_stage<KN, COH>(lds + p * STAGE, opA, lda, opB, ldb, int64_t(p) * KS, tid);
 #pragma unroll
   for (int q = 0; q < H; ++q)
-    if (dma_wave) dma_piece<KN, COH>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q);
+    if (dma_wave) dma_piece<KN, COH>(lds + (NS - 2) * STAGE, opA, lda, opB, ldb, int64_t(NS - 2) * KS, q, tid);
   MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3) + H);  // stage 0 landed (this wave's pieces)
   asm volatile("s_barrier" ::: "memory");
   // POLY with c != 0 folds the b A term into the accumulators on the way:
@@ -1596,7 +1604,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   const int bias0 = fold ? TJ * (TN / KS) + wn * (64 / KS) : -2;
   const float fb = fold ? P.b / P.c : 0.f;
   Frag f0, f1;
-  frag_load<KN>(f0, lds, 0, wm, wn);
+  frag_load<KN>(f0, lds, 0, wm, wn, tid);
   int cur = 0;  // ring slot of stage g
   // The update's low bytes of X (64 KB per tile, contiguous) take the place
   // of stages nst and nst+1 (slots nst % NS and (nst+1) % NS), which
@@ -1619,11 +1627,11 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
       // barrier; the first half went out then)
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
-      kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, [&](int c) {
+      kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, tid, [&](int c) {
         if constexpr (TAIL >= 2) {  // stage nst or nst+1: low bytes, second half
-          if (dma_wave) dma_block_piece<COH>(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c);
+          if (dma_wave) dma_block_piece<COH>(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c, tid);
         } else {
-          if (dma_wave) dma_piece<KN, COH>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c);
+          if (dma_wave) dma_piece<KN, COH>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c, tid);
         }
       });
     }
@@ -1639,11 +1647,11 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
     // values are unused)
     {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
-      kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, [&](int c) {
+      kstep_dma<OP, KN, H>(acc, f1, f0, lds + nxt * STAGE, 0, wm, wn, tid, [&](int c) {
         if constexpr (TAIL == 1 || TAIL == 2) {  // stage nst or nst+1: low bytes, first half
-          if (dma_wave) dma_block_piece<COH>(lds + old * STAGE, lo_src + (TAIL - 1) * STAGE, c);
+          if (dma_wave) dma_block_piece<COH>(lds + old * STAGE, lo_src + (TAIL - 1) * STAGE, c, tid);
         } else if constexpr (TAIL == 0) {
-          if (dma_wave) dma_piece<KN, COH>(lds + old * STAGE, opA, lda, opB, ldb, k3, c);
+          if (dma_wave) dma_piece<KN, COH>(lds + old * STAGE, opA, lda, opB, ldb, k3, c, tid);
         }
       });
     }
@@ -1651,7 +1659,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
       // (stage g stays in its slot until every wave has passed the next
       // barrier)
       __builtin_amdgcn_sched_barrier(0);
-      fold_rows<OP, J, 4>(acc, lds + cur * STAGE, wm * 128, fb);
+      fold_rows<OP, J, 4>(acc, lds + cur * STAGE, wm * 128, fb, tid);
     }
     cur = nxt;
   };
@@ -1686,6 +1694,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   constexpr int CPR = TN / 8;    // 16-byte chunks per staged row
   const int m0 = TI * TM, n0 = TJ * TN;  // tile origin
   __builtin_amdgcn_sched_barrier(0);
+  at_epilogue();
   __syncthreads();  // every wave is done reading the operand stages
 
   // Split Gram tiles: a part stores its fp32 accumulators in accumulator
@@ -1738,7 +1747,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   auto rows_out = [&](auto&& fn) {
 #pragma unroll 4
     for (int q = 0; q < TM * CPR / NTHR; ++q) {
-      const int r = q * (NTHR / CPR) + threadIdx.x / CPR, c = threadIdx.x % CPR;
+      const int r = q * (NTHR / CPR) + tid / CPR, c = tid % CPR;
       fn(m0 + r, n0 + 8 * c, *reinterpret_cast<const uint4*>(lds + soff(r, c)));
     }
   };
@@ -1862,7 +1871,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
 #pragma unroll
               for (int u = 0; u < 4; ++u)
                 x[q][u] = *reinterpret_cast<const f32x4_t*>(qbase + int64_t(q0 + q) * (TM * TN * 4) +
-                                                            ((h * 4 + u) * NTHR + threadIdx.x) * 16);
+                                                            ((h * 4 + u) * NTHR + tid) * 16);
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             if (q0 + q < S)
@@ -1871,7 +1880,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int o = ((h * 4 + u) * NTHR + threadIdx.x) * 16;
+          const int o = ((h * 4 + u) * NTHR + tid) * 16;
           const int wl = o >> 15, blk = (o >> 12) & 7, ln = (o >> 6) & 63, v = (o >> 4) & 3;
           const int r = qr * 128 + 32 * (blk >> 1) + (ln & 31);
           const int c = (2 * qc + wl) * 8 + 4 * (blk & 1) + v;
@@ -2098,7 +2107,7 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
 template <typename T, int OP, int KIND, bool LAST, bool SK = false, bool X0S = false>
 __global__ __launch_bounds__(e16::NTHR, 1) void gemm16_kernel(StepArgs P) {
   __shared__ __attribute__((aligned(16))) char lds[e16::LDS_BYTES];
-  tile16<T, OP, KIND, LAST, SK, X0S>(P, P.items[blockIdx.x], lds);
+  tile16<T, OP, KIND, LAST, SK, X0S>(P, P.items[blockIdx.x], lds, threadIdx.x);
 }
 
 // ------------------------------------------------------- chained schedule
@@ -2137,9 +2146,17 @@ __device__ __forceinline__ bool chain_wait(const int32_t* cnt, int32_t need, int
   }
 }
 
-// One workgroup per ticket: the launch has at least as many workgroups on
-// every XCD (block b runs on XCD b % 8) as that XCD's list holds tickets
-// for all steps; the rest find the list drained and exit.
+// Persistent: one workgroup per CU; each takes tickets from its XCD's list
+// until the list is drained. The ticket for the next pass is fetched when
+// the current tile's k loop is done (its epilogue hides the atomic's
+// latency; fetched earlier, a long tile would hold a ticket that others
+// wait for), by a lane of wave 4 (waves 0 .. 3 issue the ring's DMA and
+// count it with their vector-memory counters, which must not hold anything
+// else). A workgroup holding a ticket is always running, and it finishes
+// its current tile before it waits for the next one, so the lowest
+// unfinished ticket is always some workgroup's current tile and its inputs
+// are done.
+constexpr int kChainOwner = 4 * 64;  // the thread that takes tickets and waits
 __global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, ChainArgs C) {
   __shared__ __attribute__((aligned(16))) char lds[e16::LDS_BYTES];
   __shared__ int32_t slot[2];
@@ -2151,43 +2168,62 @@ __global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, Chain
   int32_t* tick = reinterpret_cast<int32_t*>(P.ws + P.chain_off);
   int32_t* done = tick + kNumXcd;
   const int32_t beg = C.beg[x], len = C.beg[x + 1] - beg, total = len * C.steps;
-  if (threadIdx.x == 0) {
-    const int32_t t = __hip_atomic_fetch_add(tick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool ok = true;
-    if (t < total) {
-      const int32_t step = t / len;
-      const ChainItem ci = C.items[beg + t - step * len];
-      ok = chain_wait(done + ci.mat, step * (ci.kind_n >> 8) + ci.need, C.err, C.wait_ticks);
+  int32_t next = 0, prev = -1;  // (owner) the tickets of the next and the last pass
+  if (threadIdx.x == kChainOwner)
+    next = __hip_atomic_fetch_add(tick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if (threadIdx.x == kChainOwner) {
+      const int32_t t = next;
+      bool ok = true;
+      if (t <= prev) {  // tickets only grow: a pass without a fetch ends the loop
+        __hip_atomic_store(C.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = false;
+      } else if (t < total) {
+        const int32_t step = t / len;
+        const ChainItem ci = C.items[beg + t - step * len];
+        ok = chain_wait(done + ci.mat, step * (ci.kind_n >> 8) + ci.need, C.err, C.wait_ticks);
+      }
+      prev = t;
+      slot[0] = t;
+      slot[1] = ok ? 1 : 0;
     }
-    slot[0] = t;
-    slot[1] = ok ? 1 : 0;
+    __syncthreads();
+    const int32_t t = __builtin_amdgcn_readfirstlane(slot[0]);
+    if (t >= total || __builtin_amdgcn_readfirstlane(slot[1]) == 0) break;
+    // The lane index through an empty move: a value the compiler cannot
+    // carry from one pass to the next, so the tile's lane arithmetic is
+    // recomputed per tile instead of being held in registers across passes.
+    uint32_t tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(static_cast<uint32_t>(threadIdx.x)));
+    const int32_t step = t / len;
+    const ChainItem ci = C.items[beg + t - step * len];
+    StepArgs Q = P;
+    Q.cur = step & 1;
+    Q.last = step == C.steps - 1 ? 1 : 0;
+    Q.x0_scaled = step == 0 ? 1 : 0;
+    const WorkItem it{ci.mat, ci.ti, ci.tj, 0};
+    const int kind = ci.kind_n & 255;
+    auto fetch = [&]() {
+      if (threadIdx.x == kChainOwner)
+        next = __hip_atomic_fetch_add(tick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (kind == MUON_K_GRAM) {
+      tile16<uint16_t, OP_F16, GRAM, false, false, false, true>(Q, it, lds, tid, fetch);
+    } else if (kind == MUON_K_POLY) {
+      tile16<uint16_t, OP_F16, POLY, false, false, false, true>(Q, it, lds, tid, fetch);
+    } else if (step == 0) {
+      if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, true, true>(Q, it, lds, tid, fetch);
+      else tile16<uint16_t, OP_F16, UPDATE, false, false, true, true>(Q, it, lds, tid, fetch);
+    } else {
+      if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, false, true>(Q, it, lds, tid, fetch);
+      else tile16<uint16_t, OP_F16, UPDATE, false, false, false, true>(Q, it, lds, tid, fetch);
+    }
+    // release: every wave's stores have reached L2, then the count goes up
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == kChainOwner)
+      __hip_atomic_fetch_add(done + ci.mat, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  const int32_t t = __builtin_amdgcn_readfirstlane(slot[0]);
-  if (t >= total || __builtin_amdgcn_readfirstlane(slot[1]) == 0) return;
-  const int32_t step = t / len;
-  const ChainItem ci = C.items[beg + t - step * len];
-  StepArgs Q = P;
-  Q.cur = step & 1;
-  Q.last = step == C.steps - 1 ? 1 : 0;
-  Q.x0_scaled = step == 0 ? 1 : 0;
-  const WorkItem it{ci.mat, ci.ti, ci.tj, 0};
-  const int kind = ci.kind_n & 255;
-  if (kind == MUON_K_GRAM) {
-    tile16<uint16_t, OP_F16, GRAM, false, false, false, true>(Q, it, lds);
-  } else if (kind == MUON_K_POLY) {
-    tile16<uint16_t, OP_F16, POLY, false, false, false, true>(Q, it, lds);
-  } else if (step == 0) {
-    if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, true, true>(Q, it, lds);
-    else tile16<uint16_t, OP_F16, UPDATE, false, false, true, true>(Q, it, lds);
-  } else {
-    if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, false, true>(Q, it, lds);
-    else tile16<uint16_t, OP_F16, UPDATE, false, false, false, true>(Q, it, lds);
-  }
-  // release: every wave's stores have reached L2, then the count goes up
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(done + ci.mat, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------- launchers
