@@ -52,7 +52,8 @@ def kernel_work(shapes, steps, dtype):
     the momentum pass, and the normalise slot only reduces per-tile sums (no
     matrix bytes; its rewrites, when the plan's guess of X0's power of two
     was wrong, are not algorithmic work). The Newton-Schulz kernels run
-    `steps` times; the last update writes `out` instead of X's parts."""
+    `steps` times; the last update writes `out` instead of X's parts. `chain`
+    (the chained launch) is the Gram, poly and update work together."""
     es = 2 if dtype == "bf16" else 4
     xb = 3 if dtype == "bf16" else 4        # X per element: hi + lo byte, or fp32
     xop = 2 if dtype == "bf16" else 4       # X as a matrix-core operand (high half)
@@ -74,6 +75,7 @@ def kernel_work(shapes, steps, dtype):
         for t in range(steps):
             out = es if t == steps - 1 else xb                             # write out, or X
             w["update"][1] += es * mm + xb * mn + out * mn                 # read B, X
+    w["chain"] = [w["gram"][0] + w["poly"][0] + w["update"][0], w["gram"][1] + w["poly"][1] + w["update"][1]]
     return {k: (v[0], v[1]) for k, v in w.items()}
 
 
@@ -213,7 +215,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 30 warm-up steps: after an idle pause the first step runs at the idle
+    # clock, the next ones at a clock the power controller has pulled far
+    # down, and the step time settles over about 20 to 30 steps (measured on
+    # the GPT-2-124M set: 1.52 ms, then 2.2 ms, falling to 1.60 ms)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="gpt2_124m_matrix_set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -335,14 +341,28 @@ def main():
     if chain_err:
         raise SystemExit(f"bench: chained launch reported error {chain_err}")
 
-    # second pass of the same length with per-launch HIP events
-    plan.set_timing(True)
+    # second pass of the same length with per-launch HIP events: each
+    # kernel over the whole set in its own launch
+    plan.set_timing(1)
     plan.kernel_times()
     for _ in range(args.steps):
         plan.step(cfg, ws, stream)
     torch.cuda.synchronize()
     kt = plan.kernel_times()
-    plan.set_timing(False)
+    # and, for a chained plan, a third pass timed as it runs: events around
+    # the momentum slot, the normalise slot and the chained launch
+    as_run = None
+    if chained:
+        plan.set_timing(2)
+        plan.kernel_times()
+        plan.chain_times()
+        for _ in range(args.steps):
+            plan.step(cfg, ws, stream)
+        torch.cuda.synchronize()
+        kr = plan.kernel_times()
+        c_ms, c_n = plan.chain_times()
+        as_run = {"momentum": kr["momentum"], "normalize": kr["normalize"], "chain": (c_ms, c_n)}
+    plan.set_timing(0)
 
     # one rank's share of an 8-GPU data-parallel step: the matrices rank 0
     # owns (ownership by algorithmic flops), through the same library; the
@@ -436,18 +456,22 @@ def main():
         if flops:
             ent["TFLOP/s"] = flops / step_s / 1e12
         per_kernel[name] = ent
-    dom = max(kt, key=lambda k: kt[k][0])
-    d_step = kt[dom][0] / args.steps * 1e-3
+    # the dominant kernel of the step as it runs: the chained launch (every
+    # Gram, poly and update tile) for a chained plan, else the kernel with
+    # the largest share in the per-kernel pass
+    times = as_run if as_run is not None else kt
+    dom = max(times, key=lambda k: times[k][0])
+    d_step = times[dom][0] / args.steps * 1e-3
     roof = roofline_of(*work[dom], d_step, wl.dtype)
     t_step = measured_traffic(wl.name, dom)
-    n_launch = kt[dom][1] / args.steps
+    n_launch = times[dom][1] / args.steps
     # HBM bytes per launch (the counter runs' per-step figure over the step's
     # launches of this kernel), null when taken on another kernel source
     roof["traffic"] = None if t_step is None else t_step / n_launch
     roof["traffic_per_step"] = t_step
     roof["kernel"] = dom
     roof["us_per_step"] = d_step * 1e6
-    roof["launches_per_step"] = kt[dom][1] / args.steps
+    roof["launches_per_step"] = n_launch
 
     line = {
         "metric": METRIC,
@@ -477,6 +501,8 @@ def main():
         "hip_graph": hip_graph,
         "separate_launches_ms_per_step": separate,
         "kernels": per_kernel,
+        "step_as_run_us": None if as_run is None else
+        {k: v[0] / args.steps * 1e3 for k, v in as_run.items()},
         "roofline": roof,
         "next": {"rank_share": {
             "world": world_d, "rank": 0, "matrices": len(share),

@@ -310,16 +310,23 @@ muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype d
 
 /* Per-kernel timing. A plan may split a large set into groups of matrices
  * whose kernels run concurrently on streams of the plan (joined back to the
- * caller's stream before muon_plan_step's work ends). While timing is on,
- * every muon_plan_step instead runs each kernel over the whole set in one
- * launch on the step's stream, with HIP events recorded around each
- * launch; the results are bitwise the same. muon_plan_kernel_times (which
- * waits for the recorded events) accumulates elapsed milliseconds and
- * launch counts per muon_kernel_kind into ms[MUON_K_COUNT] and
- * launches[MUON_K_COUNT], summed over the steps since timing was enabled
- * or last read (reading resets). Off by default. */
+ * caller's stream before muon_plan_step's work ends), or run the Newton-
+ * Schulz steps as one chained launch (below). With enable = 1, every
+ * muon_plan_step instead runs each kernel over the whole set in one launch
+ * on the step's stream, with HIP events recorded around each launch; the
+ * results are bitwise the same. With enable = 2, a step that uses the
+ * chained launch runs as it normally does, with events around its
+ * momentum slot, its normalise slot and the chained launch (a step without
+ * one is timed as with 1). enable = 0 (the default) turns timing off; other
+ * values are MUON_E_INVALID. muon_plan_kernel_times (which waits for the
+ * recorded events) accumulates elapsed milliseconds and launch counts per
+ * muon_kernel_kind into ms[MUON_K_COUNT] and launches[MUON_K_COUNT], summed
+ * over the steps since timing was enabled or last read (reading resets);
+ * muon_plan_chain_times does the same for the chained launches into *ms and
+ * *launches. */
 muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable);
 muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches);
+muon_status muon_plan_chain_times(muon_plan* plan, double* ms, int64_t* launches);
 
 /* Chained schedule. A bf16 plan with at least eight non-empty matrices
  * whose work spreads evenly over the eight XCDs (and no split Gram tiles)

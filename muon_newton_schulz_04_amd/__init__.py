@@ -20,6 +20,7 @@ __all__ = [
     "muon_step", "muon_orthogonalize", "muon_schedule_query", "muon_plan_set_timing",
     "muon_plan_kernel_times", "muon_plan_buffer_info", "MuonPlan", "make_config",
     "muon_plan_set_chained", "muon_plan_set_chain_timeout", "muon_plan_chain_state",
+    "muon_plan_chain_times",
     "MuonWeight", "MuonApply", "muon_plan_set_weights", "muon_plan_step_apply",
     "muon_plan_step_noalloc", "MUON_SCRATCH_BYTES",
     "MuonAdamTensor", "MuonAdamConfig", "AdamPlan", "muon_adam_plan_create",
@@ -106,6 +107,7 @@ def load_library(path: str = LIB_PATH):
         "muon_schedule_query": (i32, [P(MuonMatrix), i32, i32, i32, P(i32), i64, P(i64)]),
         "muon_plan_set_timing": (i32, [vp, i32]),
         "muon_plan_kernel_times": (i32, [vp, P(ctypes.c_double), P(i64)]),
+        "muon_plan_chain_times": (i32, [vp, P(ctypes.c_double), P(i64)]),
         "muon_plan_buffer_info": (i32, [vp, i32, P(MuonBufferInfo)]),
         "muon_plan_set_chained": (i32, [vp, i32]),
         "muon_plan_set_chain_timeout": (i32, [vp, i64]),
@@ -318,9 +320,18 @@ class MuonPlan:
                "muon_plan_step_apply")
         return ws
 
-    def set_timing(self, on: bool):
-        _check(load_library().muon_plan_set_timing(self.handle, 1 if on else 0),
-               "muon_plan_set_timing")
+    def set_timing(self, mode):
+        """0 / False: off; 1 / True: each kernel over the whole set in its own
+        timed launch; 2: the step's own launches timed as they run."""
+        _check(load_library().muon_plan_set_timing(self.handle, int(mode)), "muon_plan_set_timing")
+
+    def chain_times(self):
+        """(total ms, launches) of the chained launches timed with mode 2
+        since the last read."""
+        ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+        _check(load_library().muon_plan_chain_times(self.handle, ctypes.byref(ms), ctypes.byref(n)),
+               "muon_plan_chain_times")
+        return ms.value, n.value
 
     def kernel_times(self):
         """{kernel name: (total ms, launches)} since timing was enabled / last read."""
@@ -390,8 +401,12 @@ def muon_plan_step_noalloc(plan: MuonPlan, cfg: MuonConfig, stream=None):
     return plan.step_noalloc(cfg, stream)
 
 
-def muon_plan_set_timing(plan: MuonPlan, on: bool):
-    plan.set_timing(on)
+def muon_plan_set_timing(plan: MuonPlan, mode):
+    plan.set_timing(mode)
+
+
+def muon_plan_chain_times(plan: MuonPlan):
+    return plan.chain_times()
 
 
 def muon_plan_kernel_times(plan: MuonPlan):

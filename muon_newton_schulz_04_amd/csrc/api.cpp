@@ -39,11 +39,14 @@ struct muon_plan_s {
   hipStream_t gstream[muon::kMaxGroups] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[muon::kMaxGroups] = {};
-  bool timing = false;
+  // 0: off; 1: each kernel over the whole set in its own launch, timed;
+  // 2: the step's own launches timed as they run (the chained launch as one)
+  int timing = 0;
   std::vector<TimedLaunch> pending;           // recorded, not yet read
   std::vector<hipEvent_t> free_events;
-  double acc_ms[MUON_K_COUNT] = {};
-  int64_t acc_n[MUON_K_COUNT] = {};
+  // per muon_kernel_kind, then the chained launch (index MUON_K_COUNT)
+  double acc_ms[MUON_K_COUNT + 1] = {};
+  int64_t acc_n[MUON_K_COUNT + 1] = {};
   bool has_weights = false;                   // muon_plan_set_weights succeeded
   void* scratch = nullptr;                    // this device's fixed scratch array
 };
@@ -196,7 +199,11 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.hint = p->d_hint;
   // the chained schedule (not under per-kernel timing, which times each
   // kernel's own launch)
-  const bool chain = fused && H.chained && p->chain_on && !(p->timing && allow_timing);
+  const bool chain = fused && H.chained && p->chain_on && !(p->timing == 1 && allow_timing);
+  // per-kernel timing: asked for (1), or the step's own launches (2) of a
+  // step that has no chained launch
+  const bool per_kernel = allow_timing && (p->timing == 1 || (p->timing == 2 && !chain));
+  const bool as_run = allow_timing && p->timing == 2 && chain;
   a.chain_off = chain ? H.chain_off : -1;
   if (ap) {
     a.apply = 1;
@@ -240,26 +247,38 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     }
     return MUON_OK;
   };
-  // Per-kernel timing: step slot `kind` over the whole set (the one-group
-  // schedules) on the caller's stream, bracketed by HIP events.
-  auto timed = [&](int kind) -> muon_status {
-    const Slot o = slot_of(kind);
-    if (H.whole[o.sched[0]].items.empty()) return MUON_OK;
-    TimedLaunch t{o.report, get_event(p), get_event(p)};
+  // fn() (launches on the caller's stream), bracketed by HIP events whose
+  // interval is reported under `report` when `on`.
+  auto bracket = [&](bool on, int report, auto&& fn) -> muon_status {
+    if (!on) return fn() == hipSuccess ? MUON_OK : MUON_E_LAUNCH;
+    TimedLaunch t{report, get_event(p), get_event(p)};
     auto give_back = [&]() {
       if (t.start) p->free_events.push_back(t.start);
       if (t.stop) p->free_events.push_back(t.stop);
       return MUON_E_LAUNCH;
     };
     if (!t.start || !t.stop || hipEventRecord(t.start, s) != hipSuccess) return give_back();
+    if (fn() != hipSuccess || hipEventRecord(t.stop, s) != hipSuccess) return give_back();
+    p->pending.push_back(t);
+    return MUON_OK;
+  };
+  // Step slot `kind` over the whole set (the one-group schedules) on the
+  // caller's stream.
+  auto whole_slot = [&](int kind) -> hipError_t {
+    const Slot o = slot_of(kind);
     hipError_t r = hipSuccess;
     for (int k = 0; k < o.n && r == hipSuccess; ++k) {
       const auto& w = H.whole[o.sched[k]].items;
       if (!w.empty()) r = run(kind, o.kernel[k], p->d_whole[o.sched[k]], static_cast<int32_t>(w.size()), s);
     }
-    if (r != hipSuccess || hipEventRecord(t.stop, s) != hipSuccess) return give_back();
-    p->pending.push_back(t);
-    return MUON_OK;
+    return r;
+  };
+  // Per-kernel timing: step slot `kind` over the whole set, bracketed by
+  // HIP events.
+  auto timed = [&](int kind) -> muon_status {
+    const Slot o = slot_of(kind);
+    if (H.whole[o.sched[0]].items.empty()) return MUON_OK;
+    return bracket(true, o.report, [&]() { return whole_slot(kind); });
   };
   // The whole sequence of one group on stream q: momentum, normalise (or
   // the scale pass), k x (gram, poly, update).
@@ -277,7 +296,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     return MUON_OK;
   };
 
-  if (p->timing && allow_timing) {
+  if (per_kernel) {
     muon_status r;
     if ((r = timed(MUON_K_MOMENTUM)) != MUON_OK) return r;
     if ((r = timed(MUON_K_NORMALIZE)) != MUON_OK) return r;
@@ -294,16 +313,10 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     // momentum, the scale pass (which clears the chain's counters) and the
     // rewrite over the whole set (the one-group schedules), then every Gram,
     // poly and update tile of all steps in one persistent launch of one
-    // workgroup per CU
-    for (int kind : {int(MUON_K_MOMENTUM), int(MUON_K_NORMALIZE)}) {
-      const Slot o = slot_of(kind);
-      for (int k = 0; k < o.n; ++k) {
-        const auto& w = H.whole[o.sched[k]].items;
-        if (!w.empty() &&
-            run(kind, o.kernel[k], p->d_whole[o.sched[k]], static_cast<int32_t>(w.size()), s) != hipSuccess)
-          return MUON_E_LAUNCH;
-      }
-    }
+    // workgroup per CU (timing 2: each of the three slots bracketed)
+    muon_status r;
+    for (int kind : {int(MUON_K_MOMENTUM), int(MUON_K_NORMALIZE)})
+      if ((r = bracket(as_run, kind, [&]() { return whole_slot(kind); })) != MUON_OK) return r;
     muon::ChainArgs c{};
     c.items = p->d_chain;
     c.steps = cfg->steps;
@@ -313,8 +326,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
     a.cur = 0;
     a.last = 0;
     a.x0_scaled = 1;
-    if (muon::launch_chain(a, c, muon::kNumCu, s) != hipSuccess) return MUON_E_LAUNCH;
-    return MUON_OK;
+    return bracket(as_run, MUON_K_COUNT, [&]() { return muon::launch_chain(a, c, muon::kNumCu, s); });
   }
   if (H.ngroups == 1) return sequence(0, s);
   // several groups, no timing: each group runs its whole sequence on its
@@ -551,13 +563,14 @@ muon_status muon_schedule_query(const muon_matrix* mats, int32_t n, muon_dtype d
 }
 
 muon_status muon_plan_set_timing(muon_plan* plan, int32_t enable) {
-  if (plan == nullptr) return MUON_E_INVALID;
-  plan->timing = enable != 0;
+  if (plan == nullptr || enable < 0 || enable > 2) return MUON_E_INVALID;
+  plan->timing = enable;
   return MUON_OK;
 }
 
-muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches) {
-  if (plan == nullptr || ms == nullptr || launches == nullptr) return MUON_E_INVALID;
+namespace {
+// Waits for the recorded events and adds their intervals to the plan's sums.
+muon_status drain_events(muon_plan* plan) {
   for (auto& t : plan->pending) {
     if (hipEventSynchronize(t.stop) != hipSuccess) return MUON_E_DEVICE;
     float e = 0.f;
@@ -568,6 +581,25 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
     plan->free_events.push_back(t.stop);
   }
   plan->pending.clear();
+  return MUON_OK;
+}
+}  // namespace
+
+muon_status muon_plan_chain_times(muon_plan* plan, double* ms, int64_t* launches) {
+  if (plan == nullptr || ms == nullptr || launches == nullptr) return MUON_E_INVALID;
+  muon_status st = drain_events(plan);
+  if (st != MUON_OK) return st;
+  *ms = plan->acc_ms[MUON_K_COUNT];
+  *launches = plan->acc_n[MUON_K_COUNT];
+  plan->acc_ms[MUON_K_COUNT] = 0.0;
+  plan->acc_n[MUON_K_COUNT] = 0;
+  return MUON_OK;
+}
+
+muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launches) {
+  if (plan == nullptr || ms == nullptr || launches == nullptr) return MUON_E_INVALID;
+  muon_status st = drain_events(plan);
+  if (st != MUON_OK) return st;
   for (int k = 0; k < MUON_K_COUNT; ++k) {
     ms[k] = plan->acc_ms[k];
     launches[k] = plan->acc_n[k];
