@@ -152,3 +152,40 @@ def test_chained_wait_bound_ends_the_launch_and_reports():
     plan.destroy()
     want, _ = run(grads, cfg, False, 2)
     assert_same(got, want)
+
+
+def test_timing_as_run_reports_the_chained_launch():
+    """Timing mode 2 brackets the momentum slot, the normalise slot and the
+    chained launch as the step runs (the per-kernel counts of Gram, poly and
+    update stay zero); results are bitwise those of untimed steps. On a plan
+    without a chained launch, mode 2 times each kernel as mode 1 does."""
+    grads = mixed_set(15)
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True, 1e-7)
+    want, _ = run(grads, cfg, True, 3)
+    bufs = [torch.zeros_like(x) for x in grads]
+    outs = [torch.empty_like(x) for x in grads]
+    plan = mu.MuonPlan(grads, bufs, outs)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+    with pytest.raises(mu.MuonError):
+        plan.set_timing(3)
+    say("timing as run, chained")
+    plan.set_timing(2)
+    got = []
+    for _ in range(3):
+        plan.step(cfg, ws)
+        torch.cuda.synchronize()
+        got.append([o.clone() for o in outs] + [b.clone() for b in bufs])
+    kt = plan.kernel_times()
+    ms, n = plan.chain_times()
+    assert n == 3 and ms > 0
+    assert kt["momentum"][1] == 3 and kt["normalize"][1] == 3
+    assert kt["gram"][1] == kt["poly"][1] == kt["update"][1] == 0
+    assert plan.chain_times() == (0.0, 0)          # reading resets
+    assert_same(got, want)
+    say("timing as run, separate launches")
+    plan.set_chained(False)
+    plan.step(cfg, ws)
+    kt = plan.kernel_times()
+    assert kt["gram"][1] == 5 and kt["update"][1] == 5 and plan.chain_times() == (0.0, 0)
+    plan.set_timing(0)
+    plan.destroy()
