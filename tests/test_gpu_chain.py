@@ -97,6 +97,22 @@ def test_chained_step_counts(steps):
     assert_same(a, b)
 
 
+def test_chained_ragged_set_matches_separate_launches():
+    """Sides that are not multiples of the 256-wide tile (padding tiles,
+    odd tile counts, tall and wide matrices) through the chained launch."""
+    shapes = [(300, 700), (700, 300), (520, 520), (257, 1000), (1000, 257), (640, 900), (900, 640),
+              (333, 333)] * 2
+    assert len(mu.muon_schedule_query(shapes, mu.MUON_BF16, 7)) > 0
+    g = torch.Generator().manual_seed(16)
+    grads = [(torch.randn(r, c, generator=g) * 0.02).to(torch.bfloat16).to(DEV) for r, c in shapes]
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True, 1e-7)
+    say("chained ragged set")
+    a, sa = run(grads, cfg, True, 3)
+    b, sb = run(grads, cfg, False, 3)
+    assert sa == (1, 0) and sb == (0, 0)
+    assert_same(a, b)
+
+
 def test_chained_apply_matches_separate_launches():
     grads = mixed_set(12)
     g = torch.Generator().manual_seed(5)
