@@ -329,8 +329,9 @@ muon_status muon_plan_kernel_times(muon_plan* plan, double* ms, int64_t* launche
 muon_status muon_plan_chain_times(muon_plan* plan, double* ms, int64_t* launches);
 
 /* Chained schedule. A bf16 plan with at least eight non-empty matrices
- * whose work spreads evenly over the eight XCDs (and no split Gram tiles)
- * runs the Newton-Schulz steps of muon_plan_step as one launch instead of
+ * whose work spreads evenly over the eight XCDs (and no split Gram tiles),
+ * under 24 waves of 256 update tiles deep, on a device with all 256 CUs of
+ * an MI355X (not a partition of one), runs the Newton-Schulz steps of muon_plan_step as one launch instead of
  * three per step: every Gram, poly and update tile of all k steps, with
  * all tiles of a matrix on one XCD. The workgroups on an XCD take the
  * XCD's tiles in a fixed order, and a tile starts once its matrix has

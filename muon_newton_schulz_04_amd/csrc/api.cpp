@@ -33,6 +33,7 @@ struct muon_plan_s {
   const muon::ChainItem* d_chain = nullptr;   // chained schedule: the per-XCD lists
   int32_t* d_err = nullptr;                   // chained launches: a wait past its bound (sticky)
   bool chain_on = true;                       // muon_plan_set_chained
+  bool chain_ok = false;                      // the device has the 8 x 32 CUs the lists assume
   int64_t chain_wait_us = 2000000;            // muon_plan_set_chain_timeout
   // groups > 1: one stream per group (default priority) and the events that
   // fork them from, and join them back to, the caller's stream
@@ -60,6 +61,9 @@ muon_status upload(muon_plan_s* p) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MUON_E_DEVICE;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_E_DEVICE;
   p->device = dev;
+  // the chained lists are per XCD of a whole MI355X (8 XCDs of 32 CUs); on a
+  // partitioned device the plan uses the separate launches
+  p->chain_ok = prop.multiProcessorCount == muon::kNumCu;
   // set-up time: the device address of this GPU's scratch array (once per
   // device) for muon_plan_step_noalloc
   if (muon::scratch_address(&p->scratch) != hipSuccess) {
@@ -199,7 +203,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   a.hint = p->d_hint;
   // the chained schedule (not under per-kernel timing, which times each
   // kernel's own launch)
-  const bool chain = fused && H.chained && p->chain_on && !(p->timing == 1 && allow_timing);
+  const bool chain = fused && H.chained && p->chain_ok && p->chain_on && !(p->timing == 1 && allow_timing);
   // per-kernel timing: asked for (1), or the step's own launches (2) of a
   // step that has no chained launch
   const bool per_kernel = allow_timing && (p->timing == 1 || (p->timing == 2 && !chain));
@@ -623,7 +627,7 @@ muon_status muon_plan_set_chain_timeout(muon_plan* plan, int64_t microseconds) {
 
 muon_status muon_plan_chain_state(muon_plan* plan, int32_t* chained, int32_t* error) {
   if (plan == nullptr || chained == nullptr || error == nullptr) return MUON_E_INVALID;
-  *chained = plan->host.chained && plan->chain_on ? 1 : 0;
+  *chained = plan->host.chained && plan->chain_ok && plan->chain_on ? 1 : 0;
   *error = 0;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return MUON_E_DEVICE;
