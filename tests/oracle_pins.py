@@ -197,7 +197,7 @@ def pin_equal_singular_values(impl):
         a, b, c = (Fraction(str(x)) for x in QUINTIC)
         pk = float(p_scalar(s, a, b, c, 5))
         if want is not None:
-            assert abs(pk - want) < 1e-9                # the surveyed worked value
+            assert abs(pk - want) < 1e-9                # p^5 at s = 1/sqrt(768), to 10 digits
         out = impl.orthogonalize(g, *QUINTIC, 5, EPS)
         assert rel_fro(out, pk * q.T) < 1e-11
 
