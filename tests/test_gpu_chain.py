@@ -205,3 +205,21 @@ def test_timing_as_run_reports_the_chained_launch():
     assert kt["gram"][1] == 5 and kt["update"][1] == 5 and plan.chain_times() == (0.0, 0)
     plan.set_timing(0)
     plan.destroy()
+
+
+def test_chained_orthogonalize_matches_separate_launches():
+    """muon_orthogonalize (u = G, no momentum state) on a chained set, whose
+    cached plan runs chained, against a plan without momentum forced to the
+    separate launches."""
+    grads = mixed_set(17)
+    cfg = mu.make_config(*QUINTIC, 5, 0.0, False, 1e-7)
+    say("chained orthogonalisation")
+    outs_a = [torch.empty_like(x) for x in grads]
+    mu.muon_orthogonalize(grads, outs_a, cfg)
+    outs_b = [torch.empty_like(x) for x in grads]
+    plan = mu.MuonPlan(grads, None, outs_b)
+    plan.set_chained(False)
+    plan.step(cfg)
+    torch.cuda.synchronize()
+    plan.destroy()
+    assert_same([outs_a], [outs_b])
