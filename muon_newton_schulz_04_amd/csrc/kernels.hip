@@ -2169,6 +2169,7 @@ __global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, Chain
   int32_t* done = tick + kNumXcd;
   const int32_t beg = C.beg[x], len = C.beg[x + 1] - beg, total = len * C.steps;
   int32_t next = 0, prev = -1;  // (owner) the tickets of the next and the last pass
+  int32_t seen = -1;             // (owner) an early reading of the next tile's counter
   if (threadIdx.x == kChainOwner)
     next = __hip_atomic_fetch_add(tick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
@@ -2181,7 +2182,10 @@ __global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, Chain
       } else if (t < total) {
         const int32_t step = t / len;
         const ChainItem ci = C.items[beg + t - step * len];
-        ok = chain_wait(done + ci.mat, step * (ci.kind_n >> 8) + ci.need, C.err, C.wait_ticks);
+        // (counters only grow: an earlier reading that already meets the
+        // need proves it)
+        const int32_t need = step * (ci.kind_n >> 8) + ci.need;
+        if (seen < need) ok = chain_wait(done + ci.mat, need, C.err, C.wait_ticks);
       }
       prev = t;
       slot[0] = t;
@@ -2217,6 +2221,14 @@ __global__ __launch_bounds__(e16::NTHR, 1) void chain16_kernel(StepArgs P, Chain
     } else {
       if (Q.last) tile16<uint16_t, OP_F16, UPDATE, true, false, false, true>(Q, it, lds, tid, fetch);
       else tile16<uint16_t, OP_F16, UPDATE, false, false, false, true>(Q, it, lds, tid, fetch);
+    }
+    // the next tile's record and an early reading of its counter, while
+    // the stores drain (the pass's wait then usually has nothing to wait for)
+    seen = -1;
+    if (threadIdx.x == kChainOwner && next < total) {
+      const int32_t ns = next / len;
+      const ChainItem nci = C.items[beg + next - ns * len];
+      seen = __hip_atomic_load(done + nci.mat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // release: every wave's stores have reached L2, then the count goes up
     __builtin_amdgcn_s_waitcnt(0);
