@@ -223,3 +223,36 @@ def test_chained_orthogonalize_matches_separate_launches():
     torch.cuda.synchronize()
     plan.destroy()
     assert_same([outs_a], [outs_b])
+
+
+def test_two_chained_plans_on_concurrent_streams():
+    """Two chained plans stepping at the same time on two streams (their
+    persistent workgroups share the CUs; each launch only ever waits on its
+    own running workgroups): outputs and buffers bitwise those of the same
+    steps run one plan after the other."""
+    sets = [mixed_set(21), mixed_set(22)]
+    cfg = mu.make_config(*QUINTIC, 5, 0.95, True, 1e-7)
+    want = [run(g, cfg, True, 2)[0] for g in sets]
+    plans, state = [], []
+    for g in sets:
+        bufs = [torch.zeros_like(x) for x in g]
+        outs = [torch.empty_like(x) for x in g]
+        plan = mu.MuonPlan(g, bufs, outs)
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+        plans.append(plan)
+        state.append((bufs, outs, ws))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    say("two chained plans, concurrent streams")
+    got = [[], []]
+    for _ in range(2):
+        for i in range(2):
+            plans[i].step(cfg, state[i][2], streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            got[i].append([o.clone() for o in state[i][1]] + [b.clone() for b in state[i][0]])
+    for i in range(2):
+        assert plans[i].chain_state() == (1, 0)
+        assert_same(got[i], want[i])
+        plans[i].destroy()
