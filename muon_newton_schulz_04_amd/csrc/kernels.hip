@@ -1419,23 +1419,31 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
   int cur = 0;
   // one pass over stage g; J >= 0 also folds block column J (see the other
   // tiles' loop: the fold passes are loops of their own)
-  auto pass = [&](int g, auto fold_j) {
+  // TAIL (Gram: the last three passes, 1 .. 3 for g = nst-3 .. nst-1)
+  // issues no stage past the end and waits for every stage issued.
+  auto pass = [&](int g, auto fold_j, auto tail) {
     constexpr int J = decltype(fold_j)::value;
+    constexpr int TAIL = decltype(tail)::value;
     const int nxt = cur == NS - 1 ? 0 : cur + 1;
     const int old = cur == 0 ? NS - 1 : cur - 1;
     {
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
       kstep_diag<OP, ROLE>(acc, f0, f1, lds + cur * STAGE, 1, geo, tid, [&](int c) {
-        if (dma_wave) dma_piece<false, COH>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c, tid);
+        if constexpr (TAIL <= 1)
+          if (dma_wave) dma_piece<false, COH>(lds + s2 * STAGE, opA, lda, opA, lda, k2, H + c, tid);
       });
     }
-    MUON_WAIT_VMCNT(DPS * (NS - 3));
+    if constexpr (TAIL >= 2)
+      MUON_WAIT_VMCNT(0);
+    else
+      MUON_WAIT_VMCNT(DPS * (NS - 3));
     asm volatile("s_barrier" ::: "memory");
     {
       const int64_t k3 = int64_t(min(g + NS - 1, nst - 1)) * KS;
       kstep_diag<OP, ROLE>(acc, f1, f0, lds + nxt * STAGE, 0, geo, tid, [&](int c) {
-        if (dma_wave) dma_piece<false, COH>(lds + old * STAGE, opA, lda, opA, lda, k3, c, tid);
+        if constexpr (TAIL == 0)
+          if (dma_wave) dma_piece<false, COH>(lds + old * STAGE, opA, lda, opA, lda, k3, c, tid);
       });
     }
     if constexpr (J >= 0) {
@@ -1445,17 +1453,29 @@ __device__ __forceinline__ void kloop_diag(f32x16_t (&acc)[4][2], char* lds, con
     cur = nxt;
   };
   using NoFold = std::integral_constant<int, -1>;
+  using T0 = std::integral_constant<int, 0>;
   int g = 0;
-  if (FOLD && fs0 >= 0) {
-    for (; g < fs0; ++g) pass(g, NoFold{});
-    pass(g++, std::integral_constant<int, 0>{});
-    if constexpr (R::NJ == 2) {
-      for (; g < fs1; ++g) pass(g, NoFold{});
-      pass(g++, std::integral_constant<int, 1>{});
+  if constexpr (FOLD) {
+    // (poly: past the end the DMA repeats the last stage, valid addresses,
+    // unused: the last diagonal tile's fold passes fall among the last
+    // passes, and tail passes for each of them cost more registers than the
+    // chained launch has)
+    if (fs0 >= 0) {
+      for (; g < fs0; ++g) pass(g, NoFold{}, T0{});
+      pass(g++, std::integral_constant<int, 0>{}, T0{});
+      if constexpr (R::NJ == 2) {
+        for (; g < fs1; ++g) pass(g, NoFold{}, T0{});
+        pass(g++, std::integral_constant<int, 1>{}, T0{});
+      }
     }
+    for (; g < nst; ++g) pass(g, NoFold{}, T0{});
+  } else {
+    for (; g < nst - 3; ++g) pass(g, NoFold{}, T0{});
+    pass(g++, NoFold{}, std::integral_constant<int, 1>{});
+    pass(g++, NoFold{}, std::integral_constant<int, 2>{});
+    pass(g++, NoFold{}, std::integral_constant<int, 3>{});
   }
-  for (; g < nst; ++g) pass(g, NoFold{});
-  MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
+  MUON_WAIT_VMCNT(0);  // every stage issued lands before the LDS is reused or freed
 }
 
 
@@ -1548,7 +1568,9 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   //   mma(g, 0) | read (g, 1) | stage g+1 landed, barrier, DMA g+NS-1 into
   //   the slot of g-1 | mma(g, 1) | read (g+1, 0)
   // Every pass issues one stage, so the wait count is the same in every pass;
-  // past the end the DMA repeats the last stage (valid addresses, unused).
+  // past the end the DMA of poly repeats the last stage (valid addresses,
+  // unused), while the last passes of Gram and of the update are passes of
+  // their own (TAIL below) that issue no stage past the end.
   const bool fold = KIND == POLY && P.c != 0.f;
   // This wave's blocks: acc[i][j] is rows rbase + 32 i .. of the tile and
   // columns cb0 .. (j = 0) or cb1 .. (j = 1), for i < nr0 / nr1. Diagonal
@@ -1614,9 +1636,11 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   // One pass over stage g. Poly's b A term is folded into the accumulators
   // of block column J in the pass over the stage that holds those columns
   // as k; those two passes are loops of their own, so that no other pass
-  // carries the fold's branch. TAIL (the update's last three passes, 1 .. 3
-  // for g = nst-3 .. nst-1): the DMA of stages nst and nst+1 fetches the low
-  // bytes, and the last pass issues no repeat (nothing waits for it).
+  // carries the fold's branch. TAIL (the last three passes, g = nst-3 ..
+  // nst-1): the update's (1 .. 3) fetch the low bytes where stages nst and
+  // nst+1 would go, and its last pass issues nothing (nothing waits for it);
+  // Gram's (4 .. 6) issue no stage past the end and wait for every stage
+  // issued.
   auto pass = [&](int g, auto fold_j, auto tail) {
     constexpr int J = decltype(fold_j)::value;
     constexpr int TAIL = decltype(tail)::value;
@@ -1628,9 +1652,9 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
       const int s2 = cur + NS - 2 < NS ? cur + NS - 2 : cur - 2;
       const int64_t k2 = int64_t(min(g + NS - 2, nst - 1)) * KS;
       kstep_dma<OP, KN, H>(acc, f0, f1, lds + cur * STAGE, 1, wm, wn, tid, [&](int c) {
-        if constexpr (TAIL >= 2) {  // stage nst or nst+1: low bytes, second half
+        if constexpr (TAIL == 2 || TAIL == 3) {  // stage nst or nst+1: low bytes, second half
           if (dma_wave) dma_block_piece<COH>(lds + s2 * STAGE, lo_src + (TAIL - 2) * STAGE, H + c, tid);
-        } else {
+        } else if constexpr (TAIL <= 1 || TAIL == 4) {
           if (dma_wave) dma_piece<KN, COH>(lds + s2 * STAGE, opA, lda, opB, ldb, k2, H + c, tid);
         }
       });
@@ -1639,7 +1663,10 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
     // still be in flight). A bare s_barrier: the workgroup fence of
     // __syncthreads would also wait for those; the memory clobber keeps the
     // compiler from moving LDS accesses across it.
-    MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3));
+    if constexpr (TAIL >= 5)
+      MUON_WAIT_VMCNT(0);
+    else
+      MUON_WAIT_VMCNT(DMA_PER_STAGE * (NS - 3));
     asm volatile("s_barrier" ::: "memory");
     // every wave has finished reading stage g-1: refill its slot, the first
     // half of stage g+NS-1 now and the second half with the next k-step
@@ -1665,11 +1692,20 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
   };
   using NoFold = std::integral_constant<int, -1>;
   using T0 = std::integral_constant<int, 0>;
+  using Fold0 = std::integral_constant<int, 0>;
+  using Fold1 = std::integral_constant<int, 1>;
+  using T4 = std::integral_constant<int, 4>;
+  using T5 = std::integral_constant<int, 5>;
+  using T6 = std::integral_constant<int, 6>;
   if (fold) {
+    // (poly: past the end the DMA repeats the last stage, valid addresses,
+    // unused: a fold pass can be one of the last three passes, and tail
+    // passes for those cases cost more registers than the chained launch
+    // has)
     int g = 0;
     for (; g < bias0; ++g) pass(g, NoFold{}, T0{});
-    pass(g++, std::integral_constant<int, 0>{}, T0{});
-    pass(g++, std::integral_constant<int, 1>{}, T0{});
+    pass(g++, Fold0{}, T0{});
+    pass(g++, Fold1{}, T0{});
     for (; g < nst; ++g) pass(g, NoFold{}, T0{});
   } else if constexpr (LO_DMA) {
     int g = 0;
@@ -1678,9 +1714,15 @@ __device__ __forceinline__ void tile16(const StepArgs& P, const WorkItem it, cha
     pass(g++, NoFold{}, std::integral_constant<int, 2>{});
     pass(g++, NoFold{}, std::integral_constant<int, 3>{});
   } else {
-    for (int g = 0; g < nst; ++g) pass(g, NoFold{}, T0{});
+    // Gram (and poly with c = 0): the last three passes (TAIL 4 .. 6) issue
+    // no stage past the end and wait for every stage issued
+    int g = 0;
+    for (; g < nst - 3; ++g) pass(g, NoFold{}, T0{});
+    pass(g++, NoFold{}, T4{});
+    pass(g++, NoFold{}, T5{});
+    pass(g++, NoFold{}, T6{});
   }
-  MUON_WAIT_VMCNT(0);  // the repeated stages land before the LDS is reused or freed
+  MUON_WAIT_VMCNT(0);  // every stage issued lands before the LDS is reused or freed
   }
 
   // ---------------------------------------------------------------- epilogue
