@@ -772,23 +772,28 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * ROWB + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
+// 16 bytes as a native vector: the staging arrays of the fp32 engine stay in
+// registers (arrays of the uint4 struct were kept in scratch memory).
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t comp(const v4u32& v, int e) { return v[e]; }
+
 // Loads a 128-row x 128-byte slab of a row-major operand whose k index is
 // contiguous (rows r0.., bytes k0b..): 4 x 16 bytes per thread.
-__device__ __forceinline__ void load_rows(uint4 (&r)[4], const char* base, int64_t ld_bytes,
+__device__ __forceinline__ void load_rows(v4u32 (&r)[4], const char* base, int64_t ld_bytes,
                                           int64_t k0b) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (t >> 3) + 32 * q, ch = t & 7;
-    r[q] = *reinterpret_cast<const uint4*>(base + row * ld_bytes + k0b + ch * 16);
+    r[q] = *reinterpret_cast<const v4u32*>(base + row * ld_bytes + k0b + ch * 16);
   }
 }
-__device__ __forceinline__ void store_rows(char* lds, const uint4 (&r)[4]) {
+__device__ __forceinline__ void store_rows(char* lds, const v4u32 (&r)[4]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (t >> 3) + 32 * q, ch = t & 7;
-    *reinterpret_cast<uint4*>(lds + lds_off(row, ch)) = r[q];
+    *reinterpret_cast<v4u32*>(lds + lds_off(row, ch)) = r[q];
   }
 }
 
@@ -797,7 +802,7 @@ __device__ __forceinline__ void store_rows(char* lds, const uint4 (&r)[4]) {
 // block of 4 k-rows x V columns (V = 8 bf16 / 4 fp32, 16 bytes) and later
 // writes it transposed into the [n][k] LDS tile.
 template <int ES>
-__device__ __forceinline__ void load_cols(uint4 (&r)[4], const char* base, int64_t ld_bytes,
+__device__ __forceinline__ void load_cols(v4u32 (&r)[4], const char* base, int64_t ld_bytes,
                                           int64_t k0) {
   constexpr int V = 16 / ES;
   constexpr int NG = 128 / V;  // column groups per slab (16 bf16, 32 fp32)
@@ -805,10 +810,10 @@ __device__ __forceinline__ void load_cols(uint4 (&r)[4], const char* base, int64
   const int kq = t / NG, ng = t % NG;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    r[q] = *reinterpret_cast<const uint4*>(base + (k0 + 4 * kq + q) * ld_bytes + ng * 16);
+    r[q] = *reinterpret_cast<const v4u32*>(base + (k0 + 4 * kq + q) * ld_bytes + ng * 16);
 }
 template <int ES>
-__device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
+__device__ __forceinline__ void store_cols(char* lds, const v4u32 (&r)[4]) {
   constexpr int V = 16 / ES;
   constexpr int NG = 128 / V;
   const int t = threadIdx.x;
@@ -832,8 +837,8 @@ __device__ __forceinline__ void store_cols(char* lds, const uint4 (&r)[4]) {
     // k-quad kq covers fp32 k = 4kq..4kq+3: exactly chunk kq
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint4 v = make_uint4(comp(r[0], e), comp(r[1], e), comp(r[2], e), comp(r[3], e));
-      *reinterpret_cast<uint4*>(lds + lds_off(ng * 4 + e, kq)) = v;
+      const v4u32 v = {comp(r[0], e), comp(r[1], e), comp(r[2], e), comp(r[3], e)};
+      *reinterpret_cast<v4u32*>(lds + lds_off(ng * 4 + e, kq)) = v;
     }
   }
 }
@@ -914,7 +919,7 @@ __global__ __launch_bounds__(256, 1) void gemm32_kernel(StepArgs P) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[4], rb[4];
+  v4u32 ra[4], rb[4];
   load_rows(ra, opA, lda_b, 0);
   if (KIND == UPDATE) load_cols<ES>(rb, opB, ldb_b, 0);
   else load_rows(rb, opB, ldb_b, 0);
