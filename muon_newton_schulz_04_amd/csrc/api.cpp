@@ -181,6 +181,7 @@ muon_status step_impl(muon_plan_s* p, const muon_config* cfg, void* ws, size_t w
   hipStream_t s = static_cast<hipStream_t>(stream);
   muon::StepArgs a{};
   a.mats = p->d_mats;
+  a.n_mats = static_cast<int32_t>(H.info.size());
   a.ws = static_cast<char*>(ws);
   a.parts = static_cast<float*>(ws);
   a.part_exp = a.parts + H.total_partials;

@@ -743,11 +743,17 @@ __global__ __launch_bounds__(256) void x0_scale_kernel(StepArgs A) {
 // Operand rewrite: the tiles of the matrices whose flag is set, u again
 // from G and the stored buf'. Runs over the momentum pass's tile schedule
 // with a smaller grid, block b taking items b, b + grid, ... (grid a
-// multiple of 8, so each item stays on the XCD the schedule placed it on);
-// where no flag is set it only reads the items and flags.
+// multiple of 8, so each item stays on the XCD the schedule placed it on).
+// Most calls have no flag set: every workgroup first reads the flags of all
+// non-empty matrices at once and leaves when none is set, instead of
+// walking its items (two dependent loads each, one item after another).
 __global__ __launch_bounds__(256) void x0_rewrite_kernel(StepArgs A) {
   __shared__ float tile[64][65];
   const float* x0s = reinterpret_cast<const float*>(A.ws + A.x0s_off);
+  int any = 0;
+  for (int32_t i = threadIdx.x; i < A.n_mats; i += blockDim.x)
+    any |= A.mats[i].m > 0 && x0s[4 * i + 3] != 0.f;
+  if (!__syncthreads_or(any)) return;
   for (int32_t q = blockIdx.x; q < A.n_items; q += gridDim.x) {
     const WorkItem it = A.items[q];
     if (it.mat < 0 || x0s[4 * it.mat + 3] == 0.f) continue;

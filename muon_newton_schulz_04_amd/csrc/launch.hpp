@@ -31,6 +31,7 @@ struct StepArgs {
   int64_t tsum_off, tmax_off, x0s_off;  // workspace offsets (see HostPlan)
   float* hint;  // plan memory, per matrix: the largest |u| of the last call (0: none)
   int32_t n_items;  // items of the schedule (kernels whose grid is smaller)
+  int32_t n_mats;   // matrices of the set (the rewrite checks every matrix's flag first)
   // chained schedule: workspace offset of its counters (the scale pass
   // clears them), -1 without one
   int64_t chain_off;
